@@ -1,0 +1,159 @@
+"""Float64 CPU oracle for the S5 layer forward path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library imports, links or runs this
+module: only the tests, the package smoke check and the benchmark's CPU
+baseline leg may call it. It shares no code with the HIP path.
+
+It is the plain definition of what the forward path computes, written out
+step by step in float64 with an explicit sequential loop over time. Sources
+(page title and section):
+
+O1  Delta_p = exp(log Delta_p) (time-invariant) or a given Delta[b,k,p]
+    (time-varying); a negative or non-finite interval is rejected.
+    [paper Sec. 3.2 and App. A `apply_S5_layer`; abhik.ai review, row 2
+    "Integrate a held input exactly"]
+O2  zero-order hold per mode: z = lambda*Delta, Lambda_bar = exp(z),
+    gain = (exp(z) - 1)/lambda = Delta*phi1(z), with phi1(z) = (e^z - 1)/z;
+    for |z| < 1e-4 the gain is Delta times the 9-term Taylor series of phi1
+    (the review's numerical guard; removable singularity, gain -> Delta as
+    lambda -> 0). B_bar = gain[:, None] * B~.
+    [paper eq. 6; App. A `discretize`; abhik.ai review, row 2]
+O3  drive b_k = B_bar u_k (time-varying: gain_k * (B~ u_k)).
+    [abhik.ai review, row 1 "Mix input channels before the recurrence";
+    App. A `apply_ssm`]
+O4  x_{-1} = 0, x_k = Lambda_bar_k * x_{k-1} + b_k, one step at a time.
+    The associative scan of the pages reaches exactly this result up to
+    floating-point regrouping. [paper eq. 2 and Sec. 2.2; App. H]
+O5  y_k = Re(C~ x_k) + D * u_k, full spectrum (factor 1).
+    [App. A `apply_ssm` readout; abhik.ai review, row 4: the factor two applies
+    only to half-spectrum storage]
+
+Every function is pinned by the checks in tests/test_oracle_pins.py against
+closed forms, an ODE solve, the convolution-kernel form, impulse responses,
+printed values of the pages and invariants.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "SERIES_RADIUS",
+    "check_intervals",
+    "zoh",
+    "discretize",
+    "drive",
+    "scan_sequential",
+    "readout",
+    "forward",
+    "forward_timevarying",
+    "compose",
+]
+
+# |z| below which the gain uses the Taylor series of phi1 (abhik.ai review, row 2)
+SERIES_RADIUS = 1e-4
+
+
+def check_intervals(delta) -> np.ndarray:
+    """O1 precondition: intervals must be finite and non-negative."""
+    d = np.asarray(delta, dtype=np.float64)
+    if not np.all(np.isfinite(d)) or np.any(d < 0):
+        raise ValueError("intervals must be finite and non-negative")
+    return d
+
+
+def zoh(lam, delta):
+    """O2: per-element ZOH of a diagonal mode. ``lam`` and ``delta`` broadcast
+    against each other. Returns (Lambda_bar, gain), complex128."""
+    lam = np.asarray(lam, dtype=np.complex128)
+    d = check_intervals(delta)
+    lam, d = np.broadcast_arrays(lam, d)
+    z = lam * d
+    lam_bar = np.exp(z)
+    gain = np.empty_like(z)
+    small = np.abs(z) < SERIES_RADIUS
+    big = ~small
+    gain[big] = (lam_bar[big] - 1.0) / lam[big]
+    if small.any():
+        zs = z[small]
+        term = np.ones_like(zs)
+        phi = np.ones_like(zs)
+        for n in range(1, 9):          # sum_{n=0}^{8} z^n / (n+1)!
+            term = term * zs / (n + 1)
+            phi = phi + term
+        gain[small] = d[small] * phi
+    return lam_bar, gain
+
+
+def discretize(lam, b_tilde, delta):
+    """O1-O2 for the time-invariant case: returns (Lambda_bar [P],
+    B_bar [P, H]) for per-mode intervals ``delta`` [P]."""
+    lam_bar, gain = zoh(lam, delta)
+    b_bar = gain[:, None] * np.asarray(b_tilde, dtype=np.complex128)
+    return lam_bar, b_bar
+
+
+def drive(u, b_mat):
+    """O3: b_k = B u_k for every (batch, step); u [..., L, H] real,
+    ``b_mat`` [P, H] complex -> [..., L, P] complex."""
+    return np.asarray(u, dtype=np.float64) @ np.asarray(b_mat, dtype=np.complex128).T
+
+
+def scan_sequential(lam_bar, bu):
+    """O4: x_k = a_k * x_{k-1} + b_k from x_{-1} = 0, explicit loop over k.
+
+    ``bu`` is [B, L, P]; ``lam_bar`` is [P] (time-invariant) or [B, L, P]."""
+    bu = np.asarray(bu, dtype=np.complex128)
+    lam_bar = np.asarray(lam_bar, dtype=np.complex128)
+    Bn, L, P = bu.shape
+    tv = lam_bar.ndim == 3
+    x = np.zeros((Bn, P), dtype=np.complex128)
+    out = np.empty_like(bu)
+    for k in range(L):
+        a = lam_bar[:, k, :] if tv else lam_bar
+        x = a * x + bu[:, k, :]
+        out[:, k, :] = x
+    return out
+
+
+def readout(x, c_tilde, d, u):
+    """O5: y_k = Re(C~ x_k) + D * u_k (full spectrum)."""
+    cx = np.asarray(x, dtype=np.complex128) @ np.asarray(c_tilde, dtype=np.complex128).T
+    return cx.real + np.asarray(d, dtype=np.float64) * np.asarray(u, dtype=np.float64)
+
+
+def forward(u, lam, b_tilde, c_tilde, d, log_delta):
+    """Time-invariant S5 forward (pre-activation output), float64.
+
+    u [B, L, H] real; lam [P]; b_tilde [P, H]; c_tilde [H, P]; d [H];
+    log_delta [P]. Returns y [B, L, H] float64."""
+    u = np.asarray(u, dtype=np.float64)
+    delta = np.exp(np.asarray(log_delta, dtype=np.float64))          # O1
+    lam_bar, b_bar = discretize(lam, b_tilde, delta)                  # O2
+    bu = drive(u, b_bar)                                              # O3
+    x = scan_sequential(lam_bar, bu)                                  # O4
+    return readout(x, c_tilde, d, u)                                  # O5
+
+
+def forward_timevarying(u, lam, b_tilde, c_tilde, d, delta):
+    """Time-varying S5 forward: one interval per (batch, step, mode).
+
+    Step k uses Delta_k for both Lambda_bar_k and B_bar_k (the interval that
+    ends at step k). u [B, L, H]; delta [B, L, P]. Returns y [B, L, H]."""
+    u = np.asarray(u, dtype=np.float64)
+    delta = check_intervals(delta)                                    # O1
+    lam_bar, gain = zoh(np.asarray(lam)[None, None, :], delta)        # O2
+    bu = gain * drive(u, b_tilde)                                     # O3
+    x = scan_sequential(lam_bar, bu)                                  # O4
+    return readout(x, c_tilde, d, u)                                  # O5
+
+
+def compose(earlier, later):
+    """The scan's binary operator on affine maps x -> a*x + b: apply
+    ``earlier`` then ``later``; result (a_l * a_e, a_l * b_e + b_l).
+    [paper App. H; App. A `binary_operator`]"""
+    a_e, b_e = earlier
+    a_l, b_l = later
+    return a_l * a_e, a_l * b_e + b_l
