@@ -1,0 +1,239 @@
+"""Benchmark of the S5 layer forward hot path on one MI355X.
+
+One step = one complete s5_forward call (discretisation, drive projection,
+chunked scan with carry, readout) over one batch of synthetic input that is
+already resident in HBM. Default workload: B=16, L=16384, H=128, P=256 with
+bf16 u/y (the Path-X-shaped configuration). The step rotates over several
+input/output buffer sets whose total exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line with the contract fields plus
+  roofline      dominant kernel (the fused forward kernels, timed with HIP
+                events recorded by the library around them on the call's stream)
+  hbm           the same kernel against the HBM roofline (algorithmic bytes)
+  cpu_baseline  the float64 oracle timed on this host's cores
+  parity        max |y - y_oracle| / rms(y_oracle) of the benchmark's output
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "S5 layer fwd tokens/s (B·L/s) at L=16384,H=128,P=256; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0}   # fp32 io runs bf16x3 products
+CONFIG_INDEX = 3
+
+
+class HipEvents:
+    """Raw hipEvent_t handles via libamdhip64 (the library records them)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e: int) -> None:
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic_bytes(w) -> int:
+    """HBM bytes the method must move: u in, y out, (time-varying) Delta in,
+    parameters once."""
+    s = 2 if w.io == "bf16" else 4
+    tok = w.B * w.L
+    b = tok * w.H * 2 * s
+    if w.time_varying:
+        b += tok * w.P * 4
+    b += 8 * w.P + 16 * w.P * w.H + 4 * w.H + 4 * w.P
+    return b
+
+
+def algorithmic_flops(w) -> int:
+    """Dense real-equivalent work of the two complex projections: 8*P*H per token
+    (4PH for B_bar u, 4PH for Re(C~ x))."""
+    return 8 * w.P * w.H * w.B * w.L
+
+
+def cpu_baseline(w, repeats: int, budget_s: float):
+    import oracle.s5_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    times = []
+    y = None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        if w.time_varying:
+            y = orc.forward_timevarying(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.delta)
+        else:
+            y = orc.forward(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.log_delta)
+        times.append(time.perf_counter() - t0)
+        if sum(times) > budget_s:
+            break
+    t = float(np.median(times))
+    return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole workload (B={w.B}, L={w.L}), float64 NumPy, median of {len(times)} "
+                      f"run(s), {t:.2f} s each"}, y
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=CONFIG_INDEX)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the S5 forward path here runs on a single "
+              "MI355X; batch sharding across GPUs needs no communication and is not "
+              "benchmarked. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import diagonal_state_space_amd as s5
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = wl.make_config(args.config)
+    print(f"[bench] workload {w.name}: B={w.B} L={w.L} H={w.H} P={w.P} io={w.io} "
+          f"tv={w.time_varying}", file=sys.stderr, flush=True)
+
+    # parameters (shared) and rotating input/output sets (> 512 MB in total)
+    lam = torch.from_numpy(w.lam).to(dev)
+    bt = torch.from_numpy(w.b_tilde).to(dev)
+    ct = torch.from_numpy(w.c_tilde).to(dev)
+    d = torch.from_numpy(w.d).to(dev)
+    logd = torch.from_numpy(w.log_delta).to(dev)
+    if w.io == "bf16":
+        u0 = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        u0 = torch.from_numpy(w.u).to(dev)
+    delta0 = torch.from_numpy(w.delta).to(dev) if w.time_varying else None
+    set_bytes = u0.numel() * u0.element_size() * 2 + (delta0.numel() * 4 if delta0 is not None else 0)
+    n_sets = max(4, math.ceil(512e6 / set_bytes))
+    us = [u0] + [u0.clone() for _ in range(n_sets - 1)]
+    ys = [torch.empty_like(u0) for _ in range(n_sets)]
+    deltas = ([delta0] + [delta0.clone() for _ in range(n_sets - 1)]) if delta0 is not None else None
+
+    def step(i):
+        k = i % n_sets
+        if w.time_varying:
+            s5.forward_timevarying(us[k], lam, bt, ct, d, deltas[k], y=ys[k])
+        else:
+            s5.forward(us[k], lam, bt, ct, d, logd, y=ys[k])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s5.set_profiling_events(evs[i][0], evs[i][1])
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    s5.set_profiling_events(None, None)
+    kernel_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens = w.B * w.L
+    value = tokens / (ms_per_step * 1e-3)
+    k_ms = float(np.mean(kernel_ms))
+    flops = algorithmic_flops(w)
+    nbytes = algorithmic_bytes(w)
+    mfma_peak = MFMA_PEAK_TFLOPS[w.io]
+    achieved_tf = flops / (k_ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (k_ms * 1e-3) / 1e9
+    mfma_floor = flops / (mfma_peak * 1e12)
+    hbm_floor = nbytes / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if mfma_floor >= hbm_floor else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel_us"] = round(k_ms * 1e3, 2)
+    roof["per_launch"] = {"flops": flops, "bytes": nbytes}
+    hbm = {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io,
+        "data": "synthetic",
+        "config": {"workload": f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
+                               f"{'_timevarying' if w.time_varying else ''}",
+                   "B": w.B, "L": w.L, "H": w.H, "P": w.P, "io": w.io,
+                   "time_varying": w.time_varying, "buffer_sets": n_sets},
+        "roofline": roof,
+        "hbm": hbm,
+    }
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
+        cb, yo = cpu_baseline(w, args.cpu_repeats, args.cpu_budget)
+        out["cpu_baseline"] = cb
+        yg = ys[(args.warmup + args.steps - 1) % n_sets].float().cpu().numpy().astype(np.float64)
+        rms = math.sqrt(float(np.mean(yo ** 2)))
+        out["parity"] = {"max_err_over_rms": float(np.max(np.abs(yg - yo)) / rms), "tol": w.tol}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,178 @@
+"""S5 layer forward hot path on AMD MI355X (gfx950): Python binding.
+
+Thin ctypes layer over the C ABI in include/s5.h (libs5.so, built in-tree by
+``diagonal_state_space_amd.build_lib``). It only marshals arguments: checks
+device, dtype, shape and contiguity of torch tensors, passes their device
+pointers and the current HIP stream, and turns status codes into exceptions.
+Every step of the computation runs in the library's kernels; PyTorch provides
+device memory and streams. There is no fallback: if libs5.so is missing or a
+GPU is not present, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "S5Error",
+    "S5_F32",
+    "S5_BF16",
+    "S5_MAX_P",
+    "S5_MAX_H",
+    "lib",
+    "lib_path",
+    "discretize",
+    "forward",
+    "forward_timevarying",
+    "set_profiling_events",
+    "status_string",
+]
+
+S5_F32 = 0
+S5_BF16 = 1
+S5_MAX_P = 256
+S5_MAX_H = 512
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libs5.so")
+_lib = None
+
+EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_status_string",
+           "s5_set_profiling_events")
+
+
+class S5Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libs5.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} not found: build it with "
+                              "`python -m diagonal_state_space_amd.build_lib`")
+        L = ctypes.CDLL(lib_path)
+        i64, vp, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.s5_discretize.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
+        L.s5_discretize.restype = st
+        L.s5_forward.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.s5_forward.restype = st
+        L.s5_forward_timevarying.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
+                                             vp, vp, vp, vp]
+        L.s5_forward_timevarying.restype = st
+        L.s5_status_string.argtypes = [st]
+        L.s5_status_string.restype = ctypes.c_char_p
+        L.s5_set_profiling_events.argtypes = [vp, vp]
+        L.s5_set_profiling_events.restype = st
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().s5_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise S5Error(status, where)
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dev_tensor(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return S5_F32
+    if dtype == torch.bfloat16:
+        return S5_BF16
+    raise TypeError(f"u/y must be float32 or bfloat16, got {dtype}")
+
+
+def discretize(lam, b_tilde, log_delta, lam_bar=None, b_bar=None, stream=None):
+    """Zero-order hold: returns (Lambda_bar [P] complex64, B_bar [P,H] complex64)."""
+    import torch
+    P, H = b_tilde.shape
+    _dev_tensor(lam, "lam", torch.complex64, (P,))
+    _dev_tensor(b_tilde, "b_tilde", torch.complex64, (P, H))
+    _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    if lam_bar is None:
+        lam_bar = torch.empty(P, dtype=torch.complex64, device=lam.device)
+    if b_bar is None:
+        b_bar = torch.empty(P, H, dtype=torch.complex64, device=lam.device)
+    _dev_tensor(lam_bar, "lam_bar", torch.complex64, (P,))
+    _dev_tensor(b_bar, "b_bar", torch.complex64, (P, H))
+    _check(lib().s5_discretize(P, H, lam.data_ptr(), b_tilde.data_ptr(), log_delta.data_ptr(),
+                               lam_bar.data_ptr(), b_bar.data_ptr(), _stream_handle(stream)),
+           "s5_discretize")
+    return lam_bar, b_bar
+
+
+def _forward_args(u, lam, b_tilde, c_tilde, d, y):
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be [B, L, H]")
+    B, L, H = u.shape
+    P = lam.shape[0]
+    io = _io_code(u.dtype)
+    _dev_tensor(u, "u", u.dtype, (B, L, H))
+    _dev_tensor(lam, "lam", torch.complex64, (P,))
+    _dev_tensor(b_tilde, "b_tilde", torch.complex64, (P, H))
+    _dev_tensor(c_tilde, "c_tilde", torch.complex64, (H, P))
+    _dev_tensor(d, "d", torch.float32, (H,))
+    if y is None:
+        y = torch.empty_like(u)
+    _dev_tensor(y, "y", u.dtype, (B, L, H))
+    return B, L, H, P, io, y
+
+
+def forward(u, lam, b_tilde, c_tilde, d, log_delta, y=None, stream=None):
+    """Time-invariant S5 forward: y = Re(C~ x_k) + D u_k, shape of u."""
+    import torch
+    B, L, H, P, io, y = _forward_args(u, lam, b_tilde, c_tilde, d, y)
+    _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    _check(lib().s5_forward(B, L, H, P, io, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
+                            c_tilde.data_ptr(), d.data_ptr(), log_delta.data_ptr(), y.data_ptr(),
+                            _stream_handle(stream)), "s5_forward")
+    return y
+
+
+def forward_timevarying(u, lam, b_tilde, c_tilde, d, delta, y=None, stream=None):
+    """S5 forward with one interval per (batch, step, mode): delta [B, L, P]."""
+    import torch
+    B, L, H, P, io, y = _forward_args(u, lam, b_tilde, c_tilde, d, y)
+    _dev_tensor(delta, "delta", torch.float32, (B, L, P))
+    _check(lib().s5_forward_timevarying(B, L, H, P, io, u.data_ptr(), lam.data_ptr(),
+                                        b_tilde.data_ptr(), c_tilde.data_ptr(), d.data_ptr(),
+                                        delta.data_ptr(), y.data_ptr(), _stream_handle(stream)),
+           "s5_forward_timevarying")
+    return y
+
+
+def set_profiling_events(start: Optional[int], stop: Optional[int]) -> None:
+    """Raw hipEvent_t handles (ints) recorded around the fused forward kernel by
+    later calls from this thread; (None, None) turns it off."""
+    _check(lib().s5_set_profiling_events(start, stop), "s5_set_profiling_events")

@@ -1,0 +1,166 @@
+// C ABI of the S5 forward path: host-side validation, stream-ordered scratch
+// memory and dispatch to the kernels. See include/s5.h for the contract.
+#include "s5.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "s5_internal.h"
+
+namespace {
+
+thread_local hipEvent_t tl_ev_start = nullptr;
+thread_local hipEvent_t tl_ev_stop = nullptr;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Test hook: S5_TEST_FAIL_ALLOC=1 makes scratch allocation report failure.
+bool alloc_fail_hook() {
+  const char* v = std::getenv("S5_TEST_FAIL_ALLOC");
+  return v != nullptr && v[0] == '1';
+}
+
+s5_status check_sizes(int64_t P, int64_t H) {
+  if (P < 1 || H < 1) return S5_ERR_INVALID_ARGUMENT;
+  if (P > S5_MAX_P || H > S5_MAX_H) return S5_ERR_UNSUPPORTED;
+  return S5_OK;
+}
+
+s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                         const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                         const float* d, const float* log_delta, const float* delta, void* y,
+                         bool time_varying, hipStream_t stream) {
+  if (B < 0 || L < 0) return S5_ERR_INVALID_ARGUMENT;
+  s5_status st = check_sizes(P, H);
+  if (st != S5_OK) return st;
+  if (io != S5_F32 && io != S5_BF16) return S5_ERR_UNSUPPORTED;
+  const int64_t tokens = B * L;
+  if (B > 0 && L > INT32_MAX / B) return S5_ERR_UNSUPPORTED;
+  if (!lambda || !b_tilde || !c_tilde || !d) return S5_ERR_INVALID_ARGUMENT;
+  if (time_varying ? false : !log_delta) return S5_ERR_INVALID_ARGUMENT;
+  if (tokens > 0 && (!u || !y || (time_varying && !delta))) return S5_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y};
+  for (const void* p : ptrs) {
+    if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
+  }
+  const int64_t es = io == S5_BF16 ? 2 : 4;
+  if (tokens > 0) {
+    const Range ry = range_of(y, tokens * H * es);
+    const Range inputs[] = {range_of(u, tokens * H * es),
+                            range_of(lambda, P * 8),
+                            range_of(b_tilde, P * H * 8),
+                            range_of(c_tilde, H * P * 8),
+                            range_of(d, H * 4),
+                            log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
+                            delta ? range_of(delta, tokens * P * 4) : Range{0, 0}};
+    for (const Range& r : inputs) {
+      if (overlaps(ry, r)) return S5_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (tokens == 0) return S5_OK;
+
+  s5::ForwardArgs a{};
+  a.B = static_cast<int>(B);
+  a.L = static_cast<int>(L);
+  a.H = static_cast<int>(H);
+  a.P = static_cast<int>(P);
+  a.bf16_io = io == S5_BF16;
+  a.time_varying = time_varying;
+  a.u = u;
+  a.lam = reinterpret_cast<const float2*>(lambda);
+  a.b_tilde = reinterpret_cast<const float2*>(b_tilde);
+  a.c_tilde = reinterpret_cast<const float2*>(c_tilde);
+  a.d = d;
+  a.log_delta = log_delta;
+  a.delta = delta;
+  a.y = y;
+
+  if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
+  const size_t bytes = s5::forward_workspace_bytes(a);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
+  if (e != hipSuccess) return S5_ERR_HIP;
+  e = s5::launch_forward(a, ws, stream, tl_ev_start, tl_ev_stop);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
+  return S5_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+s5_status s5_discretize(int64_t P, int64_t H, const s5_c64* lambda, const s5_c64* b_tilde,
+                        const float* log_delta, s5_c64* lambda_bar, s5_c64* b_bar,
+                        hipStream_t stream) {
+  s5_status st = check_sizes(P, H);
+  if (st != S5_OK) return st;
+  if (!lambda || !b_tilde || !log_delta || !lambda_bar || !b_bar) return S5_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {lambda, b_tilde, log_delta, lambda_bar, b_bar};
+  for (const void* p : ptrs) {
+    if (!aligned16(p)) return S5_ERR_UNSUPPORTED;
+  }
+  const Range outs[] = {range_of(lambda_bar, P * 8), range_of(b_bar, P * H * 8)};
+  const Range ins[] = {range_of(lambda, P * 8), range_of(b_tilde, P * H * 8),
+                       range_of(log_delta, P * 4)};
+  if (overlaps(outs[0], outs[1])) return S5_ERR_INVALID_ARGUMENT;
+  for (const Range& o : outs) {
+    for (const Range& i : ins) {
+      if (overlaps(o, i)) return S5_ERR_INVALID_ARGUMENT;
+    }
+  }
+  const hipError_t e = s5::launch_discretize(
+      static_cast<int>(P), static_cast<int>(H), reinterpret_cast<const float2*>(lambda),
+      reinterpret_cast<const float2*>(b_tilde), log_delta, reinterpret_cast<float2*>(lambda_bar),
+      reinterpret_cast<float2*>(b_bar), nullptr, 0, nullptr, stream);
+  return e == hipSuccess ? S5_OK : S5_ERR_HIP;
+}
+
+s5_status s5_forward(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                     const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                     const float* d, const float* log_delta, void* y, hipStream_t stream) {
+  return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
+                        false, stream);
+}
+
+s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
+                                 const void* u, const s5_c64* lambda, const s5_c64* b_tilde,
+                                 const s5_c64* c_tilde, const float* d, const float* delta,
+                                 void* y, hipStream_t stream) {
+  return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, nullptr, delta, y, true,
+                        stream);
+}
+
+const char* s5_status_string(s5_status s) {
+  switch (s) {
+    case S5_OK: return "S5_OK";
+    case S5_ERR_INVALID_ARGUMENT: return "S5_ERR_INVALID_ARGUMENT";
+    case S5_ERR_UNSUPPORTED: return "S5_ERR_UNSUPPORTED";
+    case S5_ERR_OUT_OF_MEMORY: return "S5_ERR_OUT_OF_MEMORY";
+    case S5_ERR_HIP: return "S5_ERR_HIP";
+  }
+  return "S5_ERR_UNKNOWN";
+}
+
+s5_status s5_set_profiling_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return S5_ERR_INVALID_ARGUMENT;
+  tl_ev_start = start;
+  tl_ev_stop = stop;
+  return S5_OK;
+}
+
+}  // extern "C"

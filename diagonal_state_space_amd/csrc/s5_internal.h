@@ -1,0 +1,40 @@
+// Internal launcher declarations shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s5 {
+
+// Discretisation (float64 inside). Any output pointer may be null.
+hipError_t launch_discretize(int P, int H, const float2* lam, const float2* b_tilde,
+                             const float* log_delta, float2* lam_bar, float2* b_bar,
+                             float2* pow_out, int pow_n, float2* inv_lam, hipStream_t stream);
+
+hipError_t launch_inv_lambda(int P, const float2* lam, float2* out, hipStream_t stream);
+
+// Arguments of one forward call after validation on the host.
+struct ForwardArgs {
+  int B, L, H, P;
+  bool bf16_io;
+  bool time_varying;
+  const void* u;
+  const float2* lam;
+  const float2* b_tilde;
+  const float2* c_tilde;
+  const float* d;
+  const float* log_delta;  // time-invariant
+  const float* delta;      // time-varying [B, L, P]
+  void* y;
+};
+
+// Bytes of stream-ordered scratch the forward path needs for these sizes.
+size_t forward_workspace_bytes(const ForwardArgs& a);
+
+// Enqueue the whole forward path on `stream` using `ws` (forward_workspace_bytes
+// bytes, 256-byte aligned). `ev_start` / `ev_stop` (may be null) are recorded
+// around the forward kernels proper (after parameter preparation).
+hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop);
+
+}  // namespace s5

@@ -1,0 +1,159 @@
+/*
+ * s5.h - C ABI of the S5 layer forward hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The S5 layer ("Simplified State Space Layers for Sequence Modeling", Smith,
+ * Warrington & Linderman, ICLR 2023) maps an input sequence u_k in R^H to
+ * pre-activation outputs y_k in R^H through a diagonal complex linear state
+ * x_k in C^P:
+ *
+ *   zero-order hold (paper eq. 6; App. A `discretize`):
+ *       Lambda_bar = exp(Lambda * Delta),
+ *       B_bar      = ((Lambda_bar - 1) / Lambda)[:, None] * B~
+ *   recurrence (paper eq. 2, evaluated as an associative scan, Sec. 2.2/App. H):
+ *       x_k = Lambda_bar * x_{k-1} + B_bar u_k,    x_{-1} = 0
+ *   readout with diagonal feedthrough (App. A `apply_ssm`; paper eq. 5):
+ *       y_k = Re(C~ x_k) + D * u_k          (full spectrum, factor 1)
+ *
+ * The time-varying variant (paper Sec. 3.3 and 6.3: a different
+ * discretisation for every observation interval) uses one interval per
+ * (batch, step, mode): Lambda_bar_k = exp(Lambda * Delta_k) and
+ * B_bar_k = ((Lambda_bar_k - 1)/Lambda)[:, None] * B~ with the interval Delta_k
+ * that ends at step k.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer to caller-owned, contiguous,
+ *   row-major memory, aligned to at least 16 bytes. The library never frees
+ *   or retains a caller pointer after the call returns.
+ * - Complex values are interleaved (re, im) float32 pairs: `s5_c64`, the
+ *   layout of torch.complex64 and numpy.complex64.
+ * - Every call is asynchronous on `stream` (NULL = the null stream) and does
+ *   not synchronise the host. Internal scratch memory is taken from HIP's
+ *   stream-ordered allocator on `stream` and released on it.
+ * - Arguments are validated on the host before anything is enqueued; a call
+ *   that returns an error has enqueued nothing. Errors of kernels that run
+ *   later surface at the caller's next synchronisation with the stream.
+ * - Device data is not inspected: intervals must be finite and >= 0 (the
+ *   pages reject other intervals); NaN or Inf inputs propagate causally
+ *   (a bad u[b,k,:] affects only y[b,k',:] with k' >= k).
+ * - The output y must not overlap any input.
+ * - Calls are re-entrant and may run concurrently on different streams.
+ */
+#ifndef S5_H
+#define S5_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque HIP handles, declared identically to hip_runtime_api.h. */
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef struct {
+  float re;
+  float im;
+} s5_c64;
+
+/* Element type of u and y (both have the same type). */
+typedef enum { S5_F32 = 0, S5_BF16 = 1 } s5_dtype;
+
+typedef enum {
+  S5_OK = 0,
+  S5_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, overlapping output */
+  S5_ERR_UNSUPPORTED = 2,      /* dtype, size limit or alignment not supported */
+  S5_ERR_OUT_OF_MEMORY = 3,    /* scratch allocation failed */
+  S5_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} s5_status;
+
+/* Size limits of the compiled kernels. */
+#define S5_MAX_P 256  /* complex modes */
+#define S5_MAX_H 512  /* input/output features */
+
+/*
+ * s5_discretize - zero-order hold of the diagonal system (paper eq. 6;
+ * App. A `discretize`; abhik.ai review, row 2 "Integrate a held input
+ * exactly").
+ *
+ *   P, H        number of complex modes (1..S5_MAX_P), features (1..S5_MAX_H)
+ *   lambda      [P]    continuous eigenvalues Lambda
+ *   b_tilde     [P,H]  input matrix B~
+ *   log_delta   [P]    float32 log of the per-mode interval, Delta = exp(.)
+ *   lambda_bar  [P]    out: exp(Lambda * Delta)
+ *   b_bar       [P,H]  out: ((Lambda_bar - 1)/Lambda) * B~ row-wise; for
+ *                      |Lambda*Delta| < 1e-4 the gain is Delta*phi1(Lambda*Delta)
+ *                      (the removable singularity at Lambda = 0 gives Delta)
+ * Internally float64; outputs rounded to float32.
+ * Errors: S5_ERR_INVALID_ARGUMENT for a null pointer or P, H < 1;
+ *         S5_ERR_UNSUPPORTED for P > S5_MAX_P or H > S5_MAX_H or misalignment.
+ */
+s5_status s5_discretize(int64_t P, int64_t H, const s5_c64* lambda, const s5_c64* b_tilde,
+                        const float* log_delta, s5_c64* lambda_bar, s5_c64* b_bar,
+                        hipStream_t stream);
+
+/*
+ * s5_forward - time-invariant S5 forward pass (App. A `apply_ssm` composed
+ * with `discretize`; per-mode intervals Delta = exp(log_delta), paper Sec. 3.2).
+ *
+ *   B, L        batch size and sequence length (>= 0; B*L == 0 is a no-op)
+ *   H, P        features (1..S5_MAX_H) and complex modes (1..S5_MAX_P)
+ *   io          element type of u and y
+ *   u           [B,L,H] input
+ *   lambda      [P]     continuous eigenvalues
+ *   b_tilde     [P,H]   input matrix B~
+ *   c_tilde     [H,P]   output matrix C~
+ *   d           [H]     float32 diagonal feedthrough D
+ *   log_delta   [P]     float32 log interval per mode
+ *   y           [B,L,H] out: pre-activation Re(C~ x_k) + D u_k, rounded to
+ *                       `io` (bf16: round to nearest even)
+ * Precision: the state and all accumulation are float32. Products with B_bar
+ * and C~ run on the matrix cores: bf16 operands for bf16 io; for float32 io
+ * each float32 operand is split into a high and a low bf16 part and three
+ * products are summed (about 2^-16 relative per product).
+ * Errors: S5_ERR_INVALID_ARGUMENT (null pointer, negative B or L, P or H < 1,
+ * y overlapping an input), S5_ERR_UNSUPPORTED (unknown io, size limits,
+ * misalignment), S5_ERR_OUT_OF_MEMORY, S5_ERR_HIP.
+ */
+s5_status s5_forward(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                     const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                     const float* d, const float* log_delta, void* y, hipStream_t stream);
+
+/*
+ * s5_forward_timevarying - S5 forward pass with one interval per
+ * (batch, step, mode), for irregularly sampled sequences (paper Sec. 3.3
+ * "provide a different Lambda_bar_k at each step" and Sec. 6.3; abhik.ai
+ * review, "Sampling intervals carry physical meaning").
+ *
+ * Arguments as s5_forward, except
+ *   delta       [B,L,P] float32 interval Delta_k for step k and mode p
+ *               (precondition: finite and >= 0; a zero interval is the
+ *               identity step with zero input gain)
+ * Step k uses Delta_k in both Lambda_bar_k and B_bar_k.
+ * Errors: as s5_forward.
+ */
+s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
+                                 const void* u, const s5_c64* lambda, const s5_c64* b_tilde,
+                                 const s5_c64* c_tilde, const float* d, const float* delta,
+                                 void* y, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* s5_status_string(s5_status s);
+
+/*
+ * s5_set_profiling_events - measurement hook for benchmarks. When both
+ * events are non-NULL, every later s5_forward / s5_forward_timevarying call
+ * made from the calling host thread records `start` on its stream right
+ * before the fused forward kernel and `stop` right after it, so that
+ * hipEventElapsedTime gives that kernel's duration alone. Passing NULL for
+ * both turns the hook off. The setting is per host thread.
+ * Errors: S5_ERR_INVALID_ARGUMENT if exactly one event is NULL.
+ */
+s5_status s5_set_profiling_events(hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S5_H */

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/s5.h declares, and host-side validation returns the documented
+status codes before anything is enqueued (fake, aligned pointers are never
+dereferenced on these paths)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import diagonal_state_space_amd as s5
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s5.h")
+
+OK, INVALID, UNSUPPORTED, OOM, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s5_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = s5.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported by {s5.lib_path}"
+    out = subprocess.run(["nm", "-D", "--defined-only", s5.lib_path], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (s5_[a-z_]+)", out.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    assert s5.status_string(OK) == "S5_OK"
+    assert s5.status_string(INVALID) == "S5_ERR_INVALID_ARGUMENT"
+    assert s5.status_string(UNSUPPORTED) == "S5_ERR_UNSUPPORTED"
+    assert s5.status_string(OOM) == "S5_ERR_OUT_OF_MEMORY"
+    assert s5.status_string(HIPERR) == "S5_ERR_HIP"
+    assert s5.status_string(99) == "S5_ERR_UNKNOWN"
+
+
+def _fwd(B=2, L=8, H=4, P=3, io=0, u=FAKE, lam=FAKE + 0x1000, bt=FAKE + 0x2000, ct=FAKE + 0x3000,
+         d=FAKE + 0x4000, logd=FAKE + 0x5000, y=FAKE + 0x100000):
+    return s5.lib().s5_forward(B, L, H, P, io, u, lam, bt, ct, d, logd, y, None)
+
+
+def _fwd_tv(B=2, L=8, H=4, P=3, io=0, u=FAKE, delta=FAKE + 0x6000, y=FAKE + 0x100000, **kw):
+    return s5.lib().s5_forward_timevarying(B, L, H, P, io, u, FAKE + 0x1000, FAKE + 0x2000,
+                                           FAKE + 0x3000, FAKE + 0x4000, delta, y, None)
+
+
+def test_forward_validation():
+    assert _fwd(u=None) == INVALID
+    assert _fwd(y=None) == INVALID
+    assert _fwd(lam=None) == INVALID
+    assert _fwd(bt=None) == INVALID
+    assert _fwd(ct=None) == INVALID
+    assert _fwd(d=None) == INVALID
+    assert _fwd(logd=None) == INVALID
+    assert _fwd(B=-1) == INVALID
+    assert _fwd(L=-5) == INVALID
+    assert _fwd(P=0) == INVALID
+    assert _fwd(H=0) == INVALID
+    assert _fwd(P=s5.S5_MAX_P + 1) == UNSUPPORTED
+    assert _fwd(H=s5.S5_MAX_H + 1) == UNSUPPORTED
+    assert _fwd(io=7) == UNSUPPORTED
+    assert _fwd(u=FAKE + 4) == UNSUPPORTED           # misaligned
+    assert _fwd(y=FAKE + 0x100008) == UNSUPPORTED
+    # y overlapping u / a parameter
+    assert _fwd(y=FAKE + 16) == INVALID
+    assert _fwd(y=FAKE + 0x3000) == INVALID
+
+
+def test_empty_is_noop():
+    # B*L == 0 validates and returns before touching the device
+    assert _fwd(B=0) == OK
+    assert _fwd(L=0) == OK
+    assert _fwd(B=0, u=None, y=None) == OK
+    assert _fwd_tv(L=0, delta=None) == OK
+
+
+def test_timevarying_validation():
+    assert _fwd_tv(delta=None) == INVALID
+    assert _fwd_tv(delta=FAKE + 0x6004) == UNSUPPORTED
+    assert _fwd_tv(y=FAKE + 0x6000) == INVALID   # y overlaps delta
+
+
+def test_discretize_validation():
+    f = s5.lib().s5_discretize
+    a = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, FAKE + 0x4000]
+    assert f(4, 3, None, a[1], a[2], a[3], a[4], None) == INVALID
+    assert f(0, 3, *a, None) == INVALID
+    assert f(4, 0, *a, None) == INVALID
+    assert f(s5.S5_MAX_P + 1, 3, *a, None) == UNSUPPORTED
+    assert f(4, 3, a[0], a[1], a[2], a[0], a[4], None) == INVALID   # output overlaps input
+    assert f(4, 3, a[0], a[1], a[2] + 4, a[3], a[4], None) == UNSUPPORTED
+
+
+def test_profiling_events_validation():
+    L = s5.lib()
+    assert L.s5_set_profiling_events(FAKE, None) == INVALID
+    assert L.s5_set_profiling_events(None, None) == OK
+
+
+def test_alloc_failure_hook():
+    # forced from the host in a child process; returns before any HIP call
+    code = (
+        "import diagonal_state_space_amd as s5;"
+        "r = s5.lib().s5_forward(2, 8, 4, 3, 0, 0x10000, 0x11000, 0x12000, 0x13000, 0x14000,"
+        " 0x15000, 0x110000, None); print(r)"
+    )
+    env = dict(os.environ, S5_TEST_FAIL_ALLOC="1")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=120)
+    assert out.stdout.strip() == str(OOM), out.stderr
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    u = torch.zeros(1, 4, 2)
+    with pytest.raises(ValueError):
+        s5.forward(u, torch.zeros(3, dtype=torch.complex64), torch.zeros(3, 2, dtype=torch.complex64),
+                   torch.zeros(2, 3, dtype=torch.complex64), torch.zeros(2), torch.zeros(3))
