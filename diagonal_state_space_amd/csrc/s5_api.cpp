@@ -88,6 +88,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.delta = delta;
   a.y = y;
 
+  if (!s5::forward_supported(a)) return S5_ERR_UNSUPPORTED;
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
   const size_t bytes = s5::forward_workspace_bytes(a);
   void* ws = nullptr;

@@ -33,31 +33,54 @@ __device__ __forceinline__ cf cfma(cf a, cf x, cf b) {
   return {fmaf(a.re, x.re, fmaf(-a.im, x.im, b.re)), fmaf(a.re, x.im, fmaf(a.im, x.re, b.im))};
 }
 
-// Zero-order hold of one mode in float32 for an interval dt >= 0:
-//   abar = exp(lam*dt),  gain = (abar - 1)/lam.
-// abar - 1 is formed without cancellation from s = sin(w/2), c = cos(w/2),
-// w = Im(lam)*dt:  cos(w) - 1 = -2 s^2,  sin(w) = 2 s c,  so
-//   abar - 1 = (expm1(r)(1 - 2 s^2) - 2 s^2,  e^r 2 s c),   r = Re(lam)*dt.
-// `inv_lam` is 1/lam, computed once per mode. For |lam*dt| < 1e-4 the gain is
-// dt*(1 + z/2 + z^2/6), the leading terms of dt*phi1(z) (phi1(z) = (e^z-1)/z),
-// which also covers lam = 0 (gain = dt).
-__device__ __forceinline__ void zoh_f32(cf lam, cf inv_lam, float dt, cf& abar, cf& gain) {
-  const float r = lam.re * dt;
-  const float w = lam.im * dt;
-  if (fabsf(r) + fabsf(w) < 1e-4f) {
-    const float er = expf(r);
-    float sw, cw;
-    sincosf(w, &sw, &cw);
-    abar = {er * cw, er * sw};
-    // z/2 + z^2/6
-    const float hr = 0.5f * r + (r * r - w * w) * (1.0f / 6.0f);
-    const float hi = 0.5f * w + (2.0f * r * w) * (1.0f / 6.0f);
-    gain = {dt * (1.0f + hr), dt * hi};
-    return;
+// sin and cos of 2*pi*t for |t| <= 1/2 revolution (t exact): octant
+// reduction to |x| <= pi/4, then Taylor polynomials (truncation below 3e-8
+// absolute; relative accuracy is kept for small t).
+__device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
+  const float qf = rintf(4.0f * t);               // quadrant, -2..2
+  const float f = fmaf(-0.25f, qf, t);            // exact: |f| <= 1/8
+  const float x = 6.28318530717958647692f * f;
+  const float x2 = x * x;
+  float sp = fmaf(x2, 2.7557319e-6f, -1.98412698e-4f);
+  sp = fmaf(x2, sp, 8.33333333e-3f);
+  sp = fmaf(x2, sp, -1.66666667e-1f);
+  const float sx = fmaf(x * x2, sp, x);
+  float cp = fmaf(x2, 2.48015873e-5f, -1.38888889e-3f);
+  cp = fmaf(x2, cp, 4.16666667e-2f);
+  cp = fmaf(x2, cp, -0.5f);
+  const float cx = fmaf(x2, cp, 1.0f);
+  const int q = static_cast<int>(qf) & 3;
+  s = (q == 0) ? sx : (q == 1) ? cx : (q == 2) ? -sx : -cx;
+  c = (q == 0) ? cx : (q == 1) ? -sx : (q == 2) ? -cx : sx;
+}
+
+// e^r - 1: degree-8 Taylor polynomial for |r| < 1/2 (truncation < 3e-9
+// relative), exp(r) - 1 otherwise (no cancellation there).
+__device__ __forceinline__ float expm1_small(float r) {
+  if (fabsf(r) < 0.5f) {
+    float p = fmaf(r, 2.48015873e-5f, 1.98412698e-4f);
+    p = fmaf(r, p, 1.38888889e-3f);
+    p = fmaf(r, p, 8.33333333e-3f);
+    p = fmaf(r, p, 4.16666667e-2f);
+    p = fmaf(r, p, 1.66666667e-1f);
+    p = fmaf(r, p, 0.5f);
+    return fmaf(r * r, p, r);
   }
+  return __expf(r) - 1.0f;
+}
+
+// Zero-order hold of one mode for a per-step interval dt >= 0 (the
+// time-varying path), with the half-angle taken in revolutions:
+//   w/2 = Im(lam) dt / 2 = 2 pi th,  th = dt * Im(lam)/(4 pi) = dt * hrev.
+// The integer part of th is removed exactly (rint), so the angle's only error
+// is the rounding of th itself, the same as rounding w. Then as zoh_f32:
+//   abar - 1 = (expm1(r)(1 - 2 s^2) - 2 s^2,  e^r 2 s c),  gain = (abar - 1)/lam.
+__device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
+  const float r = lam.re * dt;
+  const float th = hrev * dt;
   float s, c;
-  sincosf(0.5f * w, &s, &c);
-  const float em1 = expm1f(r);
+  sincos_rev(th - rintf(th), s, c);
+  const float em1 = expm1_small(r);
   const float er = em1 + 1.0f;
   const float two_s2 = 2.0f * s * s;
   const float cosw = 1.0f - two_s2;
@@ -65,6 +88,13 @@ __device__ __forceinline__ void zoh_f32(cf lam, cf inv_lam, float dt, cf& abar, 
   abar = {er * cosw, er * sinw};
   const cf am1 = {fmaf(em1, cosw, -two_s2), er * sinw};
   gain = cmul(am1, inv_lam);
+  // |z| < 1e-4 (also covers lam = 0): dt * (1 + z/2 + z^2/6)
+  const float w = lam.im * dt;
+  if (fabsf(r) + fabsf(w) < 1e-4f) {
+    const float hr = 0.5f * r + (r * r - w * w) * (1.0f / 6.0f);
+    const float hi = 0.5f * w + (2.0f * r * w) * (1.0f / 6.0f);
+    gain = {dt * (1.0f + hr), dt * hi};
+  }
 }
 
 }  // namespace s5

@@ -31,6 +31,9 @@ struct ForwardArgs {
 // Bytes of stream-ordered scratch the forward path needs for these sizes.
 size_t forward_workspace_bytes(const ForwardArgs& a);
 
+// Whether a compiled kernel instance covers these sizes.
+bool forward_supported(const ForwardArgs& a);
+
 // Enqueue the whole forward path on `stream` using `ws` (forward_workspace_bytes
 // bytes, 256-byte aligned). `ev_start` / `ev_stop` (may be null) are recorded
 // around the forward kernels proper (after parameter preparation).

@@ -1,8 +1,13 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on
 the same seeded inputs, element by element.
 
-Acceptance: max|y_gpu - y_oracle| / rms(y_oracle) <= 2e-4 for float32 I/O and
-<= 2e-2 for bfloat16 I/O (the oracle output is not rounded)."""
+Acceptance on the five workloads: max|y_gpu - y_oracle| / rms(y_oracle) <= 2e-4
+for float32 I/O and <= 2e-2 for bfloat16 I/O (the oracle output is not rounded).
+
+Other bfloat16 cases (random shapes whose outputs can have a large peak-to-RMS
+ratio) use the same bound plus the output format's own rounding:
+|y_gpu - y_oracle| <= 2e-2 * rms(y_oracle) + 2^-8 * |y_oracle| elementwise,
+where 2^-8 is the unit roundoff of round-to-nearest bfloat16."""
 
 import math
 
@@ -71,7 +76,14 @@ def rel_err(y_gpu, y_ref):
     return float(np.max(np.abs(yg - y_ref))) / rms
 
 
-def check(w, label=""):
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+def check(w, label="", storage_allowance=None):
+    """Compare one workload; ``storage_allowance`` (default: bf16 I/O outside
+    the five named workloads) adds the bf16 output rounding bound."""
+    if storage_allowance is None:
+        storage_allowance = w.io == "bf16" and not w.name.startswith("cfg")
     print(f"[parity] {w.name} B={w.B} L={w.L} H={w.H} P={w.P} io={w.io} tv={w.time_varying} {label}",
           flush=True)
     y = run_gpu(w)
@@ -79,7 +91,15 @@ def check(w, label=""):
     assert torch.isfinite(y.float()).all()
     err = rel_err(y, yo)
     print(f"[parity]   err/rms = {err:.3e} (tol {w.tol:.0e})", flush=True)
-    assert err <= w.tol, f"{w.name}: max err / rms = {err:.3e} > {w.tol}"
+    if storage_allowance:
+        yg = y.float().cpu().numpy().astype(np.float64)
+        rms = math.sqrt(float(np.mean(yo ** 2)))
+        excess = np.abs(yg - yo) - BF16_UNIT_ROUNDOFF * np.abs(yo)
+        worst = float(np.max(excess)) / rms
+        print(f"[parity]   beyond bf16 storage rounding: {worst:.3e} of rms", flush=True)
+        assert worst <= w.tol, f"{w.name}: {worst:.3e} > {w.tol} beyond output rounding"
+    else:
+        assert err <= w.tol, f"{w.name}: max err / rms = {err:.3e} > {w.tol}"
     return err
 
 
@@ -146,11 +166,14 @@ def test_output_fully_written_nan_poison():
     assert torch.isfinite(y.float()).all()
 
 
-def test_run_to_run_bitwise_determinism():
-    w = wl.make_config(1, B=8)
+@pytest.mark.parametrize("cfg,B,reps", [(1, 8, 20), (3, 2, 10), (4, 1, 5)])
+def test_run_to_run_bitwise_determinism(cfg, B, reps):
+    # long sequences keep hundreds of chunks of one sequence in flight, so the
+    # look-back takes different paths from run to run; the output must not change
+    w = wl.make_config(cfg, B=B)
     t = dev(w)
     ref = run_gpu(w, t).clone()
-    for _ in range(20):
+    for _ in range(reps):
         assert torch.equal(run_gpu(w, t), ref)
 
 
