@@ -7,9 +7,15 @@ bf16 u/y (the Path-X-shaped configuration). The step rotates over several
 input/output buffer sets whose total exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line with the contract fields plus
-  roofline      dominant kernel (the fused forward kernels, timed with HIP
-                events recorded by the library around them on the call's stream)
-  hbm           the same kernel against the HBM roofline (algorithmic bytes)
+  roofline      dominant kernel: the state and output pass (k_scan: drive,
+                scan and readout), timed with HIP events that the library
+                records around that launch on the call's stream; its
+                algorithmic work is the two complex projections, 8*P*H flops
+                per token
+  kernels       average duration of each of the three launches of one call
+                (packing, aggregate pass k_reduce, k_scan)
+  hbm           the layer's algorithmic bytes (u in, y out, Delta in) over the
+                summed duration of the three launches
   cpu_baseline  the float64 oracle timed on this host's cores
   parity        max |y - y_oracle| / rms(y_oracle) of the benchmark's output
 """
@@ -166,29 +172,30 @@ def main() -> int:
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    evs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    evs = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        s5.set_profiling_events(evs[i][0], evs[i][1])
+        s5.set_profiling_events(evs[i])
         step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    s5.set_profiling_events(None, None)
-    kernel_ms = [ev.elapsed_ms(a, b) for a, b in evs]
-    for a, b in evs:
-        ev.destroy(a)
-        ev.destroy(b)
+    s5.set_profiling_events(None)
+    launch_ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(3)] for e in evs])
+    for e in evs:
+        for h in e:
+            ev.destroy(h)
+    kernel_ms = launch_ms[:, 2]
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens = w.B * w.L
     value = tokens / (ms_per_step * 1e-3)
     k_ms = float(np.mean(kernel_ms))
+    mean_ms = launch_ms.mean(axis=0)
     flops = algorithmic_flops(w)
     nbytes = algorithmic_bytes(w)
     mfma_peak = MFMA_PEAK_TFLOPS[w.io]
     achieved_tf = flops / (k_ms * 1e-3) / 1e12
-    achieved_gbs = nbytes / (k_ms * 1e-3) / 1e9
     mfma_floor = flops / (mfma_peak * 1e12)
     hbm_floor = nbytes / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if mfma_floor >= hbm_floor else "hbm"
@@ -196,12 +203,20 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4), "traffic": None}
     else:
-        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        a_gbs = nbytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "k_scan"
     roof["kernel_us"] = round(k_ms * 1e3, 2)
     roof["per_launch"] = {"flops": flops, "bytes": nbytes}
+    kernels = {"pack_us": round(float(mean_ms[0]) * 1e3, 2),
+               "reduce_us": round(float(mean_ms[1]) * 1e3, 2),
+               "scan_us": round(float(mean_ms[2]) * 1e3, 2),
+               "reduce_flops": flops // 2}
+    fwd_ms = float(mean_ms.sum())
+    achieved_gbs = nbytes / (fwd_ms * 1e-3) / 1e9
     hbm = {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "over": "pack + reduce + scan"}
 
     out = {
         "metric": METRIC,
@@ -221,6 +236,7 @@ def main() -> int:
                    "B": w.B, "L": w.L, "H": w.H, "P": w.P, "io": w.io,
                    "time_varying": w.time_varying, "buffer_sets": n_sets},
         "roofline": roof,
+        "kernels": kernels,
         "hbm": hbm,
     }
 

@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.s5_forward_timevarying.restype = st
         L.s5_status_string.argtypes = [st]
         L.s5_status_string.restype = ctypes.c_char_p
-        L.s5_set_profiling_events.argtypes = [vp, vp]
+        L.s5_set_profiling_events.argtypes = [vp, ctypes.c_int]
         L.s5_set_profiling_events.restype = st
         _lib = L
     return _lib
@@ -172,7 +172,11 @@ def forward_timevarying(u, lam, b_tilde, c_tilde, d, delta, y=None, stream=None)
     return y
 
 
-def set_profiling_events(start: Optional[int], stop: Optional[int]) -> None:
-    """Raw hipEvent_t handles (ints) recorded around the fused forward kernel by
-    later calls from this thread; (None, None) turns it off."""
-    _check(lib().s5_set_profiling_events(start, stop), "s5_set_profiling_events")
+def set_profiling_events(events) -> None:
+    """Raw hipEvent_t handles (ints), an even number up to 6: events[2k] and
+    events[2k+1] are recorded around the k-th kernel launch (0 packing, 1
+    aggregate pass, 2 state and output pass) of later forward calls from this
+    thread. An empty sequence (or None) turns the hook off."""
+    events = list(events or [])
+    arr = (ctypes.c_void_p * max(1, len(events)))(*events) if events else None
+    _check(lib().s5_set_profiling_events(arr, len(events)), "s5_set_profiling_events")

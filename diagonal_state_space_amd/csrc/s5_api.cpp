@@ -11,8 +11,8 @@
 
 namespace {
 
-thread_local hipEvent_t tl_ev_start = nullptr;
-thread_local hipEvent_t tl_ev_stop = nullptr;
+thread_local hipEvent_t tl_events[S5_PROFILING_MAX_EVENTS] = {};
+thread_local int tl_nevents = 0;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -95,7 +95,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   hipError_t e = hipMallocAsync(&ws, bytes, stream);
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
-  e = s5::launch_forward(a, ws, stream, tl_ev_start, tl_ev_stop);
+  e = s5::launch_forward(a, ws, stream, tl_events, tl_nevents);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
   return S5_OK;
@@ -157,10 +157,14 @@ const char* s5_status_string(s5_status s) {
   return "S5_ERR_UNKNOWN";
 }
 
-s5_status s5_set_profiling_events(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr)) return S5_ERR_INVALID_ARGUMENT;
-  tl_ev_start = start;
-  tl_ev_stop = stop;
+s5_status s5_set_profiling_events(const hipEvent_t* events, int count) {
+  if (count < 0 || count > S5_PROFILING_MAX_EVENTS || (count & 1) != 0) return S5_ERR_INVALID_ARGUMENT;
+  if (count > 0 && events == nullptr) return S5_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < count; ++i) {
+    if (events[i] == nullptr) return S5_ERR_INVALID_ARGUMENT;
+  }
+  for (int i = 0; i < S5_PROFILING_MAX_EVENTS; ++i) tl_events[i] = i < count ? events[i] : nullptr;
+  tl_nevents = count;
   return S5_OK;
 }
 

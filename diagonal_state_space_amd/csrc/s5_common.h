@@ -97,4 +97,52 @@ __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float d
   }
 }
 
+// ---- MFMA operand types and helpers ----------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint4* p) { return *p; }
+
+// relaxed agent-scope accesses: not cached in the (per-XCD) L2
+__device__ __forceinline__ void st_agent(float2* p, cf v) {
+  const uint64_t bits = (static_cast<uint64_t>(__float_as_uint(v.im)) << 32) | __float_as_uint(v.re);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ cf ld_agent(const float2* p) {
+  const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  return {__uint_as_float(static_cast<uint32_t>(bits)), __uint_as_float(static_cast<uint32_t>(bits >> 32))};
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_io(const void* p, size_t i) {
+  if constexpr (BF16) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  } else {
+    return static_cast<const float*>(p)[i];
+  }
+}
+
+
+// Write 8 float values as bf16 hi (and lo if `lo` is non-null) fragments.
+__device__ __forceinline__ void put_frag(const float (&v)[8], uint4* hi, uint4* lo) {
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v[i];
+  const bf16x8 h = __builtin_convertvector(f, bf16x8);
+  *hi = as_u4(h);
+  if (lo) {
+    const f32x8 back = __builtin_convertvector(h, f32x8);
+    *lo = as_u4(__builtin_convertvector(f - back, bf16x8));
+  }
+}
+
 }  // namespace s5

@@ -1,81 +1,155 @@
-// Host side of the S5 forward path: workspace layout and the two launches
-// (parameter packing, then the fused chunk kernel), both on the caller's stream.
+// Host side of the S5 forward path: launch plan, workspace layout and the
+// three launches (parameter packing, aggregate pass, state and output pass),
+// all on the caller's stream.
+#include <algorithm>
+#include <cstdlib>
+
 #include "s5_fused.h"
 #include "s5_internal.h"
 
 namespace s5 {
+
+using fused::kStreams;
+
+void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p) {
+  const int MPW = Ppad / 64, KS = Hpad / 32, K2 = Ppad / 16, NP = bf16_io ? 1 : 2;
+  const size_t lds_max = 160 * 1024;
+  p.R = 0;
+  // bf16 instances are compiled for R = 2 (which always fits); float32 ones
+  // also for R = 1, taken where two R = 2 x tiles and u tiles exceed the LDS
+  const int cand[2] = {2, 1};
+  for (int R : cand) {
+    if (bf16_io && R != 2) continue;
+    const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io);
+    const size_t ls = lr + 2 * fused::x_tile_bytes(K2, R, bf16_io);
+    if (ls > lds_max) continue;
+    p.R = R;
+    p.lds_reduce = lr;
+    p.lds_scan = ls;
+    break;
+  }
+  // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
+  // 16 MPW NP fragments of 16 bytes per lane; the time-varying step's own
+  // registers leave room for them up to two mode tiles per wave
+  p.keep = p.R == 2 && KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
+  // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
+  if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
+    if (env[0] == '0') p.keep = false;
+  }
+}
+
+void fused_split(int B, int L, int ncu, FusedPlan& p) {
+  const int per = kStreams * p.R;                  // tokens of one chunk of a range
+  const int chunks = (L + per - 1) / per;          // chunks with a single range
+  int Q = std::max(1, (ncu + B - 1) / B);          // ranges per sequence to fill the CUs
+  Q = std::max(1, std::min(Q, chunks));
+  p.nck = (L + Q * per - 1) / (Q * per);
+  p.Lseg = p.R * p.nck;
+  p.Q = (L + kStreams * p.Lseg - 1) / (kStreams * p.Lseg);
+}
 
 namespace {
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-  int Ppad, Hpad, T, nch;
-  size_t bpack, cpack, modes, flags, ticket, agg, agg_a, incl, total;
+  FusedPlan plan;
+  int Ppad, Hpad;
+  size_t bpack, cpack, modes, sagg, sagg_a, tot, tot_a, total;
 };
+
+int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return ncu;
+}
 
 Layout layout(const ForwardArgs& a) {
   Layout l{};
   l.Ppad = ((a.P + 63) / 64) * 64;
   l.Hpad = ((a.H + 31) / 32) * 32;
-  l.T = fused_chunk_tokens(a.bf16_io, a.time_varying, l.Ppad, l.Hpad);
-  if (l.T == 0) return l;
-  l.nch = (a.L + l.T - 1) / l.T;
+  fused_shape(a.bf16_io, a.time_varying, l.Ppad, l.Hpad, l.plan);
+  if (l.plan.R == 0) return l;
+  const int ncu = device_cus();
+  fused_split(a.B, a.L, ncu > 0 ? ncu : 256, l.plan);
   const size_t planes = a.bf16_io ? 1 : 2;
   const size_t nb = static_cast<size_t>(l.Ppad / 16) * 2 * (l.Hpad / 32) * 64;
   const size_t nc = static_cast<size_t>(l.Hpad / 16) * (2 * l.Ppad / 32) * 64;
-  const size_t nflags = static_cast<size_t>(a.B) * l.nch;
-  const size_t nagg = nflags * l.Ppad;
+  const size_t nranges = static_cast<size_t>(a.B) * l.plan.Q;
   size_t off = 0;
   l.bpack = off;  off += align_up(planes * nb * 16);
   l.cpack = off;  off += align_up(planes * nc * 16);
   l.modes = off;  off += align_up(l.Ppad * sizeof(ModeParams));
-  l.flags = off;  off += align_up(nflags * sizeof(unsigned));
-  l.ticket = off; off += align_up(sizeof(unsigned));
-  l.agg = off;    off += align_up(nagg * sizeof(float2));
-  l.agg_a = off;  off += a.time_varying ? align_up(nagg * sizeof(float2)) : 0;
-  l.incl = off;   off += align_up(nagg * sizeof(float2));
+  l.sagg = off;   off += align_up(nranges * kStreams * l.Ppad * sizeof(float2));
+  l.sagg_a = off; off += a.time_varying ? align_up(nranges * kStreams * l.Ppad * sizeof(float2)) : 0;
+  l.tot = off;    off += align_up(nranges * l.Ppad * sizeof(float2));
+  l.tot_a = off;  off += align_up(nranges * l.Ppad * sizeof(float2));
   l.total = off;
   return l;
 }
 
+using Launcher = hipError_t (*)(const FusedParams&, const FusedPlan&, hipStream_t);
+
+hipError_t timed(int k, const hipEvent_t* ev, int nev, hipStream_t s, hipError_t (*fn)(const FusedParams&, const FusedPlan&, hipStream_t),
+                 const FusedParams& q, const FusedPlan& p) {
+  const bool rec = ev != nullptr && 2 * k + 1 < nev;
+  if (rec) (void)hipEventRecord(ev[2 * k], s);
+  const hipError_t e = fn(q, p, s);
+  if (rec) (void)hipEventRecord(ev[2 * k + 1], s);
+  return e;
+}
+
+hipError_t pack_launcher(const FusedParams& q, const FusedPlan&, hipStream_t s) { return launch_pack(q, s); }
+
 }  // namespace
+
+hipError_t launch_reduce(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  if (q.bf16_io) return q.time_varying ? launch_reduce_bf16_tv(q, p, s) : launch_reduce_bf16_ti(q, p, s);
+  return q.time_varying ? launch_reduce_f32_tv(q, p, s) : launch_reduce_f32_ti(q, p, s);
+}
+
+hipError_t launch_scan(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  if (q.bf16_io) return q.time_varying ? launch_scan_bf16_tv(q, p, s) : launch_scan_bf16_ti(q, p, s);
+  return q.time_varying ? launch_scan_f32_tv(q, p, s) : launch_scan_f32_ti(q, p, s);
+}
 
 size_t forward_workspace_bytes(const ForwardArgs& a) {
   const Layout l = layout(a);
-  return l.T == 0 ? 0 : l.total;
+  return l.plan.R == 0 ? 0 : l.total;
 }
 
-bool forward_supported(const ForwardArgs& a) { return layout(a).T != 0; }
+bool forward_supported(const ForwardArgs& a) {
+  FusedPlan p;
+  fused_shape(a.bf16_io, a.time_varying, ((a.P + 63) / 64) * 64, ((a.H + 31) / 32) * 32, p);
+  return p.R != 0;
+}
 
-hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, hipEvent_t ev_start,
-                          hipEvent_t ev_stop) {
+hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, const hipEvent_t* ev, int nev) {
   const Layout l = layout(a);
-  if (l.T == 0) return hipErrorInvalidValue;
+  if (l.plan.R == 0) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   FusedParams q{};
   q.B = a.B; q.L = a.L; q.H = a.H; q.P = a.P;
   q.Hpad = l.Hpad; q.Ppad = l.Ppad;
-  q.T = l.T; q.R = l.T / 16;
-  q.nch = l.nch;
-  q.nflags = a.B * l.nch;
+  q.R = l.plan.R; q.nck = l.plan.nck; q.Lseg = l.plan.Lseg; q.Q = l.plan.Q;
   q.bf16_io = a.bf16_io;
   q.time_varying = a.time_varying;
-  q.spin_limit = 1u << 24;
   q.u = a.u; q.y = a.y;
   q.lam = a.lam; q.b_tilde = a.b_tilde; q.c_tilde = a.c_tilde;
   q.d = a.d; q.log_delta = a.log_delta; q.delta = a.delta;
   q.bpack = reinterpret_cast<uint4*>(base + l.bpack);
   q.cpack = reinterpret_cast<uint4*>(base + l.cpack);
   q.modes = reinterpret_cast<ModeParams*>(base + l.modes);
-  q.flags = reinterpret_cast<unsigned*>(base + l.flags);
-  q.ticket = reinterpret_cast<unsigned*>(base + l.ticket);
-  q.agg = reinterpret_cast<float2*>(base + l.agg);
-  q.agg_a = a.time_varying ? reinterpret_cast<float2*>(base + l.agg_a) : nullptr;
-  q.incl = reinterpret_cast<float2*>(base + l.incl);
-  hipError_t e = launch_pack(q, stream);
+  q.sagg = reinterpret_cast<float2*>(base + l.sagg);
+  q.sagg_a = a.time_varying ? reinterpret_cast<float2*>(base + l.sagg_a) : nullptr;
+  q.tot = reinterpret_cast<float2*>(base + l.tot);
+  q.tot_a = reinterpret_cast<float2*>(base + l.tot_a);
+  hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
   if (e != hipSuccess) return e;
-  return launch_fused(q, stream, ev_start, ev_stop);
+  e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);
+  if (e != hipSuccess) return e;
+  return timed(2, ev, nev, stream, launch_scan, q, l.plan);
 }
 
 }  // namespace s5

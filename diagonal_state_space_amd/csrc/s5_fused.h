@@ -1,4 +1,4 @@
-// Internal interface of the fused S5 forward kernel.
+// Internal interface of the fused S5 forward kernels (host side).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,25 +6,44 @@
 
 namespace s5 {
 
+namespace fused {
+constexpr int kStreams = 16;   // token streams per workgroup (the MFMA N columns)
+constexpr int kBlock = 1024;   // one LDS block: 64 lanes x 16 bytes
+
+// LDS bytes of one u tile (KS K-steps x R steps; float32 keeps 32 bytes per
+// lane) and of one x tile (K2 mode tiles x R steps; float32 keeps hi and lo).
+__host__ __device__ constexpr size_t u_tile_bytes(int KS, int R, bool bf16) {
+  return static_cast<size_t>(KS) * R * (bf16 ? 1 : 2) * kBlock;
+}
+__host__ __device__ constexpr size_t x_tile_bytes(int K2, int R, bool bf16) {
+  return static_cast<size_t>(K2) * R * (bf16 ? 1 : 2) * kBlock;
+}
+}  // namespace fused
+
 // Per-mode constants written by the packing kernel.
 struct ModeParams {
   float2 lam;      // continuous eigenvalue
   float2 inv_lam;  // 1/lambda
-  float2 abar;     // exp(lambda Delta)            (time-invariant)
-  float2 abar_R;   // exp(R lambda Delta), R = T/16 (time-invariant)
-  float2 abar_T;   // exp(T lambda Delta)          (time-invariant)
+  float2 abar;     // exp(lambda Delta)                         (time-invariant)
+  float2 aseg;     // exp(Lseg lambda Delta): one whole stream   (time-invariant)
   float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval
   float pad_;
 };
 
+// One forward call, as the kernels see it.
+//
+// Work split: sequence b is cut into Q workgroup ranges of 16 streams; stream
+// t of range qq holds the Lseg consecutive tokens starting at
+// (16 qq + t) Lseg, and is processed in chunks of R tokens (Lseg = R nck).
+// The 16 streams of a workgroup are the 16 columns of every MFMA tile.
 struct FusedParams {
   int B, L, H, P;
   int Hpad, Ppad;  // H rounded up to 32, P rounded up to 64
-  int T, R;        // tokens per chunk, tokens per lane run (T/16)
-  int nch;         // chunks per sequence
-  int nflags;      // B * nch
+  int R;           // tokens of one stream per chunk
+  int nck;         // chunks per stream
+  int Lseg;        // tokens per stream (R * nck)
+  int Q;           // workgroup ranges per sequence
   bool bf16_io, time_varying;
-  unsigned spin_limit;  // bound on look-back polling (never reached in a correct run)
   const void* u;
   void* y;
   const float2* lam;
@@ -37,18 +56,38 @@ struct FusedParams {
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O)
   uint4* cpack;       // readout operand fragments (hi, then lo)
   ModeParams* modes;  // [Ppad]
-  unsigned* flags;    // [B * nch] 0 none, 1 aggregate, 2 inclusive
-  unsigned* ticket;   // chunk ticket counter
-  float2* agg;        // [B * nch * Ppad] chunk state from zero carry-in
-  float2* agg_a;      // [B * nch * Ppad] chunk transition product (time-varying)
-  float2* incl;       // [B * nch * Ppad] state at the end of the chunk
+  float2* sagg;       // [B*Q][16][Ppad] stream state from a zero start
+  float2* sagg_a;     // [B*Q][16][Ppad] stream transition product (time-varying)
+  float2* tot;        // [B*Q][Ppad] workgroup range state from a zero start
+  float2* tot_a;      // [B*Q][Ppad] workgroup range transition product
 };
 
-// Tokens per chunk for these sizes (64, or 32 where registers / LDS require).
-int fused_chunk_tokens(bool bf16_io, bool time_varying, int Ppad, int Hpad);
-size_t fused_lds_bytes(bool bf16_io, bool time_varying, int T, int Ppad, int Hpad);
+// Launch plan of one call: chunk size, stream length, grid and LDS bytes.
+struct FusedPlan {
+  int R = 0, nck = 0, Lseg = 0, Q = 0;
+  bool keep = false;   // weights held in registers for the whole kernel
+  size_t lds_reduce = 0, lds_scan = 0;
+};
+
+// R and `keep` for these sizes (R = 0: no compiled instance fits).
+void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p);
+// Fill in nck, Lseg and Q for B sequences of length L on `ncu` compute units.
+void fused_split(int B, int L, int ncu, FusedPlan& p);
 
 hipError_t launch_pack(const FusedParams& q, hipStream_t stream);
-hipError_t launch_fused(const FusedParams& q, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+
+// Pass 1 (stream and range aggregates) and pass 2 (states and outputs).
+hipError_t launch_reduce(const FusedParams& q, const FusedPlan& p, hipStream_t stream);
+hipError_t launch_scan(const FusedParams& q, const FusedPlan& p, hipStream_t stream);
+
+// Per-kind entry points (one translation unit each).
+hipError_t launch_reduce_bf16_ti(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_scan_bf16_ti(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_reduce_bf16_tv(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_scan_bf16_tv(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_reduce_f32_ti(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_scan_f32_ti(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_reduce_f32_tv(const FusedParams& q, const FusedPlan& p, hipStream_t s);
+hipError_t launch_scan_f32_tv(const FusedParams& q, const FusedPlan& p, hipStream_t s);
 
 }  // namespace s5

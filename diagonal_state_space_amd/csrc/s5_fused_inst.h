@@ -1,0 +1,56 @@
+// Instances and dispatch of the fused kernels for one I/O type and one kind
+// (time-invariant or time-varying). Included once by each of four translation
+// units, which define S5_INST_BF16 and S5_INST_TV (0 or 1) and compile in
+// parallel.
+#pragma once
+
+#include "s5_fused_kernels.h"
+
+#if !defined(S5_INST_BF16) || !defined(S5_INST_TV)
+#error "define S5_INST_BF16 and S5_INST_TV before including s5_fused_inst.h"
+#endif
+
+namespace s5 {
+namespace {
+
+constexpr bool kBF16 = S5_INST_BF16 != 0;
+constexpr bool kTV = S5_INST_TV != 0;
+
+// Register-resident weights are compiled where they fit: float32 I/O doubles
+// every operand, so there only up to two mode tiles per wave.
+constexpr int kKeepMaxMPW = kBF16 ? 4 : 2;
+
+template <bool REDUCE, int MPW, int R, bool KEEP>
+hipError_t one(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  if constexpr (KEEP && (MPW > kKeepMaxMPW || R != 2)) {
+    return hipErrorInvalidValue;
+  } else if constexpr (REDUCE) {
+    return fused::launch_reduce_t<MPW, R, kTV, kBF16, KEEP>(q, p, s);
+  } else {
+    return fused::launch_scan_t<MPW, R, kTV, kBF16, KEEP>(q, p, s);
+  }
+}
+
+template <bool REDUCE, int R, bool KEEP>
+hipError_t by_mpw(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  switch (q.Ppad / 64) {
+    case 1: return one<REDUCE, 1, R, KEEP>(q, p, s);
+    case 2: return one<REDUCE, 2, R, KEEP>(q, p, s);
+    case 3: return one<REDUCE, 3, R, KEEP>(q, p, s);
+    case 4: return one<REDUCE, 4, R, KEEP>(q, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool REDUCE>
+hipError_t dispatch(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  if (q.bf16_io != kBF16 || q.time_varying != kTV) return hipErrorInvalidValue;
+  if (p.R == 2) return p.keep ? by_mpw<REDUCE, 2, true>(q, p, s) : by_mpw<REDUCE, 2, false>(q, p, s);
+  if constexpr (!kBF16) {
+    if (p.R == 1 && !p.keep) return by_mpw<REDUCE, 1, false>(q, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace s5

@@ -1,0 +1,748 @@
+// Fused S5 forward kernels for gfx950 (CDNA4): device templates.
+//
+// The recurrence x_k = a_k x_{k-1} + b_k (paper eq. 2 after the zero-order
+// hold of eq. 6; App. H gives the pair operator (a_j a_i, a_j b_i + b_j)) is
+// computed without writing the L x P state to HBM, in two passes over u:
+//
+//   pass 1 (k_reduce): per stream, the state reached from a zero start and the
+//     product of its a_k; per workgroup range, the same for its 16 streams
+//     combined (a 16-lane scan of pairs with DPP row shifts).
+//   pass 2 (k_scan): the state entering each stream (carry of the earlier
+//     ranges, then a 16-lane exclusive scan), then per chunk
+//       drive    Bu^T[2P x 16R] = B_bar[2P x H] . u^T[H x 16R]   (MFMA)
+//       scan     x_k = a_k x_{k-1} + b_k, sequential in each lane (VALU)
+//       readout  y^T[H x 16R] = C'[H x 2P] . x^T[2P x 16R] + D u  (MFMA)
+//
+// with C'[h, 2p] = Re C~[h,p], C'[h, 2p+1] = -Im C~[h,p], so that
+// Re(C~ x) = C' [Re x; Im x] (paper eq. 2 and App. A; output factor 1 for a
+// full spectrum). The 16 columns of every MFMA tile are 16 streams of
+// consecutive tokens, so lane (t = l%16, g = l/16) of wave w owns stream t
+// and, of mode tile j = w + 4jj, the modes 16 j + 4 g + r (r < 4): the
+// drive's result tile is already in the lane that scans it, and the lane's
+// states (modes 4g..4g+3 of the tile, both parts) are already the readout's
+// B operand fragment. Float32 I/O splits every float32 operand v into bf16
+// parts hi = bf16(v), lo = bf16(v - hi) and sums hi.hi + hi.lo + lo.hi.
+//
+// LDS holds 1 KB blocks of 64 lanes x 16 bytes in operand-fragment order, so
+// every LDS access is lane-contiguous: u tiles (two buffers, filled with
+// global_load_lds_dwordx4 where the chunk is complete) and x tiles (two
+// buffers).
+#pragma once
+
+#include "s5_common.h"
+#include "s5_fused.h"
+
+namespace s5 {
+namespace fused {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeepKS = 4;     // drive K-steps held in registers (H <= 128)
+constexpr int kKeepHT = 2;     // readout h-tiles per wave held in registers (H <= 128)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---- 16-lane row scan of (a, x) pairs -----------------------------------------
+
+template <int D>
+__device__ __forceinline__ float row_shr(float v, float fill) {
+  // DPP row_shr:D; lanes t < D of each 16-lane row get `fill`
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), 0x110 + D, 0xF, 0xF, false));
+}
+
+template <int D>
+__device__ __forceinline__ void row_scan_step(cf& A, cf& X) {
+  const cf Ap = {row_shr<D>(A.re, 1.0f), row_shr<D>(A.im, 0.0f)};
+  const cf Xp = {row_shr<D>(X.re, 0.0f), row_shr<D>(X.im, 0.0f)};
+  X = cfma(A, Xp, X);   // later segment (A, X) after the earlier (Ap, Xp)
+  A = cmul(A, Ap);
+}
+
+// Inclusive scan over the 16 lanes of each row, lane order = stream order.
+__device__ __forceinline__ void row_scan(cf& A, cf& X) {
+  row_scan_step<1>(A, X);
+  row_scan_step<2>(A, X);
+  row_scan_step<4>(A, X);
+  row_scan_step<8>(A, X);
+}
+
+// ---- geometry ---------------------------------------------------------------------
+
+struct Lane {
+  int tid, w, l, t, g;
+};
+
+__device__ __forceinline__ Lane lane_ids() {
+  Lane x;
+  x.tid = threadIdx.x;
+  x.w = x.tid >> 6;
+  x.l = x.tid & 63;
+  x.t = x.l & 15;
+  x.g = x.l >> 4;
+  return x;
+}
+
+// token (within the sequence) of stream t, chunk i, step n
+template <int R>
+__device__ __forceinline__ int tok_of(const FusedParams& q, int qq, int t, int i, int n) {
+  return (qq * kStreams + t) * q.Lseg + i * R + n;
+}
+
+// ---- u tile: global -> LDS in fragment order ---------------------------------------
+// Block (s, n[, half]) holds, in lane (t, g), u[tok(t, i, n)][32 s + 8 g + ...]:
+// 8 bf16, or 4 floats per half (halves 0 and 1 = elements 0-3 and 4-7).
+template <int R, bool BF16>
+__device__ __forceinline__ void load_u(const FusedParams& q, int b, int qq, int i, unsigned char* ub) {
+  constexpr int NPU = BF16 ? 1 : 2;
+  const Lane ln = lane_ids();
+  const int KS = q.Hpad >> 5;
+  const int nblk = KS * R * NPU;
+  const int last = tok_of<R>(q, qq, kStreams - 1, i, R - 1);
+  const bool dma = (q.H & 31) == 0 && last < q.L;
+  const size_t rowb = static_cast<size_t>(b) * q.L;
+  for (int blk = ln.w; blk < nblk; blk += kWaves) {
+    const int half = blk % NPU;
+    const int f = blk / NPU;
+    const int n = f % R;
+    const int s = f / R;
+    const int tok = tok_of<R>(q, qq, ln.t, i, n);
+    const int h0 = 32 * s + 8 * ln.g + 4 * half;
+    unsigned char* dst = ub + static_cast<size_t>(blk) * kBlock;
+    if (dma) {
+      const size_t off = (rowb + tok) * q.H + h0;
+      const void* src = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(q.u) + off)
+                             : static_cast<const void*>(static_cast<const float*>(q.u) + off);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    } else {
+      uint32_t v4[4] = {0u, 0u, 0u, 0u};
+      if (tok < q.L) {
+        const size_t off = (rowb + tok) * q.H;
+        if constexpr (BF16) {
+          const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int h = h0 + 2 * m;
+            const uint32_t lo = h < q.H ? up[h] : 0u;
+            const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
+            v4[m] = lo | (hi << 16);
+          }
+        } else {
+          const float* up = static_cast<const float*>(q.u) + off;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
+        }
+      }
+      *reinterpret_cast<uint4*>(dst + ln.l * 16) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+    }
+  }
+}
+
+// drive operand fragments of K-step s from the u tile: [plane][n]
+template <int R, bool BF16>
+__device__ __forceinline__ void get_u(const unsigned char* ub, int s, int l, bf16x8 (&uf)[BF16 ? 1 : 2][R]) {
+#pragma unroll
+  for (int n = 0; n < R; ++n) {
+    if constexpr (BF16) {
+      uf[0][n] = as_bf16x8(*reinterpret_cast<const uint4*>(ub + (s * R + n) * kBlock + l * 16));
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2) * kBlock + l * 16);
+      const float4 c = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2 + 1) * kBlock + l * 16);
+      const f32x8 f = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      const bf16x8 hi = __builtin_convertvector(f, bf16x8);
+      uf[0][n] = hi;
+      uf[1][n] = __builtin_convertvector(f - __builtin_convertvector(hi, f32x8), bf16x8);
+    }
+  }
+}
+
+// ---- drive: acc[jj][cc][n] = rows (mode 16 j + 4 g + r, part cc) of B_bar . u^T ----
+
+template <int MPW, int NP>
+__device__ __forceinline__ void load_b_step(const FusedParams& q, int w, int l, int s, bf16x8 (&a)[MPW][2][NP]) {
+  const int KS = q.Hpad >> 5;
+  const int nb = (q.Ppad / 16) * 2 * KS * 64;
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+        a[jj][cc][pl] = as_bf16x8(ldg16(q.bpack + pl * nb + (((w + kWaves * jj) * 2 + cc) * KS + s) * 64 + l));
+}
+
+template <int MPW, int R, int NP>
+__device__ __forceinline__ void mfma_drive(const bf16x8 (&a)[MPW][2][NP], const bf16x8 (&uf)[NP][R],
+                                           f32x4 (&acc)[MPW][2][R]) {
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        acc[jj][cc][n] = mfma(a[jj][cc][0], uf[0][n], acc[jj][cc][n]);
+        if constexpr (NP == 2) {
+          acc[jj][cc][n] = mfma(a[jj][cc][0], uf[1][n], acc[jj][cc][n]);
+          acc[jj][cc][n] = mfma(a[jj][cc][1], uf[0][n], acc[jj][cc][n]);
+        }
+      }
+}
+
+// B_bar held in registers for all (at most kKeepKS) K-steps
+template <int MPW, int NP>
+struct BKeep {
+  bf16x8 f[kKeepKS][MPW][2][NP];
+};
+
+template <int MPW, int NP>
+__device__ __forceinline__ void load_b_keep(const FusedParams& q, int w, int l, BKeep<MPW, NP>& bk) {
+  const int KS = q.Hpad >> 5;
+#pragma unroll
+  for (int s = 0; s < kKeepKS; ++s) {
+    if (s < KS) {
+      load_b_step<MPW, NP>(q, w, l, s, bk.f[s]);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) bk.f[s][jj][cc][pl] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+    }
+  }
+}
+
+template <int MPW, int R, bool BF16, bool KEEP>
+__device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF16 ? 1 : 2>& bk,
+                                      const unsigned char* ub, int w, int l, f32x4 (&acc)[MPW][2][R]) {
+  constexpr int NP = BF16 ? 1 : 2;
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int n = 0; n < R; ++n) acc[jj][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int KS = q.Hpad >> 5;
+  if constexpr (KEEP) {
+#pragma unroll
+    for (int s = 0; s < kKeepKS; ++s) {
+      if (s < KS) {
+        bf16x8 uf[NP][R];
+        get_u<R, BF16>(ub, s, l, uf);
+        mfma_drive<MPW, R, NP>(bk.f[s], uf, acc);
+      }
+    }
+  } else {
+    bf16x8 a[MPW][2][NP];
+    load_b_step<MPW, NP>(q, w, l, 0, a);
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 an[MPW][2][NP];
+      if (s + 1 < KS) load_b_step<MPW, NP>(q, w, l, s + 1, an);
+      bf16x8 uf[NP][R];
+      get_u<R, BF16>(ub, s, l, uf);
+      mfma_drive<MPW, R, NP>(a, uf, acc);
+      if (s + 1 < KS) {
+#pragma unroll
+        for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl) a[jj][cc][pl] = an[jj][cc][pl];
+      }
+    }
+  }
+}
+
+// ---- time-varying inputs: Delta for the lane's 4 modes of each tile ------------------
+
+template <int MPW, int R>
+__device__ __forceinline__ void load_delta(const FusedParams& q, int b, int qq, int i, const Lane& ln,
+                                           float4 (&dl)[MPW][R]) {
+  const bool vec = (q.P & 3) == 0;
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj) {
+    const int pm0 = 16 * (ln.w + kWaves * jj) + 4 * ln.g;
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      const int tok = tok_of<R>(q, qq, ln.t, i, n);
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (tok < q.L && pm0 < q.P) {
+        const float* dp = q.delta + (static_cast<size_t>(b) * q.L + tok) * q.P + pm0;
+        if (vec) {
+          const float4 x = *reinterpret_cast<const float4*>(dp);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = pm0 + r < q.P ? dp[r] : 0.0f;
+        }
+      }
+      dl[jj][n] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+__device__ __forceinline__ float f4_at(const float4& v, int r) {
+  return r == 0 ? v.x : (r == 1 ? v.y : (r == 2 ? v.z : v.w));
+}
+
+// ---- pass 1 --------------------------------------------------------------------------
+
+// MPW: mode tiles per wave (Ppad = 64 MPW); R: tokens per stream per chunk.
+template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+__global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
+  constexpr int NP = BF16 ? 1 : 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
+  const Lane ln = lane_ids();
+  const int bq = blockIdx.x;
+  const int b = bq / q.Q;
+  const int qq = bq - b * q.Q;
+  const int KS = q.Hpad >> 5;
+  unsigned char* ubuf[2] = {smem, smem + u_tile_bytes(KS, R, BF16)};
+
+  BKeep<MPW, NP> bk;
+  if constexpr (KEEP) load_b_keep<MPW, NP>(q, ln.w, ln.l, bk);
+
+  cf abar[MPW][4];
+  cf z[MPW][4];
+  cf A[MPW][4];
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      const float2 ab = q.modes[pm].abar;
+      abar[jj][r] = {ab.x, ab.y};
+      z[jj][r] = {0.0f, 0.0f};
+      A[jj][r] = {1.0f, 0.0f};
+    }
+
+  load_u<R, BF16>(q, b, qq, 0, ubuf[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < q.nck; ++i) {
+    if (i + 1 < q.nck) load_u<R, BF16>(q, b, qq, i + 1, ubuf[(i + 1) & 1]);
+    float4 dl[TV ? MPW : 1][TV ? R : 1];
+    if constexpr (TV) load_delta<MPW, R>(q, b, qq, i, ln, dl);
+    f32x4 acc[MPW][2][R];
+    drive<MPW, R, BF16, KEEP>(q, bk, ubuf[i & 1], ln.w, ln.l, acc);
+#pragma unroll
+    for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cf x = z[jj][r];
+        if constexpr (TV) {
+          const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+          const ModeParams& mq = q.modes[pm];
+          const cf lam = {mq.lam.x, mq.lam.y};
+          const cf inv = {mq.inv_lam.x, mq.inv_lam.y};
+          cf Ar = A[jj][r];
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            cf a, gn;
+            zoh_step(lam, inv, mq.hrev, f4_at(dl[jj][n], r), a, gn);
+            x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+            Ar = cmul(a, Ar);
+          }
+          A[jj][r] = Ar;
+        } else {
+#pragma unroll
+          for (int n = 0; n < R; ++n) x = cfma(abar[jj][r], x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+        }
+        z[jj][r] = x;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next u tile has landed
+    __syncthreads();
+  }
+
+  // stream aggregates, then the range total over the 16 streams
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
+      q.sagg[si] = make_float2(z[jj][r].re, z[jj][r].im);
+      cf At;
+      if constexpr (TV) {
+        q.sagg_a[si] = make_float2(A[jj][r].re, A[jj][r].im);
+        At = A[jj][r];
+      } else {
+        const float2 as = q.modes[pm].aseg;
+        At = {as.x, as.y};
+      }
+      cf Xt = z[jj][r];
+      row_scan(At, Xt);
+      if (ln.t == kStreams - 1) {
+        const size_t ti = static_cast<size_t>(bq) * q.Ppad + pm;
+        q.tot[ti] = make_float2(Xt.re, Xt.im);
+        q.tot_a[ti] = make_float2(At.re, At.im);
+      }
+    }
+  }
+}
+
+// ---- pass 2 --------------------------------------------------------------------------
+
+template <int MPW, int NP>
+struct CKeep {
+  bf16x8 f[kKeepHT][4 * MPW][NP];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, const f32x4& acc,
+                                        const float (&dv)[4]) {
+  if (tok >= q.L || h0 >= q.H) return;
+  const size_t row = (static_cast<size_t>(b) * q.L + tok) * q.H;
+  const bool vec = (q.H & 3) == 0;   // then h0 + 4 <= H (h0 is a multiple of 4)
+  float uv[4];
+  if (vec) {
+    if constexpr (BF16) {
+      const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q.u) + row + h0);
+      uv[0] = __uint_as_float(p.x << 16);
+      uv[1] = __uint_as_float(p.x & 0xffff0000u);
+      uv[2] = __uint_as_float(p.y << 16);
+      uv[3] = __uint_as_float(p.y & 0xffff0000u);
+    } else {
+      const float4 p = *reinterpret_cast<const float4*>(static_cast<const float*>(q.u) + row + h0);
+      uv[0] = p.x; uv[1] = p.y; uv[2] = p.z; uv[3] = p.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) uv[r] = h0 + r < q.H ? load_io<BF16>(q.u, row + h0 + r) : 0.0f;
+  }
+  float yv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) yv[r] = fmaf(dv[r], uv[r], acc[r]);
+  if (vec) {
+    if constexpr (BF16) {
+      uint2 pk;
+      pk.x = static_cast<uint32_t>(f32_to_bf16(yv[0])) | (static_cast<uint32_t>(f32_to_bf16(yv[1])) << 16);
+      pk.y = static_cast<uint32_t>(f32_to_bf16(yv[2])) | (static_cast<uint32_t>(f32_to_bf16(yv[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(q.y) + row + h0) = pk;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(q.y) + row + h0) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (h0 + r < q.H) {
+        if constexpr (BF16) {
+          static_cast<uint16_t*>(q.y)[row + h0 + r] = f32_to_bf16(yv[r]);
+        } else {
+          static_cast<float*>(q.y)[row + h0 + r] = yv[r];
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_d(const FusedParams& q, int h0, float (&dv)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dv[r] = h0 + r < q.H ? q.d[h0 + r] : 0.0f;
+}
+
+// readout operand fragments of K-step s from the x tile: [plane][n]
+template <int R, int NP>
+__device__ __forceinline__ void get_x(const unsigned char* xb, int K2, int s, int l, bf16x8 (&xf)[NP][R]) {
+#pragma unroll
+  for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+    for (int n = 0; n < R; ++n)
+      xf[pl][n] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + ((pl * K2 + s) * R + n) * kBlock + l * 16));
+}
+
+template <int R, int NP>
+__device__ __forceinline__ void mfma_read(const bf16x8 (&c)[NP], const bf16x8 (&xf)[NP][R], f32x4 (&y)[R]) {
+#pragma unroll
+  for (int n = 0; n < R; ++n) {
+    y[n] = mfma(c[0], xf[0][n], y[n]);
+    if constexpr (NP == 2) {
+      y[n] = mfma(c[0], xf[1][n], y[n]);
+      y[n] = mfma(c[1], xf[0][n], y[n]);
+    }
+  }
+}
+
+template <int MPW, int NP>
+__device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s, int l, bf16x8 (&c)[NP]) {
+  constexpr int K2 = 4 * MPW;
+  const int nc = (q.Hpad / 16) * K2 * 64;
+#pragma unroll
+  for (int pl = 0; pl < NP; ++pl) c[pl] = as_bf16x8(ldg16(q.cpack + pl * nc + (ht * K2 + s) * 64 + l));
+}
+
+// y for chunk i of the workgroup's streams from the x tile in LDS
+template <int MPW, int R, bool BF16, bool KEEP>
+__device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, BF16 ? 1 : 2>& ck,
+                                        const float (&dk)[kKeepHT][4], const unsigned char* xb, int b,
+                                        int qq, int i, const Lane& ln) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int K2 = 4 * MPW;
+  const int HT = q.Hpad >> 4;
+  if constexpr (KEEP) {
+    f32x4 yacc[kKeepHT][R];
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e)
+#pragma unroll
+      for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < K2; ++s) {
+      bf16x8 xf[NP][R];
+      get_x<R, NP>(xb, K2, s, ln.l, xf);
+#pragma unroll
+      for (int e = 0; e < kKeepHT; ++e) {
+        if (ln.w + kWaves * e < HT) mfma_read<R, NP>(ck.f[e][s], xf, yacc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+      if (ht >= HT) continue;
+#pragma unroll
+      for (int n = 0; n < R; ++n)
+        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dk[e]);
+    }
+  } else {
+    // C' streamed from L2: h-tiles (ht0, ht0 + 4), K-steps in batches of G, one batch ahead
+    constexpr int G = BF16 ? 4 : 2;
+    static_assert(K2 % G == 0, "readout K-steps must split into whole batches");
+    for (int ht0 = ln.w; ht0 < HT; ht0 += 2 * kWaves) {
+      const bool has1 = ht0 + kWaves < HT;
+      f32x4 yacc[2][R];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      bf16x8 cb[G][2][NP];
+#pragma unroll
+      for (int kk = 0; kk < G; ++kk) {
+        load_c_step<MPW, NP>(q, ht0, kk, ln.l, cb[kk][0]);
+        if (has1) load_c_step<MPW, NP>(q, ht0 + kWaves, kk, ln.l, cb[kk][1]);
+      }
+#pragma unroll 1
+      for (int s0 = 0; s0 < K2; s0 += G) {
+        bf16x8 cn[G][2][NP];
+        if (s0 + G < K2) {
+#pragma unroll
+          for (int kk = 0; kk < G; ++kk) {
+            load_c_step<MPW, NP>(q, ht0, s0 + G + kk, ln.l, cn[kk][0]);
+            if (has1) load_c_step<MPW, NP>(q, ht0 + kWaves, s0 + G + kk, ln.l, cn[kk][1]);
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < G; ++kk) {
+          bf16x8 xf[NP][R];
+          get_x<R, NP>(xb, K2, s0 + kk, ln.l, xf);
+          mfma_read<R, NP>(cb[kk][0], xf, yacc[0]);
+          if (has1) mfma_read<R, NP>(cb[kk][1], xf, yacc[1]);
+        }
+        if (s0 + G < K2) {
+#pragma unroll
+          for (int kk = 0; kk < G; ++kk)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+              for (int pl = 0; pl < NP; ++pl) cb[kk][e][pl] = cn[kk][e][pl];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (e == 1 && !has1) continue;
+        const int h0 = 16 * (ht0 + kWaves * e) + 4 * ln.g;
+        float dv[4];
+        load_d(q, h0, dv);
+#pragma unroll
+        for (int n = 0; n < R; ++n) store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), h0, yacc[e][n], dv);
+      }
+    }
+  }
+}
+
+template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+__global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int K2 = 4 * MPW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
+  const Lane ln = lane_ids();
+  const int bq = blockIdx.x;
+  const int b = bq / q.Q;
+  const int qq = bq - b * q.Q;
+  const int KS = q.Hpad >> 5;
+  const size_t ut = u_tile_bytes(KS, R, BF16);
+  const size_t xt = x_tile_bytes(K2, R, BF16);
+  unsigned char* ubuf[2] = {smem, smem + ut};
+  unsigned char* xbuf[2] = {smem + 2 * ut, smem + 2 * ut + xt};
+
+  BKeep<MPW, NP> bk;
+  CKeep<MPW, NP> ck;
+  float dk[kKeepHT][4];
+  if constexpr (KEEP) {
+    load_b_keep<MPW, NP>(q, ln.w, ln.l, bk);
+    const int HT = q.Hpad >> 4;
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+#pragma unroll
+      for (int s = 0; s < K2; ++s) {
+        if (ht < HT) {
+          load_c_step<MPW, NP>(q, ht, s, ln.l, ck.f[e][s]);
+        } else {
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) ck.f[e][s][pl] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+        }
+      }
+      load_d(q, 16 * ht + 4 * ln.g, dk[e]);
+    }
+  }
+
+  // ---- state entering each stream ----
+  // carry into the range: the totals of the sequence's earlier ranges, folded in
+  // order; it waits in LDS (the second x buffer is not written before the loop).
+  float2* s_c0 = reinterpret_cast<float2*>(xbuf[1]);
+  if (ln.tid < q.Ppad) {
+    cf c = {0.0f, 0.0f};
+    const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + ln.tid;
+    constexpr int kBatch = 8;
+    for (int q0 = 0; q0 < qq; q0 += kBatch) {
+      cf xs[kBatch], as[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        if (q0 + e < qq) {
+          const float2 xv = q.tot[base + static_cast<size_t>(q0 + e) * q.Ppad];
+          const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
+          xs[e] = {xv.x, xv.y};
+          as[e] = {av.x, av.y};
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        if (q0 + e < qq) c = cfma(as[e], c, xs[e]);
+      }
+    }
+    s_c0[ln.tid] = make_float2(c.re, c.im);
+  }
+  __syncthreads();
+
+  cf abar[MPW][4];
+  cf st[MPW][4];
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      const ModeParams& mq = q.modes[pm];
+      abar[jj][r] = {mq.abar.x, mq.abar.y};
+      const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
+      const float2 xv = q.sagg[si];
+      cf X = {xv.x, xv.y};
+      cf A;
+      if constexpr (TV) {
+        const float2 av = q.sagg_a[si];
+        A = {av.x, av.y};
+      } else {
+        A = {mq.aseg.x, mq.aseg.y};
+      }
+      row_scan(A, X);
+      const cf Ae = {row_shr<1>(A.re, 1.0f), row_shr<1>(A.im, 0.0f)};
+      const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
+      const float2 c0 = s_c0[pm];
+      st[jj][r] = cfma(Ae, {c0.x, c0.y}, Xe);
+    }
+  }
+
+  // ---- chunk pipeline ----
+  load_u<R, BF16>(q, b, qq, 0, ubuf[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (q.nck > 1) load_u<R, BF16>(q, b, qq, 1, ubuf[1]);
+  float4 dl[TV ? MPW : 1][TV ? R : 1];
+  if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
+  f32x4 acc[MPW][2][R];
+  drive<MPW, R, BF16, KEEP>(q, bk, ubuf[0], ln.w, ln.l, acc);
+
+  for (int i = 0; i < q.nck; ++i) {
+    // scan chunk i in place: acc becomes x
+#pragma unroll
+    for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cf x = st[jj][r];
+        if constexpr (TV) {
+          const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+          const ModeParams& mq = q.modes[pm];
+          const cf lam = {mq.lam.x, mq.lam.y};
+          const cf inv = {mq.inv_lam.x, mq.inv_lam.y};
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            cf a, gn;
+            zoh_step(lam, inv, mq.hrev, f4_at(dl[jj][n], r), a, gn);
+            x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+            acc[jj][0][n][r] = x.re;
+            acc[jj][1][n][r] = x.im;
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            x = cfma(abar[jj][r], x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+            acc[jj][0][n][r] = x.re;
+            acc[jj][1][n][r] = x.im;
+          }
+        }
+        st[jj][r] = x;
+      }
+    }
+    // x tile: block (mode tile j, n), lane (t, g): modes 16 j + 4 g + r, parts interleaved
+    unsigned char* xb = xbuf[i & 1];
+#pragma unroll
+    for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[2 * r] = acc[jj][0][n][r];
+          v[2 * r + 1] = acc[jj][1][n][r];
+        }
+        const int blk = (ln.w + kWaves * jj) * R + n;
+        put_frag(v, reinterpret_cast<uint4*>(xb + blk * kBlock + ln.l * 16),
+                 BF16 ? nullptr : reinterpret_cast<uint4*>(xb + (K2 * R + blk) * kBlock + ln.l * 16));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of u tile i+1 has landed
+    __syncthreads();                 // x tile i and u tile i+1 complete; u tile i free
+    if (i + 2 < q.nck) load_u<R, BF16>(q, b, qq, i + 2, ubuf[i & 1]);
+    if (i + 1 < q.nck) {
+      if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
+      drive<MPW, R, BF16, KEEP>(q, bk, ubuf[(i + 1) & 1], ln.w, ln.l, acc);
+    }
+    readout<MPW, R, BF16, KEEP>(q, ck, dk, xb, b, qq, i, ln);
+  }
+}
+
+// ---- launch -----------------------------------------------------------------------------
+
+template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  auto kern = k_reduce<MPW, R, TV, BF16, KEEP>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_reduce, s, q);
+  return hipGetLastError();
+}
+
+template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  auto kern = k_scan<MPW, R, TV, BF16, KEEP>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_scan, s, q);
+  return hipGetLastError();
+}
+
+}  // namespace fused
+}  // namespace s5

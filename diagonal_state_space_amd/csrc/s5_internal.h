@@ -35,9 +35,9 @@ size_t forward_workspace_bytes(const ForwardArgs& a);
 bool forward_supported(const ForwardArgs& a);
 
 // Enqueue the whole forward path on `stream` using `ws` (forward_workspace_bytes
-// bytes, 256-byte aligned). `ev_start` / `ev_stop` (may be null) are recorded
-// around the forward kernels proper (after parameter preparation).
-hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, hipEvent_t ev_start,
-                          hipEvent_t ev_stop);
+// bytes, 256-byte aligned). ev[2k] / ev[2k+1] are recorded around the k-th
+// kernel launch for k < nev/2.
+hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, const hipEvent_t* ev,
+                          int nev);
 
 }  // namespace s5

@@ -1,0 +1,137 @@
+// Parameter packing for the fused S5 forward kernels: zero-order-hold
+// discretisation in float64 (paper eq. 6; App. A `discretize`; abhik.ai
+// review, row 2), the MFMA operand layouts of B_bar and C', and the per-mode
+// constants.
+#include "s5_common.h"
+#include "s5_fused.h"
+
+namespace s5 {
+
+namespace {
+
+struct zd {
+  double re, im;
+};
+__device__ __forceinline__ zd zmul(zd a, zd b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
+__device__ __forceinline__ zd zdiv(zd a, zd b) {
+  const double den = b.re * b.re + b.im * b.im;
+  return {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
+}
+__device__ __forceinline__ zd zexp(zd z) {
+  const double e = exp(z.re);
+  double s, c;
+  sincos(z.im, &s, &c);
+  return {e * c, e * s};
+}
+
+// gain (exp(z)-1)/lambda, z = lambda*delta; 9-term phi1 series for |z| < 1e-4
+__device__ zd gain64(zd lam, double delta) {
+  const zd z = {lam.re * delta, lam.im * delta};
+  if (sqrt(z.re * z.re + z.im * z.im) < 1e-4) {
+    zd term = {1.0, 0.0}, phi = {1.0, 0.0};
+    for (int n = 1; n <= 8; ++n) {
+      term = zmul(term, z);
+      term.re /= (n + 1);
+      term.im /= (n + 1);
+      phi.re += term.re;
+      phi.im += term.im;
+    }
+    return {delta * phi.re, delta * phi.im};
+  }
+  const zd e = zexp(z);
+  return zdiv({e.re - 1.0, e.im}, lam);
+}
+
+__global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
+  const int KS = q.Hpad / 32;
+  const int K2 = 2 * q.Ppad / 32;
+  const int nb = (q.Ppad / 16) * 2 * KS * 64;  // B_bar fragment lanes
+  const int nc = (q.Hpad / 16) * K2 * 64;      // C' fragment lanes
+  const int nm = q.Ppad;                        // per-mode values
+  const int total = nb + nc + nm;
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+    if (idx < nb) {
+      // fragment ((j*2 + c)*KS + s), lane l: row m = l%16 (mode 16j+m), k = 8(l/16)+i
+      const int l = idx & 63;
+      const int f = idx >> 6;
+      const int s = f % KS;
+      const int c = (f / KS) & 1;
+      const int j = f / (2 * KS);
+      const int p = 16 * j + (l & 15);
+      float v[8];
+      zd g = {0.0, 0.0};
+      if (p < q.P) {
+        const zd lam = {q.lam[p].x, q.lam[p].y};
+        g = q.time_varying ? zd{1.0, 0.0} : gain64(lam, exp(static_cast<double>(q.log_delta[p])));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int h = 32 * s + 8 * (l >> 4) + i;
+        double val = 0.0;
+        if (p < q.P && h < q.H) {
+          const float2 bt = q.b_tilde[static_cast<size_t>(p) * q.H + h];
+          const zd b = zmul(g, {bt.x, bt.y});
+          val = c == 0 ? b.re : b.im;
+        }
+        v[i] = static_cast<float>(val);
+      }
+      put_frag(v, q.bpack + idx, split ? q.bpack + nb + idx : nullptr);
+    } else if (idx < nb + nc) {
+      // fragment (ht*K2 + s), lane l: row h = 16 ht + l%16, k = 32 s + 8(l/16) + i,
+      // k = 2p + comp with comp 0 -> Re C~, comp 1 -> -Im C~
+      const int e = idx - nb;
+      const int l = e & 63;
+      const int f = e >> 6;
+      const int s = f % K2;
+      const int ht = f / K2;
+      const int h = 16 * ht + (l & 15);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 32 * s + 8 * (l >> 4) + i;
+        const int p = k >> 1;
+        float val = 0.0f;
+        if (h < q.H && p < q.P) {
+          const float2 ct = q.c_tilde[static_cast<size_t>(h) * q.P + p];
+          val = (k & 1) ? -ct.y : ct.x;
+        }
+        v[i] = val;
+      }
+      put_frag(v, q.cpack + e, split ? q.cpack + nc + e : nullptr);
+    } else if (idx < nb + nc + nm) {
+      const int p = idx - nb - nc;
+      ModeParams mp{};
+      if (p < q.P) {
+        const zd lam = {q.lam[p].x, q.lam[p].y};
+        mp.lam = make_float2(q.lam[p].x, q.lam[p].y);
+        const zd il = zdiv({1.0, 0.0}, lam);
+        mp.inv_lam = make_float2(static_cast<float>(il.re), static_cast<float>(il.im));
+        mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
+        if (!q.time_varying) {
+          const double dt = exp(static_cast<double>(q.log_delta[p]));
+          const zd z = {lam.re * dt, lam.im * dt};
+          const zd a = zexp(z);
+          const zd as = zexp({z.re * q.Lseg, z.im * q.Lseg});
+          mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));
+          mp.aseg = make_float2(static_cast<float>(as.re), static_cast<float>(as.im));
+        }
+      } else {
+        mp.inv_lam = make_float2(0.0f, 0.0f);
+      }
+      q.modes[p] = mp;
+    }
+  }
+}
+
+
+}  // namespace
+
+hipError_t launch_pack(const FusedParams& q, hipStream_t stream) {
+  const int KS = q.Hpad / 32, K2 = 2 * q.Ppad / 32;
+  const int total = (q.Ppad / 16) * 2 * KS * 64 + (q.Hpad / 16) * K2 * 64 + q.Ppad;
+  const int blocks = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
+  hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, stream, q, q.bf16_io ? 0 : 1);
+  return hipGetLastError();
+}
+
+}  // namespace s5

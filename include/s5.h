@@ -142,15 +142,22 @@ s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_
 const char* s5_status_string(s5_status s);
 
 /*
- * s5_set_profiling_events - measurement hook for benchmarks. When both
- * events are non-NULL, every later s5_forward / s5_forward_timevarying call
- * made from the calling host thread records `start` on its stream right
- * before the fused forward kernel and `stop` right after it, so that
- * hipEventElapsedTime gives that kernel's duration alone. Passing NULL for
- * both turns the hook off. The setting is per host thread.
- * Errors: S5_ERR_INVALID_ARGUMENT if exactly one event is NULL.
+ * s5_set_profiling_events - measurement hook for benchmarks. `events` holds
+ * `count` caller-owned events (count even, 0..S5_PROFILING_MAX_EVENTS). Every
+ * later s5_forward / s5_forward_timevarying call made from the calling host
+ * thread records events[2k] on its stream right before its k-th kernel launch
+ * and events[2k+1] right after it, for k < count/2, so that
+ * hipEventElapsedTime gives that kernel's duration alone. The launches of one
+ * forward call are, in order: k = 0 parameter packing (discretisation and
+ * operand layouts), k = 1 the aggregate pass (state of every token range from
+ * a zero start), k = 2 the state and output pass. count 0 turns the hook off.
+ * The handles are copied; the events stay owned by the caller and must
+ * outlive the calls that record them. The setting is per host thread.
+ * Errors: S5_ERR_INVALID_ARGUMENT for an odd or out-of-range count, a NULL
+ * array with count > 0, or a NULL handle among the first count.
  */
-s5_status s5_set_profiling_events(hipEvent_t start, hipEvent_t stop);
+#define S5_PROFILING_MAX_EVENTS 6
+s5_status s5_set_profiling_events(const hipEvent_t* events, int count);
 
 #ifdef __cplusplus
 }
