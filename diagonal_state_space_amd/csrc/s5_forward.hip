@@ -21,7 +21,7 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   for (int R : cand) {
     if (bf16_io && R != 2) continue;
     const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io);
-    const size_t ls = lr + 2 * fused::x_tile_bytes(K2, R, bf16_io);
+    const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io);
     if (ls > lds_max) continue;
     p.R = R;
     p.lds_reduce = lr;

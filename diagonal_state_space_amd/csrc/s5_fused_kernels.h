@@ -99,8 +99,23 @@ __device__ __forceinline__ void load_u(const FusedParams& q, int b, int qq, int 
   const int KS = q.Hpad >> 5;
   const int nblk = KS * R * NPU;
   const int last = tok_of<R>(q, qq, kStreams - 1, i, R - 1);
-  const bool dma = (q.H & 31) == 0 && last < q.L;
   const size_t rowb = static_cast<size_t>(b) * q.L;
+  if ((q.H & 31) == 0 && last < q.L) {
+    // complete chunk: asynchronous copies, nothing waits here
+    for (int blk = ln.w; blk < nblk; blk += kWaves) {
+      const int half = blk % NPU;
+      const int f = blk / NPU;
+      const int n = f % R;
+      const int s = f / R;
+      const int tok = tok_of<R>(q, qq, ln.t, i, n);
+      const size_t off = (rowb + tok) * q.H + 32 * s + 8 * ln.g + 4 * half;
+      const void* src = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(q.u) + off)
+                             : static_cast<const void*>(static_cast<const float*>(q.u) + off);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(ub + static_cast<size_t>(blk) * kBlock), 16, 0, 0);
+    }
+    return;
+  }
+  // ragged chunk (tokens past L or H not a multiple of 32): guarded loads, zero fill
   for (int blk = ln.w; blk < nblk; blk += kWaves) {
     const int half = blk % NPU;
     const int f = blk / NPU;
@@ -108,33 +123,25 @@ __device__ __forceinline__ void load_u(const FusedParams& q, int b, int qq, int 
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    unsigned char* dst = ub + static_cast<size_t>(blk) * kBlock;
-    if (dma) {
-      const size_t off = (rowb + tok) * q.H + h0;
-      const void* src = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(q.u) + off)
-                             : static_cast<const void*>(static_cast<const float*>(q.u) + off);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-    } else {
-      uint32_t v4[4] = {0u, 0u, 0u, 0u};
-      if (tok < q.L) {
-        const size_t off = (rowb + tok) * q.H;
-        if constexpr (BF16) {
-          const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
+    uint32_t v4[4] = {0u, 0u, 0u, 0u};
+    if (tok < q.L) {
+      const size_t off = (rowb + tok) * q.H;
+      if constexpr (BF16) {
+        const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int h = h0 + 2 * m;
-            const uint32_t lo = h < q.H ? up[h] : 0u;
-            const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
-            v4[m] = lo | (hi << 16);
-          }
-        } else {
-          const float* up = static_cast<const float*>(q.u) + off;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
+        for (int m = 0; m < 4; ++m) {
+          const int h = h0 + 2 * m;
+          const uint32_t lo = h < q.H ? up[h] : 0u;
+          const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
+          v4[m] = lo | (hi << 16);
         }
+      } else {
+        const float* up = static_cast<const float*>(q.u) + off;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
       }
-      *reinterpret_cast<uint4*>(dst + ln.l * 16) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
     }
+    *reinterpret_cast<uint4*>(ub + static_cast<size_t>(blk) * kBlock + ln.l * 16) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
   }
 }
 
@@ -224,13 +231,13 @@ __device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF1
       for (int n = 0; n < R; ++n) acc[jj][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int KS = q.Hpad >> 5;
   if constexpr (KEEP) {
+    // branch-free: weights of K-steps s >= KS are zero, and their u operand is
+    // read from the last real K-step (finite data of the same tokens)
 #pragma unroll
     for (int s = 0; s < kKeepKS; ++s) {
-      if (s < KS) {
-        bf16x8 uf[NP][R];
-        get_u<R, BF16>(ub, s, l, uf);
-        mfma_drive<MPW, R, NP>(bk.f[s], uf, acc);
-      }
+      bf16x8 uf[NP][R];
+      get_u<R, BF16>(ub, s < KS ? s : KS - 1, l, uf);
+      mfma_drive<MPW, R, NP>(bk.f[s], uf, acc);
     }
   } else {
     bf16x8 a[MPW][2][NP];
@@ -390,32 +397,36 @@ struct CKeep {
   bf16x8 f[kKeepHT][4 * MPW][NP];
 };
 
-template <bool BF16>
-__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, const f32x4& acc,
-                                        const float (&dv)[4]) {
-  if (tok >= q.L || h0 >= q.H) return;
-  const size_t row = (static_cast<size_t>(b) * q.L + tok) * q.H;
-  const bool vec = (q.H & 3) == 0;   // then h0 + 4 <= H (h0 is a multiple of 4)
-  float uv[4];
-  if (vec) {
-    if constexpr (BF16) {
-      const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q.u) + row + h0);
-      uv[0] = __uint_as_float(p.x << 16);
-      uv[1] = __uint_as_float(p.x & 0xffff0000u);
-      uv[2] = __uint_as_float(p.y << 16);
-      uv[3] = __uint_as_float(p.y & 0xffff0000u);
-    } else {
-      const float4 p = *reinterpret_cast<const float4*>(static_cast<const float*>(q.u) + row + h0);
-      uv[0] = p.x; uv[1] = p.y; uv[2] = p.z; uv[3] = p.w;
-    }
+// D u feedthrough of the readout lane's 4 outputs y[tok(t, i, n)][h0..h0+3],
+// h0 = 16 ht + 4 g, taken from u tile i in LDS (zero past H and L): block
+// (ht/2, n), lane t + 16 (2 (ht&1) + g/2), elements 4 (g&1)..+3.
+template <int R, bool BF16>
+__device__ __forceinline__ void u_for_y(const unsigned char* ub, int ht, int n, const Lane& ln, float (&uv)[4]) {
+  const int s = ht >> 1;
+  const int lp = ln.t + 16 * (2 * (ht & 1) + (ln.g >> 1));
+  if constexpr (BF16) {
+    const uint2 p = *reinterpret_cast<const uint2*>(ub + (s * R + n) * kBlock + lp * 16 + 8 * (ln.g & 1));
+    uv[0] = __uint_as_float(p.x << 16);
+    uv[1] = __uint_as_float(p.x & 0xffff0000u);
+    uv[2] = __uint_as_float(p.y << 16);
+    uv[3] = __uint_as_float(p.y & 0xffff0000u);
   } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) uv[r] = h0 + r < q.H ? load_io<BF16>(q.u, row + h0 + r) : 0.0f;
+    const float4 p = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2 + (ln.g & 1)) * kBlock + lp * 16);
+    uv[0] = p.x; uv[1] = p.y; uv[2] = p.z; uv[3] = p.w;
   }
+}
+
+// y = acc + D u for 4 consecutive features; `full`: token < L and h0 + 4 <= H
+// are known, the row is 16-byte aligned (fp32) or 8-byte aligned (bf16)
+template <bool BF16>
+__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, bool full, const f32x4& acc,
+                                        const float (&dv)[4], const float (&uv)[4]) {
   float yv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) yv[r] = fmaf(dv[r], uv[r], acc[r]);
-  if (vec) {
+  if (!full && (tok >= q.L || h0 >= q.H)) return;
+  const size_t row = (static_cast<size_t>(b) * q.L + tok) * q.H;
+  if (full || ((q.H & 3) == 0)) {   // h0 + 4 <= H: h0 is a multiple of 4
     if constexpr (BF16) {
       uint2 pk;
       pk.x = static_cast<uint32_t>(f32_to_bf16(yv[0])) | (static_cast<uint32_t>(f32_to_bf16(yv[1])) << 16);
@@ -473,36 +484,41 @@ __device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s,
   for (int pl = 0; pl < NP; ++pl) c[pl] = as_bf16x8(ldg16(q.cpack + pl * nc + (ht * K2 + s) * 64 + l));
 }
 
-// y for chunk i of the workgroup's streams from the x tile in LDS
+// y for chunk i of the workgroup's streams from the x tile and u tile in LDS
 template <int MPW, int R, bool BF16, bool KEEP>
 __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, BF16 ? 1 : 2>& ck,
-                                        const float (&dk)[kKeepHT][4], const unsigned char* xb, int b,
-                                        int qq, int i, const Lane& ln) {
+                                        const float (&dk)[kKeepHT][4], const unsigned char* xb,
+                                        const unsigned char* ub, int b, int qq, int i, const Lane& ln) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   const int HT = q.Hpad >> 4;
+  // complete chunk with whole 16-feature tiles: no per-lane bounds in the stores
+  const bool full = tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L && (q.H & 15) == 0;
+  const int HTv = (q.H + 15) >> 4;   // h-tiles holding a feature < H
   if constexpr (KEEP) {
     f32x4 yacc[kKeepHT][R];
 #pragma unroll
     for (int e = 0; e < kKeepHT; ++e)
 #pragma unroll
       for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // branch-free: C' fragments of h-tiles >= HT are zero
 #pragma unroll
     for (int s = 0; s < K2; ++s) {
       bf16x8 xf[NP][R];
       get_x<R, NP>(xb, K2, s, ln.l, xf);
 #pragma unroll
-      for (int e = 0; e < kKeepHT; ++e) {
-        if (ln.w + kWaves * e < HT) mfma_read<R, NP>(ck.f[e][s], xf, yacc[e]);
-      }
+      for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(ck.f[e][s], xf, yacc[e]);
     }
 #pragma unroll
     for (int e = 0; e < kKeepHT; ++e) {
       const int ht = ln.w + kWaves * e;
-      if (ht >= HT) continue;
+      if (ht >= HTv) continue;
 #pragma unroll
-      for (int n = 0; n < R; ++n)
-        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dk[e]);
+      for (int n = 0; n < R; ++n) {
+        float uv[4];
+        u_for_y<R, BF16>(ub, ht, n, ln, uv);
+        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, full, yacc[e][n], dk[e], uv);
+      }
     }
   } else {
     // C' streamed from L2: h-tiles (ht0, ht0 + 4), K-steps in batches of G, one batch ahead
@@ -549,12 +565,17 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        if (e == 1 && !has1) continue;
-        const int h0 = 16 * (ht0 + kWaves * e) + 4 * ln.g;
+        const int ht = ht0 + kWaves * e;
+        if ((e == 1 && !has1) || ht >= HTv) continue;
+        const int h0 = 16 * ht + 4 * ln.g;
         float dv[4];
         load_d(q, h0, dv);
 #pragma unroll
-        for (int n = 0; n < R; ++n) store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), h0, yacc[e][n], dv);
+        for (int n = 0; n < R; ++n) {
+          float uv[4];
+          u_for_y<R, BF16>(ub, ht, n, ln, uv);
+          store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), h0, full, yacc[e][n], dv, uv);
+        }
       }
     }
   }
@@ -573,8 +594,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   const int KS = q.Hpad >> 5;
   const size_t ut = u_tile_bytes(KS, R, BF16);
   const size_t xt = x_tile_bytes(K2, R, BF16);
-  unsigned char* ubuf[2] = {smem, smem + ut};
-  unsigned char* xbuf[2] = {smem + 2 * ut, smem + 2 * ut + xt};
+  // u tile i lives in ubuf[i % 3] from its load (two chunks ahead) to the
+  // feedthrough of its readout
+  unsigned char* ubuf[3] = {smem, smem + ut, smem + 2 * ut};
+  unsigned char* xbuf[2] = {smem + 3 * ut, smem + 3 * ut + xt};
 
   BKeep<MPW, NP> bk;
   CKeep<MPW, NP> ck;
@@ -663,7 +686,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   f32x4 acc[MPW][2][R];
   drive<MPW, R, BF16, KEEP>(q, bk, ubuf[0], ln.w, ln.l, acc);
 
+  int ui = 0;   // i % 3
   for (int i = 0; i < q.nck; ++i) {
+    const int ui1 = ui == 2 ? 0 : ui + 1;
+    const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
     // scan chunk i in place: acc becomes x
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
@@ -712,13 +738,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's part of u tile i+1 has landed
-    __syncthreads();                 // x tile i and u tile i+1 complete; u tile i free
-    if (i + 2 < q.nck) load_u<R, BF16>(q, b, qq, i + 2, ubuf[i & 1]);
+    __syncthreads();                 // x tile i and u tile i+1 complete; u tile i-1 free
+    if (i + 2 < q.nck) load_u<R, BF16>(q, b, qq, i + 2, ubuf[ui2]);
     if (i + 1 < q.nck) {
       if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
-      drive<MPW, R, BF16, KEEP>(q, bk, ubuf[(i + 1) & 1], ln.w, ln.l, acc);
+      drive<MPW, R, BF16, KEEP>(q, bk, ubuf[ui1], ln.w, ln.l, acc);
     }
-    readout<MPW, R, BF16, KEEP>(q, ck, dk, xb, b, qq, i, ln);
+    readout<MPW, R, BF16, KEEP>(q, ck, dk, xb, ubuf[ui], b, qq, i, ln);
+    ui = ui1;
   }
 }
 
