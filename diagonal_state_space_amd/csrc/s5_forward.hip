@@ -14,27 +14,32 @@ using fused::kStreams;
 void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p) {
   const int MPW = Ppad / 64, KS = Hpad / 32, K2 = Ppad / 16, NP = bf16_io ? 1 : 2;
   const size_t lds_max = 160 * 1024;
-  p.R = 0;
-  // bf16 instances are compiled for R = 2 (which always fits); float32 ones
-  // also for R = 1, taken where two R = 2 x tiles and u tiles exceed the LDS
-  const int cand[2] = {2, 1};
-  for (int R : cand) {
-    if (bf16_io && R != 2) continue;
-    const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io);
-    const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io);
-    if (ls > lds_max) continue;
-    p.R = R;
-    p.lds_reduce = lr;
-    p.lds_scan = ls;
-    break;
-  }
   // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
   // 16 MPW NP fragments of 16 bytes per lane; the time-varying step's own
   // registers leave room for them up to two mode tiles per wave
-  p.keep = p.R == 2 && KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
+  bool keep = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
   // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
   if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
-    if (env[0] == '0') p.keep = false;
+    if (env[0] == '0') keep = false;
+  }
+  p.R = 0;
+  // bf16 instances are compiled for R = 2 (which always fits); float32 ones
+  // also for R = 1, taken where three u tiles and two x tiles of R = 2
+  // exceed the LDS
+  const int cand[2] = {2, 1};
+  for (int R : cand) {
+    if (bf16_io && R != 2) continue;
+    const bool k = keep && R == 2;
+    const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
+                      (time_varying ? fused::mode_table_bytes(Ppad, Hpad, true, false) : 0);
+    const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
+                      (k ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
+    if (ls > lds_max || lr > lds_max) continue;
+    p.R = R;
+    p.keep = k;
+    p.lds_reduce = lr;
+    p.lds_scan = ls;
+    break;
   }
 }
 

@@ -18,6 +18,11 @@ __host__ __device__ constexpr size_t u_tile_bytes(int KS, int R, bool bf16) {
 __host__ __device__ constexpr size_t x_tile_bytes(int K2, int R, bool bf16) {
   return static_cast<size_t>(K2) * R * (bf16 ? 1 : 2) * kBlock;
 }
+// LDS bytes of the per-mode constants (abar, or lambda, 1/lambda and hrev for
+// the time-varying path) and optionally D.
+__host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool tv, bool with_d) {
+  return static_cast<size_t>(Ppad) * (tv ? 20 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
+}
 }  // namespace fused
 
 // Per-mode constants written by the packing kernel.

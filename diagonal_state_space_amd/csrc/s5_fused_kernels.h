@@ -24,9 +24,9 @@
 // parts hi = bf16(v), lo = bf16(v - hi) and sums hi.hi + hi.lo + lo.hi.
 //
 // LDS holds 1 KB blocks of 64 lanes x 16 bytes in operand-fragment order, so
-// every LDS access is lane-contiguous: u tiles (two buffers, filled with
-// global_load_lds_dwordx4 where the chunk is complete) and x tiles (two
-// buffers).
+// every LDS access is lane-contiguous: u tiles (staged through registers one
+// chunk ahead; two buffers in pass 1, three in pass 2, where the readout's D u
+// term reads them too) and x tiles (two buffers).
 #pragma once
 
 #include "s5_common.h"
@@ -40,7 +40,43 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kKeepKS = 4;     // drive K-steps held in registers (H <= 128)
 constexpr int kKeepHT = 2;     // readout h-tiles per wave held in registers (H <= 128)
 
-typedef __attribute__((address_space(3))) void lds_void;
+// LDS pointers keep their address space explicitly: a generic pointer picked
+// at run time compiles to FLAT accesses, whose waits also wait (in-order
+// vmcnt) for the asynchronous global->LDS copies in flight.
+#define S5_LDS __attribute__((address_space(3)))
+typedef S5_LDS unsigned char lds_byte;
+
+struct pf2 {   // plain float pair, accessed member by member in LDS
+  float x, y;
+};
+__device__ __forceinline__ void st_pf2(S5_LDS pf2* p, float x, float y) {
+  p->x = x;
+  p->y = y;
+}
+__device__ __forceinline__ cf ld_pf2(const S5_LDS pf2* p) { return {p->x, p->y}; }
+
+typedef uint32_t lds_v4 __attribute__((ext_vector_type(4)));
+typedef uint32_t lds_v2 __attribute__((ext_vector_type(2)));
+
+// 16- or 8-byte LDS accesses of HIP vector types through native vectors
+template <typename T>
+__device__ __forceinline__ T lds_ld(const lds_byte* p) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte LDS access");
+  if constexpr (sizeof(T) == 16) {
+    return __builtin_bit_cast(T, *reinterpret_cast<const S5_LDS lds_v4*>(p));
+  } else {
+    return __builtin_bit_cast(T, *reinterpret_cast<const S5_LDS lds_v2*>(p));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(lds_byte* p, const T& v) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte LDS access");
+  if constexpr (sizeof(T) == 16) {
+    *reinterpret_cast<S5_LDS lds_v4*>(p) = __builtin_bit_cast(lds_v4, v);
+  } else {
+    *reinterpret_cast<S5_LDS lds_v2*>(p) = __builtin_bit_cast(lds_v2, v);
+  }
+}
 
 // ---- 16-lane row scan of (a, x) pairs -----------------------------------------
 
@@ -89,72 +125,91 @@ __device__ __forceinline__ int tok_of(const FusedParams& q, int qq, int t, int i
   return (qq * kStreams + t) * q.Lseg + i * R + n;
 }
 
-// ---- u tile: global -> LDS in fragment order ---------------------------------------
+// ---- u tile: global -> registers -> LDS in fragment order -----------------------------
 // Block (s, n[, half]) holds, in lane (t, g), u[tok(t, i, n)][32 s + 8 g + ...]:
-// 8 bf16, or 4 floats per half (halves 0 and 1 = elements 0-3 and 4-7).
-template <int R, bool BF16>
-__device__ __forceinline__ void load_u(const FusedParams& q, int b, int qq, int i, unsigned char* ub) {
+// 8 bf16, or 4 floats per half (halves 0 and 1 = elements 0-3 and 4-7). Wave w
+// moves blocks w, w + 4, ...: fetch_u loads them into registers a chunk ahead,
+// stash_u writes them to LDS before the barrier that publishes the tile.
+// (Copies straight from global memory to LDS were measured slower here: every
+// LDS access after one waits for it.)
+template <int NB>
+struct UStage {
+  uint4 v[NB];
+};
+
+// registers per thread for the u tile: KS R NPU blocks over 4 waves
+template <int R, bool BF16, bool KEEP>
+constexpr int u_stage_blocks() {
+  return ((KEEP ? kKeepKS : 16) * R * (BF16 ? 1 : 2) + kWaves - 1) / kWaves;
+}
+
+template <int R, bool BF16, int NB>
+__device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int i, UStage<NB>& st) {
   constexpr int NPU = BF16 ? 1 : 2;
   const Lane ln = lane_ids();
   const int KS = q.Hpad >> 5;
   const int nblk = KS * R * NPU;
-  const int last = tok_of<R>(q, qq, kStreams - 1, i, R - 1);
+  const bool full = (q.H & 31) == 0 && tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L;
   const size_t rowb = static_cast<size_t>(b) * q.L;
-  if ((q.H & 31) == 0 && last < q.L) {
-    // complete chunk: asynchronous copies, nothing waits here
-    for (int blk = ln.w; blk < nblk; blk += kWaves) {
-      const int half = blk % NPU;
-      const int f = blk / NPU;
-      const int n = f % R;
-      const int s = f / R;
-      const int tok = tok_of<R>(q, qq, ln.t, i, n);
-      const size_t off = (rowb + tok) * q.H + 32 * s + 8 * ln.g + 4 * half;
-      const void* src = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(q.u) + off)
-                             : static_cast<const void*>(static_cast<const float*>(q.u) + off);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(ub + static_cast<size_t>(blk) * kBlock), 16, 0, 0);
-    }
-    return;
-  }
-  // ragged chunk (tokens past L or H not a multiple of 32): guarded loads, zero fill
-  for (int blk = ln.w; blk < nblk; blk += kWaves) {
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int blk = ln.w + kWaves * e;
+    if (blk >= nblk) continue;
     const int half = blk % NPU;
     const int f = blk / NPU;
     const int n = f % R;
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    uint32_t v4[4] = {0u, 0u, 0u, 0u};
-    if (tok < q.L) {
-      const size_t off = (rowb + tok) * q.H;
-      if constexpr (BF16) {
-        const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
+    const size_t off = (rowb + tok) * q.H;
+    if (full) {
+      st.v[e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.u) + off + h0)
+                     : *reinterpret_cast<const uint4*>(static_cast<const float*>(q.u) + off + h0);
+    } else {
+      // ragged chunk (tokens past L or H not a multiple of 32): zero fill
+      uint32_t v4[4] = {0u, 0u, 0u, 0u};
+      if (tok < q.L) {
+        if constexpr (BF16) {
+          const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int h = h0 + 2 * m;
-          const uint32_t lo = h < q.H ? up[h] : 0u;
-          const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
-          v4[m] = lo | (hi << 16);
+          for (int m = 0; m < 4; ++m) {
+            const int h = h0 + 2 * m;
+            const uint32_t lo = h < q.H ? up[h] : 0u;
+            const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
+            v4[m] = lo | (hi << 16);
+          }
+        } else {
+          const float* up = static_cast<const float*>(q.u) + off;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
         }
-      } else {
-        const float* up = static_cast<const float*>(q.u) + off;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
       }
+      st.v[e] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
     }
-    *reinterpret_cast<uint4*>(ub + static_cast<size_t>(blk) * kBlock + ln.l * 16) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+  }
+}
+
+template <int R, bool BF16, int NB>
+__device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& st, lds_byte* ub) {
+  const Lane ln = lane_ids();
+  const int nblk = (q.Hpad >> 5) * R * (BF16 ? 1 : 2);
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int blk = ln.w + kWaves * e;
+    if (blk < nblk) lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
   }
 }
 
 // drive operand fragments of K-step s from the u tile: [plane][n]
 template <int R, bool BF16>
-__device__ __forceinline__ void get_u(const unsigned char* ub, int s, int l, bf16x8 (&uf)[BF16 ? 1 : 2][R]) {
+__device__ __forceinline__ void get_u(const lds_byte* ub, int s, int l, bf16x8 (&uf)[BF16 ? 1 : 2][R]) {
 #pragma unroll
   for (int n = 0; n < R; ++n) {
     if constexpr (BF16) {
-      uf[0][n] = as_bf16x8(*reinterpret_cast<const uint4*>(ub + (s * R + n) * kBlock + l * 16));
+      uf[0][n] = as_bf16x8(lds_ld<uint4>(ub + (s * R + n) * kBlock + l * 16));
     } else {
-      const float4 a = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2) * kBlock + l * 16);
-      const float4 c = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2 + 1) * kBlock + l * 16);
+      const float4 a = lds_ld<float4>(ub + ((s * R + n) * 2) * kBlock + l * 16);
+      const float4 c = lds_ld<float4>(ub + ((s * R + n) * 2 + 1) * kBlock + l * 16);
       const f32x8 f = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
       const bf16x8 hi = __builtin_convertvector(f, bf16x8);
       uf[0][n] = hi;
@@ -221,7 +276,7 @@ __device__ __forceinline__ void load_b_keep(const FusedParams& q, int w, int l, 
 
 template <int MPW, int R, bool BF16, bool KEEP>
 __device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF16 ? 1 : 2>& bk,
-                                      const unsigned char* ub, int w, int l, f32x4 (&acc)[MPW][2][R]) {
+                                      const lds_byte* ub, int w, int l, f32x4 (&acc)[MPW][2][R]) {
   constexpr int NP = BF16 ? 1 : 2;
 #pragma unroll
   for (int jj = 0; jj < MPW; ++jj)
@@ -292,6 +347,39 @@ __device__ __forceinline__ float f4_at(const float4& v, int r) {
   return r == 0 ? v.x : (r == 1 ? v.y : (r == 2 ? v.z : v.w));
 }
 
+// ---- per-mode constants in LDS --------------------------------------------------------
+// Read inside the chunk loops from LDS rather than global memory: a global
+// load there would wait (in-order vmcnt) behind the asynchronous u copies.
+struct ModeTable {
+  S5_LDS pf2* ab;      // abar (time-invariant) or lambda (time-varying)   [Ppad]
+  S5_LDS pf2* il;      // 1/lambda (time-varying)                          [Ppad]
+  S5_LDS float* hr;    // hrev (time-varying)                              [Ppad]
+  S5_LDS float* d;     // D, zero past H (pass 2)                          [Hpad]
+};
+
+template <bool TV>
+__device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_byte* base, bool with_d) {
+  ModeTable mt;
+  mt.ab = reinterpret_cast<S5_LDS pf2*>(base);
+  mt.il = mt.ab + q.Ppad;
+  mt.hr = reinterpret_cast<S5_LDS float*>(TV ? mt.il + q.Ppad : mt.ab + q.Ppad);
+  mt.d = TV ? mt.hr + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
+  for (int p = threadIdx.x; p < q.Ppad; p += kThreads) {
+    const ModeParams& mq = q.modes[p];
+    if constexpr (TV) {
+      st_pf2(mt.ab + p, mq.lam.x, mq.lam.y);
+      st_pf2(mt.il + p, mq.inv_lam.x, mq.inv_lam.y);
+      mt.hr[p] = mq.hrev;
+    } else {
+      st_pf2(mt.ab + p, mq.abar.x, mq.abar.y);
+    }
+  }
+  if (with_d) {
+    for (int h = threadIdx.x; h < q.Hpad; h += kThreads) mt.d[h] = h < q.H ? q.d[h] : 0.0f;
+  }
+  return mt;   // visible after the caller's next barrier
+}
+
 // ---- pass 1 --------------------------------------------------------------------------
 
 // MPW: mode tiles per wave (Ppad = 64 MPW); R: tokens per stream per chunk.
@@ -305,7 +393,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
   const int KS = q.Hpad >> 5;
-  unsigned char* ubuf[2] = {smem, smem + u_tile_bytes(KS, R, BF16)};
+  lds_byte* lds = (lds_byte*)smem;
+  const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
+  ModeTable mt{};
+  if constexpr (TV) mt = fill_mode_table<true>(q, lds + 2 * ut, false);
 
   BKeep<MPW, NP> bk;
   if constexpr (KEEP) load_b_keep<MPW, NP>(q, ln.w, ln.l, bk);
@@ -324,15 +415,23 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
       A[jj][r] = {1.0f, 0.0f};
     }
 
-  load_u<R, BF16>(q, b, qq, 0, ubuf[0]);
-  __builtin_amdgcn_s_waitcnt(0);
+  constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
+  UStage<NB> ust;
+  float4 dl[TV ? MPW : 1][TV ? R : 1];
+  if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
+  fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
+  stash_u<R, BF16, NB>(q, ust, lds);
   __syncthreads();
+  if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
   for (int i = 0; i < q.nck; ++i) {
-    if (i + 1 < q.nck) load_u<R, BF16>(q, b, qq, i + 1, ubuf[(i + 1) & 1]);
-    float4 dl[TV ? MPW : 1][TV ? R : 1];
-    if constexpr (TV) load_delta<MPW, R>(q, b, qq, i, ln, dl);
+    // Delta of the next chunk is loaded before the next u tile is, so that
+    // waiting for it (in-order vmcnt) never waits for the u loads
+    float4 dn[TV ? MPW : 1][TV ? R : 1];
+    if constexpr (TV) {
+      if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dn);
+    }
     f32x4 acc[MPW][2][R];
-    drive<MPW, R, BF16, KEEP>(q, bk, ubuf[i & 1], ln.w, ln.l, acc);
+    drive<MPW, R, BF16, KEEP>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
 #pragma unroll
@@ -340,14 +439,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
         cf x = z[jj][r];
         if constexpr (TV) {
           const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
-          const ModeParams& mq = q.modes[pm];
-          const cf lam = {mq.lam.x, mq.lam.y};
-          const cf inv = {mq.inv_lam.x, mq.inv_lam.y};
+          const cf lam = ld_pf2(mt.ab + pm);
+          const cf inv = ld_pf2(mt.il + pm);
+          const float hrev = mt.hr[pm];
           cf Ar = A[jj][r];
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            zoh_step(lam, inv, mq.hrev, f4_at(dl[jj][n], r), a, gn);
+            zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
             Ar = cmul(a, Ar);
           }
@@ -359,8 +458,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
         z[jj][r] = x;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next u tile has landed
+    // u tile i+1 into the buffer that drive(i-1) read before the last barrier
+    if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ((i + 1) & 1) * ut);
     __syncthreads();
+    if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
+    if constexpr (TV) {
+#pragma unroll
+      for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+        for (int n = 0; n < R; ++n) dl[jj][n] = dn[jj][n];
+    }
   }
 
   // stream aggregates, then the range total over the 16 streams
@@ -401,17 +508,17 @@ struct CKeep {
 // h0 = 16 ht + 4 g, taken from u tile i in LDS (zero past H and L): block
 // (ht/2, n), lane t + 16 (2 (ht&1) + g/2), elements 4 (g&1)..+3.
 template <int R, bool BF16>
-__device__ __forceinline__ void u_for_y(const unsigned char* ub, int ht, int n, const Lane& ln, float (&uv)[4]) {
+__device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const Lane& ln, float (&uv)[4]) {
   const int s = ht >> 1;
   const int lp = ln.t + 16 * (2 * (ht & 1) + (ln.g >> 1));
   if constexpr (BF16) {
-    const uint2 p = *reinterpret_cast<const uint2*>(ub + (s * R + n) * kBlock + lp * 16 + 8 * (ln.g & 1));
+    const uint2 p = lds_ld<uint2>(ub + (s * R + n) * kBlock + lp * 16 + 8 * (ln.g & 1));
     uv[0] = __uint_as_float(p.x << 16);
     uv[1] = __uint_as_float(p.x & 0xffff0000u);
     uv[2] = __uint_as_float(p.y << 16);
     uv[3] = __uint_as_float(p.y & 0xffff0000u);
   } else {
-    const float4 p = *reinterpret_cast<const float4*>(ub + ((s * R + n) * 2 + (ln.g & 1)) * kBlock + lp * 16);
+    const float4 p = lds_ld<float4>(ub + ((s * R + n) * 2 + (ln.g & 1)) * kBlock + lp * 16);
     uv[0] = p.x; uv[1] = p.y; uv[2] = p.z; uv[3] = p.w;
   }
 }
@@ -456,12 +563,12 @@ __device__ __forceinline__ void load_d(const FusedParams& q, int h0, float (&dv)
 
 // readout operand fragments of K-step s from the x tile: [plane][n]
 template <int R, int NP>
-__device__ __forceinline__ void get_x(const unsigned char* xb, int K2, int s, int l, bf16x8 (&xf)[NP][R]) {
+__device__ __forceinline__ void get_x(const lds_byte* xb, int K2, int s, int l, bf16x8 (&xf)[NP][R]) {
 #pragma unroll
   for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
     for (int n = 0; n < R; ++n)
-      xf[pl][n] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + ((pl * K2 + s) * R + n) * kBlock + l * 16));
+      xf[pl][n] = as_bf16x8(lds_ld<uint4>(xb + ((pl * K2 + s) * R + n) * kBlock + l * 16));
 }
 
 template <int R, int NP>
@@ -487,8 +594,8 @@ __device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s,
 // y for chunk i of the workgroup's streams from the x tile and u tile in LDS
 template <int MPW, int R, bool BF16, bool KEEP>
 __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, BF16 ? 1 : 2>& ck,
-                                        const float (&dk)[kKeepHT][4], const unsigned char* xb,
-                                        const unsigned char* ub, int b, int qq, int i, const Lane& ln) {
+                                        const S5_LDS float* s_d, const lds_byte* xb,
+                                        const lds_byte* ub, int b, int qq, int i, const Lane& ln) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   const int HT = q.Hpad >> 4;
@@ -517,7 +624,9 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
       for (int n = 0; n < R; ++n) {
         float uv[4];
         u_for_y<R, BF16>(ub, ht, n, ln, uv);
-        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, full, yacc[e][n], dk[e], uv);
+        const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + 16 * ht + 4 * ln.g));
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, full, yacc[e][n], dv, uv);
       }
     }
   } else {
@@ -592,16 +701,18 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
   const int KS = q.Hpad >> 5;
-  const size_t ut = u_tile_bytes(KS, R, BF16);
-  const size_t xt = x_tile_bytes(K2, R, BF16);
-  // u tile i lives in ubuf[i % 3] from its load (two chunks ahead) to the
-  // feedthrough of its readout
-  unsigned char* ubuf[3] = {smem, smem + ut, smem + 2 * ut};
-  unsigned char* xbuf[2] = {smem + 3 * ut, smem + 3 * ut + xt};
+  const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
+  const int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
+  // u tile i lives in u buffer i % 3 from its load (two chunks ahead) to the
+  // feedthrough of its readout; x tile i in x buffer i % 2
+  lds_byte* lds = (lds_byte*)smem;
+  lds_byte* xlds = lds + 3 * ut;
+  // register-weight instances read per-mode constants and D from LDS
+  ModeTable mt{};
+  if constexpr (KEEP) mt = fill_mode_table<TV>(q, lds + 3 * ut + 2 * xt, true);
 
   BKeep<MPW, NP> bk;
   CKeep<MPW, NP> ck;
-  float dk[kKeepHT][4];
   if constexpr (KEEP) {
     load_b_keep<MPW, NP>(q, ln.w, ln.l, bk);
     const int HT = q.Hpad >> 4;
@@ -617,14 +728,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
           for (int pl = 0; pl < NP; ++pl) ck.f[e][s][pl] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
         }
       }
-      load_d(q, 16 * ht + 4 * ln.g, dk[e]);
     }
   }
 
   // ---- state entering each stream ----
   // carry into the range: the totals of the sequence's earlier ranges, folded in
   // order; it waits in LDS (the second x buffer is not written before the loop).
-  float2* s_c0 = reinterpret_cast<float2*>(xbuf[1]);
+  S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);
   if (ln.tid < q.Ppad) {
     cf c = {0.0f, 0.0f};
     const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + ln.tid;
@@ -645,11 +755,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
         if (q0 + e < qq) c = cfma(as[e], c, xs[e]);
       }
     }
-    s_c0[ln.tid] = make_float2(c.re, c.im);
+    st_pf2(s_c0 + ln.tid, c.re, c.im);
   }
   __syncthreads();
 
-  cf abar[MPW][4];
+  cf abar[KEEP ? 1 : MPW][4];   // register copy when the table is not in LDS
   cf st[MPW][4];
 #pragma unroll
   for (int jj = 0; jj < MPW; ++jj) {
@@ -657,7 +767,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
     for (int r = 0; r < 4; ++r) {
       const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
       const ModeParams& mq = q.modes[pm];
-      abar[jj][r] = {mq.abar.x, mq.abar.y};
+      if constexpr (!KEEP) abar[jj][r] = {mq.abar.x, mq.abar.y};
       const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
       const float2 xv = q.sagg[si];
       cf X = {xv.x, xv.y};
@@ -671,25 +781,25 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       row_scan(A, X);
       const cf Ae = {row_shr<1>(A.re, 1.0f), row_shr<1>(A.im, 0.0f)};
       const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
-      const float2 c0 = s_c0[pm];
-      st[jj][r] = cfma(Ae, {c0.x, c0.y}, Xe);
+      st[jj][r] = cfma(Ae, ld_pf2(s_c0 + pm), Xe);
     }
   }
 
   // ---- chunk pipeline ----
-  load_u<R, BF16>(q, b, qq, 0, ubuf[0]);
-  __builtin_amdgcn_s_waitcnt(0);
+  constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
+  UStage<NB> ust;
+  fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
+  stash_u<R, BF16, NB>(q, ust, lds);
   __syncthreads();
-  if (q.nck > 1) load_u<R, BF16>(q, b, qq, 1, ubuf[1]);
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
+  if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
   f32x4 acc[MPW][2][R];
-  drive<MPW, R, BF16, KEEP>(q, bk, ubuf[0], ln.w, ln.l, acc);
+  drive<MPW, R, BF16, KEEP>(q, bk, lds, ln.w, ln.l, acc);
 
   int ui = 0;   // i % 3
   for (int i = 0; i < q.nck; ++i) {
     const int ui1 = ui == 2 ? 0 : ui + 1;
-    const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
     // scan chunk i in place: acc becomes x
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
@@ -698,21 +808,36 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
         cf x = st[jj][r];
         if constexpr (TV) {
           const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
-          const ModeParams& mq = q.modes[pm];
-          const cf lam = {mq.lam.x, mq.lam.y};
-          const cf inv = {mq.inv_lam.x, mq.inv_lam.y};
+          cf lam, inv;
+          float hrev;
+          if constexpr (KEEP) {
+            lam = ld_pf2(mt.ab + pm);
+            inv = ld_pf2(mt.il + pm);
+            hrev = mt.hr[pm];
+          } else {
+            const ModeParams& mq = q.modes[pm];
+            lam = {mq.lam.x, mq.lam.y};
+            inv = {mq.inv_lam.x, mq.inv_lam.y};
+            hrev = mq.hrev;
+          }
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            zoh_step(lam, inv, mq.hrev, f4_at(dl[jj][n], r), a, gn);
+            zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
             acc[jj][0][n][r] = x.re;
             acc[jj][1][n][r] = x.im;
           }
         } else {
+          cf ab;
+          if constexpr (KEEP) {
+            ab = ld_pf2(mt.ab + 16 * (ln.w + kWaves * jj) + 4 * ln.g + r);
+          } else {
+            ab = abar[jj][r];
+          }
 #pragma unroll
           for (int n = 0; n < R; ++n) {
-            x = cfma(abar[jj][r], x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+            x = cfma(ab, x, {acc[jj][0][n][r], acc[jj][1][n][r]});
             acc[jj][0][n][r] = x.re;
             acc[jj][1][n][r] = x.im;
           }
@@ -721,7 +846,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       }
     }
     // x tile: block (mode tile j, n), lane (t, g): modes 16 j + 4 g + r, parts interleaved
-    unsigned char* xb = xbuf[i & 1];
+    lds_byte* xb = xlds + (i & 1) * xt;
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
 #pragma unroll
@@ -733,18 +858,24 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
           v[2 * r + 1] = acc[jj][1][n][r];
         }
         const int blk = (ln.w + kWaves * jj) * R + n;
-        put_frag(v, reinterpret_cast<uint4*>(xb + blk * kBlock + ln.l * 16),
-                 BF16 ? nullptr : reinterpret_cast<uint4*>(xb + (K2 * R + blk) * kBlock + ln.l * 16));
+        uint4 hi, lo;
+        put_frag(v, &hi, BF16 ? nullptr : &lo);
+        lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
+        if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of u tile i+1 has landed
-    __syncthreads();                 // x tile i and u tile i+1 complete; u tile i-1 free
-    if (i + 2 < q.nck) load_u<R, BF16>(q, b, qq, i + 2, ubuf[ui2]);
-    if (i + 1 < q.nck) {
-      if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
-      drive<MPW, R, BF16, KEEP>(q, bk, ubuf[ui1], ln.w, ln.l, acc);
+    // u tile i+1 into the buffer that held tile i-2 (its last reader, the
+    // feedthrough of readout(i-2), finished before the previous barrier)
+    if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui1 * ut);
+    __syncthreads();   // x tile i and u tile i+1 complete
+    // Delta of chunk i+1 is loaded before u tile i+2, so that waiting for it
+    // (in-order vmcnt) never waits for the u loads
+    if constexpr (TV) {
+      if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
     }
-    readout<MPW, R, BF16, KEEP>(q, ck, dk, xb, ubuf[ui], b, qq, i, ln);
+    if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
+    if (i + 1 < q.nck) drive<MPW, R, BF16, KEEP>(q, bk, lds + ui1 * ut, ln.w, ln.l, acc);
+    readout<MPW, R, BF16, KEEP>(q, ck, mt.d, xb, lds + ui * ut, b, qq, i, ln);
     ui = ui1;
   }
 }
