@@ -15,12 +15,15 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   const int MPW = Ppad / 64, KS = Hpad / 32, K2 = Ppad / 16, NP = bf16_io ? 1 : 2;
   const size_t lds_max = 160 * 1024;
   // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
-  // 16 MPW NP fragments of 16 bytes per lane; the time-varying step's own
-  // registers leave room for them up to two mode tiles per wave
+  // 16 MPW NP fragments of 16 bytes per lane. Pass 1 (one wave per SIMD) keeps
+  // them up to MPW NP = 4 (two mode tiles per wave with the time-varying
+  // step's registers); pass 2 (two waves per SIMD, 256 registers each) up to
+  // MPW NP = 4, or 2 with the time-varying step
   bool keep = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
+  bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW * NP > 2);
   // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
   if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
-    if (env[0] == '0') keep = false;
+    if (env[0] == '0') keep = keep_scan = false;
   }
   p.R = 0;
   // bf16 instances are compiled for R = 2 (which always fits); float32 ones
@@ -30,20 +33,22 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   for (int R : cand) {
     if (bf16_io && R != 2) continue;
     const bool k = keep && R == 2;
+    const bool ks = keep_scan && R == 2;
     const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
                       (time_varying ? fused::mode_table_bytes(Ppad, Hpad, true, false) : 0);
     const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
-                      (k ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
+                      (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
     p.R = R;
     p.keep = k;
+    p.keep_scan = ks;
     p.lds_reduce = lr;
     p.lds_scan = ls;
     break;
   }
 }
 
-void fused_split(int B, int L, int ncu, FusedPlan& p) {
+void fused_split(int B, int L, int H, int P, int ncu, FusedPlan& p) {
   const int per = kStreams * p.R;                  // tokens of one chunk of a range
   const int chunks = (L + per - 1) / per;          // chunks with a single range
   int Q = std::max(1, (ncu + B - 1) / B);          // ranges per sequence to fill the CUs
@@ -51,6 +56,14 @@ void fused_split(int B, int L, int ncu, FusedPlan& p) {
   p.nck = (L + Q * per - 1) / (Q * per);
   p.Lseg = p.R * p.nck;
   p.Q = (L + kStreams * p.Lseg - 1) / (kStreams * p.Lseg);
+  // a range's rows of u, y and Delta stay below 1 GiB (32-bit lane offsets)
+  const int64_t row_bytes = static_cast<int64_t>(std::max(H, P)) * 4;
+  while (static_cast<int64_t>(kStreams) * p.Lseg * row_bytes >= (int64_t{1} << 30) && p.nck > 1) {
+    Q = std::min(chunks, 2 * Q);
+    p.nck = (L + Q * per - 1) / (Q * per);
+    p.Lseg = p.R * p.nck;
+    p.Q = (L + kStreams * p.Lseg - 1) / (kStreams * p.Lseg);
+  }
 }
 
 namespace {
@@ -77,7 +90,7 @@ Layout layout(const ForwardArgs& a) {
   fused_shape(a.bf16_io, a.time_varying, l.Ppad, l.Hpad, l.plan);
   if (l.plan.R == 0) return l;
   const int ncu = device_cus();
-  fused_split(a.B, a.L, ncu > 0 ? ncu : 256, l.plan);
+  fused_split(a.B, a.L, a.H, a.P, ncu > 0 ? ncu : 256, l.plan);
   const size_t planes = a.bf16_io ? 1 : 2;
   const size_t nb = static_cast<size_t>(l.Ppad / 16) * 2 * (l.Hpad / 32) * 64;
   const size_t nc = static_cast<size_t>(l.Hpad / 16) * (2 * l.Ppad / 32) * 64;

@@ -70,14 +70,16 @@ struct FusedParams {
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.
 struct FusedPlan {
   int R = 0, nck = 0, Lseg = 0, Q = 0;
-  bool keep = false;   // weights held in registers for the whole kernel
+  bool keep = false;        // pass 1 holds B_bar in registers
+  bool keep_scan = false;   // pass 2 holds B_bar and C' in registers (wave-specialized kernel)
   size_t lds_reduce = 0, lds_scan = 0;
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).
 void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p);
-// Fill in nck, Lseg and Q for B sequences of length L on `ncu` compute units.
-void fused_split(int B, int L, int ncu, FusedPlan& p);
+// Fill in nck, Lseg and Q for B sequences of length L (features H, modes P)
+// on `ncu` compute units.
+void fused_split(int B, int L, int H, int P, int ncu, FusedPlan& p);
 
 hipError_t launch_pack(const FusedParams& q, hipStream_t stream);
 

@@ -45,9 +45,10 @@ hipError_t by_mpw(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
 template <bool REDUCE>
 hipError_t dispatch(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   if (q.bf16_io != kBF16 || q.time_varying != kTV) return hipErrorInvalidValue;
-  if (p.R == 2) return p.keep ? by_mpw<REDUCE, 2, true>(q, p, s) : by_mpw<REDUCE, 2, false>(q, p, s);
+  const bool keep = REDUCE ? p.keep : p.keep_scan;
+  if (p.R == 2) return keep ? by_mpw<REDUCE, 2, true>(q, p, s) : by_mpw<REDUCE, 2, false>(q, p, s);
   if constexpr (!kBF16) {
-    if (p.R == 1 && !p.keep) return by_mpw<REDUCE, 1, false>(q, p, s);
+    if (p.R == 1 && !keep) return by_mpw<REDUCE, 1, false>(q, p, s);
   }
   return hipErrorInvalidValue;
 }

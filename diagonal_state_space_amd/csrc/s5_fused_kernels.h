@@ -109,9 +109,10 @@ struct Lane {
   int tid, w, l, t, g;
 };
 
+// ids within a group of kWaves waves (the role of a wave-specialized kernel)
 __device__ __forceinline__ Lane lane_ids() {
   Lane x;
-  x.tid = threadIdx.x;
+  x.tid = threadIdx.x & (kThreads - 1);
   x.w = x.tid >> 6;
   x.l = x.tid & 63;
   x.t = x.l & 15;
@@ -123,6 +124,19 @@ __device__ __forceinline__ Lane lane_ids() {
 template <int R>
 __device__ __forceinline__ int tok_of(const FusedParams& q, int qq, int t, int i, int n) {
   return (qq * kStreams + t) * q.Lseg + i * R + n;
+}
+
+// Row (in [B*L]) of the first token of workgroup range (b, qq). Hot global
+// accesses use this uniform row's address plus a 32-bit lane offset (the host
+// keeps a range below 1 GiB), so that no 64-bit per-lane address stays live.
+__device__ __forceinline__ size_t range_row0(const FusedParams& q, int b, int qq) {
+  return static_cast<size_t>(b) * q.L + static_cast<size_t>(qq) * kStreams * q.Lseg;
+}
+
+// row of (stream t, chunk i, step n) relative to range_row0
+template <int R>
+__device__ __forceinline__ uint32_t rel_row(const FusedParams& q, int t, int i, int n) {
+  return static_cast<uint32_t>(t * q.Lseg + i * R + n);
 }
 
 // ---- u tile: global -> registers -> LDS in fragment order -----------------------------
@@ -150,6 +164,7 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int
   const int KS = q.Hpad >> 5;
   const int nblk = KS * R * NPU;
   const bool full = (q.H & 31) == 0 && tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L;
+  const size_t row0 = range_row0(q, b, qq);
   const size_t rowb = static_cast<size_t>(b) * q.L;
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
@@ -161,11 +176,12 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    const size_t off = (rowb + tok) * q.H;
     if (full) {
-      st.v[e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.u) + off + h0)
-                     : *reinterpret_cast<const uint4*>(static_cast<const float*>(q.u) + off + h0);
+      const uint32_t o = rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0;
+      st.v[e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.u) + row0 * q.H + o)
+                     : *reinterpret_cast<const uint4*>(static_cast<const float*>(q.u) + row0 * q.H + o);
     } else {
+      const size_t off = (rowb + tok) * q.H;
       // ragged chunk (tokens past L or H not a multiple of 32): zero fill
       uint32_t v4[4] = {0u, 0u, 0u, 0u};
       if (tok < q.L) {
@@ -329,7 +345,8 @@ __device__ __forceinline__ void load_delta(const FusedParams& q, int b, int qq, 
       const int tok = tok_of<R>(q, qq, ln.t, i, n);
       float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (tok < q.L && pm0 < q.P) {
-        const float* dp = q.delta + (static_cast<size_t>(b) * q.L + tok) * q.P + pm0;
+        const float* dp = q.delta + range_row0(q, b, qq) * q.P +
+                          (rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.P) + pm0);
         if (vec) {
           const float4 x = *reinterpret_cast<const float4*>(dp);
           v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -523,34 +540,37 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
   }
 }
 
-// y = acc + D u for 4 consecutive features; `full`: token < L and h0 + 4 <= H
-// are known, the row is 16-byte aligned (fp32) or 8-byte aligned (bf16)
+// y = acc + D u for 4 consecutive features y[tok][h0..h0+3], tok < L and
+// h0 + 4 <= H known (complete chunk, H a multiple of 16): one vector store,
+// bf16 rounding by the hardware conversion (round to nearest even)
 template <bool BF16>
-__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, bool full, const f32x4& acc,
+__device__ __forceinline__ void store_y_full(void* yrow, const f32x4& acc, const float4& d4, const float (&uv)[4]) {
+  const f32x4 yv = {fmaf(d4.x, uv[0], acc[0]), fmaf(d4.y, uv[1], acc[1]), fmaf(d4.z, uv[2], acc[2]),
+                    fmaf(d4.w, uv[3], acc[3])};
+  if constexpr (BF16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<uint2*>(yrow) = __builtin_bit_cast(uint2, __builtin_convertvector(yv, bf16x4));
+  } else {
+    *reinterpret_cast<float4*>(yrow) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+  }
+}
+
+// the same for a ragged chunk: per-lane bounds on the token and the features
+template <bool BF16>
+__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, const f32x4& acc,
                                         const float (&dv)[4], const float (&uv)[4]) {
   float yv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) yv[r] = fmaf(dv[r], uv[r], acc[r]);
-  if (!full && (tok >= q.L || h0 >= q.H)) return;
+  if (tok >= q.L || h0 >= q.H) return;
   const size_t row = (static_cast<size_t>(b) * q.L + tok) * q.H;
-  if (full || ((q.H & 3) == 0)) {   // h0 + 4 <= H: h0 is a multiple of 4
-    if constexpr (BF16) {
-      uint2 pk;
-      pk.x = static_cast<uint32_t>(f32_to_bf16(yv[0])) | (static_cast<uint32_t>(f32_to_bf16(yv[1])) << 16);
-      pk.y = static_cast<uint32_t>(f32_to_bf16(yv[2])) | (static_cast<uint32_t>(f32_to_bf16(yv[3])) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(q.y) + row + h0) = pk;
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(q.y) + row + h0) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-    }
-  } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (h0 + r < q.H) {
-        if constexpr (BF16) {
-          static_cast<uint16_t*>(q.y)[row + h0 + r] = f32_to_bf16(yv[r]);
-        } else {
-          static_cast<float*>(q.y)[row + h0 + r] = yv[r];
-        }
+  for (int r = 0; r < 4; ++r) {
+    if (h0 + r < q.H) {
+      if constexpr (BF16) {
+        static_cast<uint16_t*>(q.y)[row + h0 + r] = f32_to_bf16(yv[r]);
+      } else {
+        static_cast<float*>(q.y)[row + h0 + r] = yv[r];
       }
     }
   }
@@ -616,17 +636,38 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
 #pragma unroll
       for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(ck.f[e][s], xf, yacc[e]);
     }
+    if (full) {
+      // lane's token rows of this chunk: tok(t, i, n) = tok(t, i, 0) + n
+      const size_t row0 = (static_cast<size_t>(b) * q.L + tok_of<R>(q, qq, ln.t, i, 0)) * q.H;
 #pragma unroll
-    for (int e = 0; e < kKeepHT; ++e) {
-      const int ht = ln.w + kWaves * e;
-      if (ht >= HTv) continue;
+      for (int e = 0; e < kKeepHT; ++e) {
+        const int ht = ln.w + kWaves * e;
+        if (ht >= HTv) continue;
+        const int h0 = 16 * ht + 4 * ln.g;
+        const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + h0));
 #pragma unroll
-      for (int n = 0; n < R; ++n) {
-        float uv[4];
-        u_for_y<R, BF16>(ub, ht, n, ln, uv);
+        for (int n = 0; n < R; ++n) {
+          float uv[4];
+          u_for_y<R, BF16>(ub, ht, n, ln, uv);
+          const size_t off = row0 + static_cast<size_t>(n) * q.H + h0;
+          store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + off)
+                                  : static_cast<void*>(static_cast<float*>(q.y) + off),
+                             yacc[e][n], d4, uv);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kKeepHT; ++e) {
+        const int ht = ln.w + kWaves * e;
+        if (ht >= HTv) continue;
         const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + 16 * ht + 4 * ln.g));
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, full, yacc[e][n], dv, uv);
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          float uv[4];
+          u_for_y<R, BF16>(ub, ht, n, ln, uv);
+          store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dv, uv);
+        }
       }
     }
   } else {
@@ -683,8 +724,59 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
         for (int n = 0; n < R; ++n) {
           float uv[4];
           u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), h0, full, yacc[e][n], dv, uv);
+          const int tok = tok_of<R>(q, qq, ln.t, i, n);
+          if (full) {
+            const size_t off = range_row0(q, b, qq) * q.H + (rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0);
+            store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + off)
+                                    : static_cast<void*>(static_cast<float*>(q.y) + off),
+                               yacc[e][n], make_float4(dv[0], dv[1], dv[2], dv[3]), uv);
+          } else {
+            store_y<BF16>(q, b, tok, h0, yacc[e][n], dv, uv);
+          }
         }
+      }
+    }
+  }
+}
+
+// y of chunk i from the register-weight readout's accumulators: feedthrough
+// from u tile i in LDS and D from the LDS table
+template <int R, bool BF16>
+__device__ __forceinline__ void readout_store(const FusedParams& q, const S5_LDS float* s_d,
+                                              const f32x4 (&yacc)[kKeepHT][R], const lds_byte* ub, int HT,
+                                              int HTv, int b, int qq, int i, const Lane& ln) {
+  (void)HT;
+  const bool full = tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L && (q.H & 15) == 0;
+  if (full) {
+    const size_t base = range_row0(q, b, qq) * q.H;   // uniform
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+      if (ht >= HTv) continue;
+      const int h0 = 16 * ht + 4 * ln.g;
+      const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + h0));
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        float uv[4];
+        u_for_y<R, BF16>(ub, ht, n, ln, uv);
+        const uint32_t o = rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0;
+        store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + base + o)
+                                : static_cast<void*>(static_cast<float*>(q.y) + base + o),
+                           yacc[e][n], d4, uv);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+      if (ht >= HTv) continue;
+      const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + 16 * ht + 4 * ln.g));
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        float uv[4];
+        u_for_y<R, BF16>(ub, ht, n, ln, uv);
+        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dv, uv);
       }
     }
   }
@@ -797,85 +889,347 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   f32x4 acc[MPW][2][R];
   drive<MPW, R, BF16, KEEP>(q, bk, lds, ln.w, ln.l, acc);
 
+  // scan of mode group (jj, r) of the chunk in acc, in place: acc becomes x
+  auto scan_group = [&](int jj, int r) {
+    cf x = st[jj][r];
+    if constexpr (TV) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      cf lam, inv;
+      float hrev;
+      if constexpr (KEEP) {
+        lam = ld_pf2(mt.ab + pm);
+        inv = ld_pf2(mt.il + pm);
+        hrev = mt.hr[pm];
+      } else {
+        const ModeParams& mq = q.modes[pm];
+        lam = {mq.lam.x, mq.lam.y};
+        inv = {mq.inv_lam.x, mq.inv_lam.y};
+        hrev = mq.hrev;
+      }
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        cf a, gn;
+        zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
+        x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+        acc[jj][0][n][r] = x.re;
+        acc[jj][1][n][r] = x.im;
+      }
+    } else {
+      cf ab;
+      if constexpr (KEEP) {
+        ab = ld_pf2(mt.ab + 16 * (ln.w + kWaves * jj) + 4 * ln.g + r);
+      } else {
+        ab = abar[jj][r];
+      }
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        x = cfma(ab, x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+        acc[jj][0][n][r] = x.re;
+        acc[jj][1][n][r] = x.im;
+      }
+    }
+    st[jj][r] = x;
+  };
+  // x tile blocks (mode tile j = w + 4 jj, n), lane (t, g): modes 16 j + 4 g + r, parts interleaved
+  auto write_x = [&](int jj, lds_byte* xb) {
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[2 * r] = acc[jj][0][n][r];
+        v[2 * r + 1] = acc[jj][1][n][r];
+      }
+      const int blk = (ln.w + kWaves * jj) * R + n;
+      uint4 hi, lo;
+      put_frag(v, &hi, BF16 ? nullptr : &lo);
+      lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
+      if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+    }
+  };
+
+  {
+    int ui = 0;   // i % 3
+    for (int i = 0; i < q.nck; ++i) {
+      const int ui1 = ui == 2 ? 0 : ui + 1;
+#pragma unroll
+      for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scan_group(jj, r);
+      lds_byte* xb = xlds + (i & 1) * xt;
+#pragma unroll
+      for (int jj = 0; jj < MPW; ++jj) write_x(jj, xb);
+      // u tile i+1 into the buffer that held tile i-2 (its last reader, the
+      // feedthrough of readout(i-2), finished before the previous barrier)
+      if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui1 * ut);
+      __syncthreads();   // x tile i and u tile i+1 complete
+      // Delta of chunk i+1 is loaded before u tile i+2, so that waiting for it
+      // (in-order vmcnt) never waits for the u loads
+      if constexpr (TV) {
+        if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
+      }
+      if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
+      drive<MPW, R, BF16, KEEP>(q, bk, lds + ui1 * ut, ln.w, ln.l, acc);
+      readout<MPW, R, BF16, KEEP>(q, ck, mt.d, xb, lds + ui * ut, b, qq, i, ln);
+      ui = ui1;
+    }
+  }
+}
+
+// ---- pass 2, wave-specialized (register-resident weights) ------------------------------
+// Eight waves: waves 0-3 drive (B_bar in registers: drive MFMA, scan, x tile),
+// waves 4-7 read out (C' in registers: readout MFMA, D u feedthrough, y, and
+// the staging of the u tiles). Waves are placed on the four SIMDs in turn, so
+// every SIMD runs one wave of each kind: the drive wave's scan and the
+// readout wave's LDS waits proceed while the other wave's MFMAs run. Chunk
+// i+1 is driven and scanned while chunk i is read out; one barrier per chunk.
+
+// carry into the workgroup's range: the totals of the sequence's earlier
+// ranges folded in order (one thread per mode)
+__device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq, int p, S5_LDS pf2* s_c0) {
+  cf c = {0.0f, 0.0f};
+  const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + p;
+  constexpr int kBatch = 8;
+  for (int q0 = 0; q0 < qq; q0 += kBatch) {
+    cf xs[kBatch], as[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      if (q0 + e < qq) {
+        const float2 xv = q.tot[base + static_cast<size_t>(q0 + e) * q.Ppad];
+        const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
+        xs[e] = {xv.x, xv.y};
+        as[e] = {av.x, av.y};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      if (q0 + e < qq) c = cfma(as[e], c, xs[e]);
+    }
+  }
+  st_pf2(s_c0 + p, c.re, c.im);
+}
+
+// state entering the lane's stream for its modes: exclusive 16-lane scan of
+// the stream aggregates, applied to the range carry
+template <int MPW, bool TV>
+__device__ __forceinline__ void stream_start(const FusedParams& q, int bq, const Lane& ln, const S5_LDS pf2* s_c0,
+                                             cf (&st)[MPW][4]) {
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
+      const float2 xv = q.sagg[si];
+      cf X = {xv.x, xv.y};
+      cf A;
+      if constexpr (TV) {
+        const float2 av = q.sagg_a[si];
+        A = {av.x, av.y};
+      } else {
+        const float2 as = q.modes[pm].aseg;
+        A = {as.x, as.y};
+      }
+      row_scan(A, X);
+      const cf Ae = {row_shr<1>(A.re, 1.0f), row_shr<1>(A.im, 0.0f)};
+      const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
+      st[jj][r] = cfma(Ae, ld_pf2(s_c0 + pm), Xe);
+    }
+  }
+}
+
+// Drive, scan and x tile of the wave's mode tiles j0 .. j0 + JG - 1 (those
+// below MPW) for one chunk: the accumulators of JG tiles only are live.
+template <int MPW, int JG, int R, bool TV, bool BF16>
+__device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk,
+                                                 const lds_byte* ub, const ModeTable& mt, const Lane& ln,
+                                                 const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
+                                                 cf (&st)[MPW][4], lds_byte* xb) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int K2 = 4 * MPW;
+  f32x4 acc[JG][2][R];
+#pragma unroll
+  for (int jj = 0; jj < JG; ++jj)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int n = 0; n < R; ++n) acc[jj][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < kKeepKS; ++s) {
+    bf16x8 uf[NP][R];
+    get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
+#pragma unroll
+    for (int jj = 0; jj < JG; ++jj) {
+      if (j0 + jj >= MPW) continue;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uf[0][n], acc[jj][cc][n]);
+          if constexpr (NP == 2) {
+            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uf[1][n], acc[jj][cc][n]);
+            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][1], uf[0][n], acc[jj][cc][n]);
+          }
+        }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < JG; ++jj) {
+    if (j0 + jj >= MPW) continue;
+    const int j = j0 + jj;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * j) + 4 * ln.g + r;
+      cf x = st[j][r];
+      if constexpr (TV) {
+        const cf lam = ld_pf2(mt.ab + pm);
+        const cf inv = ld_pf2(mt.il + pm);
+        const float hrev = mt.hr[pm];
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          cf a, gn;
+          zoh_step(lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
+          x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+          acc[jj][0][n][r] = x.re;
+          acc[jj][1][n][r] = x.im;
+        }
+      } else {
+        const cf ab = ld_pf2(mt.ab + pm);
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          x = cfma(ab, x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+          acc[jj][0][n][r] = x.re;
+          acc[jj][1][n][r] = x.im;
+        }
+      }
+      st[j][r] = x;
+    }
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[2 * r] = acc[jj][0][n][r];
+        v[2 * r + 1] = acc[jj][1][n][r];
+      }
+      const int blk = (ln.w + kWaves * j) * R + n;
+      uint4 hi, lo;
+      put_frag(v, &hi, BF16 ? nullptr : &lo);
+      lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
+      if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+    }
+  }
+}
+
+// one chunk of a drive wave, JG mode tiles at a time
+template <int MPW, int R, bool TV, bool BF16>
+__device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk, const lds_byte* ub,
+                                                 const ModeTable& mt, const Lane& ln,
+                                                 const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
+                                                 cf (&st)[MPW][4], lds_byte* xb) {
+  constexpr int JG = MPW >= 4 ? 1 : (MPW < 2 ? MPW : 2);
+#pragma unroll
+  for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16>(j0, KS, bk, ub, mt, ln, dl, st, xb);
+}
+
+template <int MPW, int R, bool TV, bool BF16>
+__global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int K2 = 4 * MPW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
+  const bool driver = threadIdx.x < kThreads;    // waves 0-3; waves 4-7 read out
+  const Lane ln = lane_ids();                    // ids within the role
+  const int bq = blockIdx.x;
+  const int b = bq / q.Q;
+  const int qq = bq - b * q.Q;
+  const int KS = q.Hpad >> 5;
+  const int HT = q.Hpad >> 4;
+  const int HTv = (q.H + 15) >> 4;
+  const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
+  const int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
+  // u tile i in buffer i % 3 (staged by the readout waves two chunks ahead,
+  // read by drive(i) and by the feedthrough of readout(i)); x tile i in x
+  // buffer i % 2 (written by the drive waves, read by the readout waves)
+  lds_byte* lds = (lds_byte*)smem;
+  lds_byte* xlds = lds + 3 * ut;
+  const ModeTable mt = fill_mode_table<TV>(q, lds + 3 * ut + 2 * xt, true);
+  S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
+  if (driver && ln.tid < q.Ppad) range_carry(q, b, qq, ln.tid, s_c0);
+
+  constexpr int NB = u_stage_blocks<R, BF16, true>();
+  UStage<NB> ust;
+  // one register array holds the role's weights: B_bar fragments [s][jj][cc][pl]
+  // in drive waves, C' fragments [e][s][pl] in readout waves (16 MPW NP each)
+  static_assert(sizeof(BKeep<MPW, NP>) == sizeof(CKeep<MPW, NP>), "both roles hold 16 MPW NP fragments");
+  union Weights {
+    BKeep<MPW, NP> b;
+    CKeep<MPW, NP> c;
+  };
+  Weights wts;
+  cf st[MPW][4];
+  if (driver) {
+    load_b_keep<MPW, NP>(q, ln.w, ln.l, wts.b);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+#pragma unroll
+      for (int s = 0; s < K2; ++s) {
+        if (ht < HT) {
+          load_c_step<MPW, NP>(q, ht, s, ln.l, wts.c.f[e][s]);
+        } else {
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) wts.c.f[e][s][pl] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+        }
+      }
+    }
+    fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
+    stash_u<R, BF16, NB>(q, ust, lds);
+    if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
+  }
+  __syncthreads();   // carry, mode table, u tile 0
+  float4 dl[TV ? MPW : 1][TV ? R : 1];
+  if (driver) {
+    stream_start<MPW, TV>(q, bq, ln, s_c0, st);
+    if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
+    drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds, mt, ln, dl, st, xlds);
+  } else {
+    if (q.nck > 1) stash_u<R, BF16, NB>(q, ust, lds + ut);
+    if (q.nck > 2) fetch_u<R, BF16, NB>(q, b, qq, 2, ust);
+  }
+  __syncthreads();   // x tile 0, u tile 1
+
   int ui = 0;   // i % 3
   for (int i = 0; i < q.nck; ++i) {
     const int ui1 = ui == 2 ? 0 : ui + 1;
-    // scan chunk i in place: acc becomes x
-#pragma unroll
-    for (int jj = 0; jj < MPW; ++jj) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        cf x = st[jj][r];
-        if constexpr (TV) {
-          const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
-          cf lam, inv;
-          float hrev;
-          if constexpr (KEEP) {
-            lam = ld_pf2(mt.ab + pm);
-            inv = ld_pf2(mt.il + pm);
-            hrev = mt.hr[pm];
-          } else {
-            const ModeParams& mq = q.modes[pm];
-            lam = {mq.lam.x, mq.lam.y};
-            inv = {mq.inv_lam.x, mq.inv_lam.y};
-            hrev = mq.hrev;
-          }
-#pragma unroll
-          for (int n = 0; n < R; ++n) {
-            cf a, gn;
-            zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
-            x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
-            acc[jj][0][n][r] = x.re;
-            acc[jj][1][n][r] = x.im;
-          }
-        } else {
-          cf ab;
-          if constexpr (KEEP) {
-            ab = ld_pf2(mt.ab + 16 * (ln.w + kWaves * jj) + 4 * ln.g + r);
-          } else {
-            ab = abar[jj][r];
-          }
-#pragma unroll
-          for (int n = 0; n < R; ++n) {
-            x = cfma(ab, x, {acc[jj][0][n][r], acc[jj][1][n][r]});
-            acc[jj][0][n][r] = x.re;
-            acc[jj][1][n][r] = x.im;
-          }
-        }
-        st[jj][r] = x;
+    const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
+    if (driver) {
+      if (i + 1 < q.nck) {
+        if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
+        drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds + ui1 * ut, mt, ln, dl, st, xlds + ((i + 1) & 1) * xt);
       }
-    }
-    // x tile: block (mode tile j, n), lane (t, g): modes 16 j + 4 g + r, parts interleaved
-    lds_byte* xb = xlds + (i & 1) * xt;
+    } else {
+      const lds_byte* xr = xlds + (i & 1) * xt;
+      f32x4 yacc[kKeepHT][R];
 #pragma unroll
-    for (int jj = 0; jj < MPW; ++jj) {
+      for (int e = 0; e < kKeepHT; ++e)
 #pragma unroll
-      for (int n = 0; n < R; ++n) {
-        float v[8];
+        for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[2 * r] = acc[jj][0][n][r];
-          v[2 * r + 1] = acc[jj][1][n][r];
-        }
-        const int blk = (ln.w + kWaves * jj) * R + n;
-        uint4 hi, lo;
-        put_frag(v, &hi, BF16 ? nullptr : &lo);
-        lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
-        if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+      for (int s = 0; s < K2; ++s) {
+        bf16x8 xf[NP][R];
+        get_x<R, NP>(xr, K2, s, ln.l, xf);
+#pragma unroll
+        for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(wts.c.f[e][s], xf, yacc[e]);
       }
+      readout_store<R, BF16>(q, mt.d, yacc, lds + ui * ut, HT, HTv, b, qq, i, ln);
+      // u tile i+2 into the buffer of tile i-1 (read by drive(i-1) and
+      // readout(i-1), both before the previous barrier)
+      if (i + 2 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui2 * ut);
+      if (i + 3 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 3, ust);
     }
-    // u tile i+1 into the buffer that held tile i-2 (its last reader, the
-    // feedthrough of readout(i-2), finished before the previous barrier)
-    if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui1 * ut);
-    __syncthreads();   // x tile i and u tile i+1 complete
-    // Delta of chunk i+1 is loaded before u tile i+2, so that waiting for it
-    // (in-order vmcnt) never waits for the u loads
-    if constexpr (TV) {
-      if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
-    }
-    if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
-    if (i + 1 < q.nck) drive<MPW, R, BF16, KEEP>(q, bk, lds + ui1 * ut, ln.w, ln.l, acc);
-    readout<MPW, R, BF16, KEEP>(q, ck, mt.d, xb, lds + ui * ut, b, qq, i, ln);
+    __syncthreads();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
     ui = ui1;
   }
 }
@@ -894,11 +1248,19 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
 
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
-  auto kern = k_scan<MPW, R, TV, BF16, KEEP>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_scan, s, q);
+  if constexpr (KEEP) {
+    auto kern = k_scan_ws<MPW, R, TV, BF16>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(2 * kThreads), p.lds_scan, s, q);
+  } else {
+    auto kern = k_scan<MPW, R, TV, BF16, KEEP>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_scan, s, q);
+  }
   return hipGetLastError();
 }
 
