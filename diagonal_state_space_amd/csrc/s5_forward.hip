@@ -15,11 +15,10 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   const int MPW = Ppad / 64, KS = Hpad / 32, K2 = Ppad / 16, NP = bf16_io ? 1 : 2;
   const size_t lds_max = 160 * 1024;
   // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
-  // 16 MPW NP fragments of 16 bytes per lane. Pass 1 (one wave per SIMD) keeps
-  // them up to MPW NP = 4 (two mode tiles per wave with the time-varying
-  // step's registers); pass 2 (two waves per SIMD, 256 registers each) up to
-  // MPW NP = 4, or 2 with the time-varying step
-  bool keep = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
+  // 16 MPW NP fragments of 16 bytes per lane. Pass 1 (eight waves, each with
+  // half the mode tiles) keeps them up to MPW NP = 4; pass 2 (two waves per
+  // SIMD, 256 registers each) up to MPW NP = 4, or 2 with the time-varying step
+  bool keep = KS <= 4 && MPW * NP <= 4;
   bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW * NP > 2);
   // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
   if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
@@ -39,9 +38,14 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
     const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
                       (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
+    // eight-wave pass 1: two u tiles and the mode table
+    const size_t lrw = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
+                       fused::mode_table_bytes(Ppad, Hpad, time_varying, false);
+    if (k && lrw > lds_max) continue;
     p.R = R;
     p.keep = k;
     p.keep_scan = ks;
+    p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;
     p.lds_scan = ls;
     break;

@@ -70,9 +70,9 @@ struct FusedParams {
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.
 struct FusedPlan {
   int R = 0, nck = 0, Lseg = 0, Q = 0;
-  bool keep = false;        // pass 1 holds B_bar in registers
+  bool keep = false;        // pass 1 holds B_bar in registers (eight-wave kernel)
   bool keep_scan = false;   // pass 2 holds B_bar and C' in registers (wave-specialized kernel)
-  size_t lds_reduce = 0, lds_scan = 0;
+  size_t lds_reduce = 0, lds_scan = 0, lds_reduce_ws = 0;
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).

@@ -152,15 +152,16 @@ struct UStage {
 };
 
 // registers per thread for the u tile: KS R NPU blocks over 4 waves
-template <int R, bool BF16, bool KEEP>
+template <int R, bool BF16, bool KEEP, int NWV = kWaves>
 constexpr int u_stage_blocks() {
-  return ((KEEP ? kKeepKS : 16) * R * (BF16 ? 1 : 2) + kWaves - 1) / kWaves;
+  return ((KEEP ? kKeepKS : 16) * R * (BF16 ? 1 : 2) + NWV - 1) / NWV;
 }
 
-template <int R, bool BF16, int NB>
+template <int R, bool BF16, int NB, int NWV = kWaves>
 __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int i, UStage<NB>& st) {
   constexpr int NPU = BF16 ? 1 : 2;
-  const Lane ln = lane_ids();
+  Lane ln = lane_ids();
+  if constexpr (NWV != kWaves) ln.w = threadIdx.x >> 6;
   const int KS = q.Hpad >> 5;
   const int nblk = KS * R * NPU;
   const bool full = (q.H & 31) == 0 && tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int
   const size_t rowb = static_cast<size_t>(b) * q.L;
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
-    const int blk = ln.w + kWaves * e;
+    const int blk = ln.w + NWV * e;
     if (blk >= nblk) continue;
     const int half = blk % NPU;
     const int f = blk / NPU;
@@ -205,13 +206,14 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int
   }
 }
 
-template <int R, bool BF16, int NB>
+template <int R, bool BF16, int NB, int NWV = kWaves>
 __device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& st, lds_byte* ub) {
-  const Lane ln = lane_ids();
+  Lane ln = lane_ids();
+  if constexpr (NWV != kWaves) ln.w = threadIdx.x >> 6;
   const int nblk = (q.Hpad >> 5) * R * (BF16 ? 1 : 2);
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
-    const int blk = ln.w + kWaves * e;
+    const int blk = ln.w + NWV * e;
     if (blk < nblk) lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
   }
 }
@@ -504,6 +506,176 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
         At = {as.x, as.y};
       }
       cf Xt = z[jj][r];
+      row_scan(At, Xt);
+      if (ln.t == kStreams - 1) {
+        const size_t ti = static_cast<size_t>(bq) * q.Ppad + pm;
+        q.tot[ti] = make_float2(Xt.re, Xt.im);
+        q.tot_a[ti] = make_float2(At.re, At.im);
+      }
+    }
+  }
+}
+
+// ---- pass 1 with eight waves (register-resident B_bar) --------------------------------
+// Wave w (0..7) owns mode tiles j = w + 8 jj (j < 4 MPW): half the weights
+// and states of a four-wave split, so two waves fit on each SIMD and one
+// wave's scan overlaps the other's MFMAs. All waves share each u tile.
+template <int MPW, int R, bool TV, bool BF16>
+__global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int NW8 = 2 * kWaves;
+  constexpr int NT = 4 * MPW;                 // mode tiles
+  constexpr int M8 = (NT + NW8 - 1) / NW8;    // tiles per wave, at most
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
+  Lane ln = lane_ids();
+  ln.w = threadIdx.x >> 6;                      // 0..7
+  const int bq = blockIdx.x;
+  const int b = bq / q.Q;
+  const int qq = bq - b * q.Q;
+  const int KS = q.Hpad >> 5;
+  const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
+  lds_byte* lds = (lds_byte*)smem;
+  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * ut, false);
+
+  // B_bar fragments of the wave's tiles, all K-steps: [s][m][cc][pl]
+  bf16x8 bw[kKeepKS][M8][2][NP];
+  {
+    const int nb = (q.Ppad / 16) * 2 * KS * 64;
+#pragma unroll
+    for (int s = 0; s < kKeepKS; ++s)
+#pragma unroll
+      for (int m = 0; m < M8; ++m)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) {
+            const int j = ln.w + NW8 * m;
+            bw[s][m][cc][pl] = (s < KS && j < NT)
+                ? as_bf16x8(ldg16(q.bpack + pl * nb + ((j * 2 + cc) * KS + s) * 64 + ln.l))
+                : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+          }
+  }
+  cf z[M8][4];
+  cf A[TV ? M8 : 1][4];
+#pragma unroll
+  for (int m = 0; m < M8; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      z[m][r] = {0.0f, 0.0f};
+      if constexpr (TV) A[m][r] = {1.0f, 0.0f};
+    }
+
+  constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
+  UStage<NB> ust;
+  fetch_u<R, BF16, NB, NW8>(q, b, qq, 0, ust);
+  stash_u<R, BF16, NB, NW8>(q, ust, lds);
+  __syncthreads();   // mode table, u tile 0
+  if (q.nck > 1) fetch_u<R, BF16, NB, NW8>(q, b, qq, 1, ust);
+  for (int i = 0; i < q.nck; ++i) {
+    const lds_byte* ub = lds + (i & 1) * ut;
+    float4 dl[TV ? M8 : 1][TV ? R : 1];
+    if constexpr (TV) {
+#pragma unroll
+      for (int m = 0; m < M8; ++m) {
+        const int pm0 = 16 * (ln.w + NW8 * m) + 4 * ln.g;
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          const int tok = tok_of<R>(q, qq, ln.t, i, n);
+          float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (tok < q.L && pm0 < q.P) {
+            const float* dp = q.delta + range_row0(q, b, qq) * q.P +
+                              (rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.P) + pm0);
+            if ((q.P & 3) == 0) {
+              const float4 x = *reinterpret_cast<const float4*>(dp);
+              v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = pm0 + r < q.P ? dp[r] : 0.0f;
+            }
+          }
+          dl[m][n] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    f32x4 acc[M8][2][R];
+#pragma unroll
+    for (int m = 0; m < M8; ++m)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int n = 0; n < R; ++n) acc[m][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kKeepKS; ++s) {
+      bf16x8 uf[NP][R];
+      get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
+#pragma unroll
+      for (int m = 0; m < M8; ++m)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            acc[m][cc][n] = mfma(bw[s][m][cc][0], uf[0][n], acc[m][cc][n]);
+            if constexpr (NP == 2) {
+              acc[m][cc][n] = mfma(bw[s][m][cc][0], uf[1][n], acc[m][cc][n]);
+              acc[m][cc][n] = mfma(bw[s][m][cc][1], uf[0][n], acc[m][cc][n]);
+            }
+          }
+    }
+#pragma unroll
+    for (int m = 0; m < M8; ++m) {
+      const int j = ln.w + NW8 * m;
+      if (j >= NT) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pm = 16 * j + 4 * ln.g + r;
+        cf x = z[m][r];
+        if constexpr (TV) {
+          const cf lam = ld_pf2(mt.ab + pm);
+          const cf inv = ld_pf2(mt.il + pm);
+          const float hrev = mt.hr[pm];
+          cf Ar = A[m][r];
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            cf a, gn;
+            zoh_step(lam, inv, hrev, f4_at(dl[m][n], r), a, gn);
+            x = cfma(a, x, cmul(gn, {acc[m][0][n][r], acc[m][1][n][r]}));
+            Ar = cmul(a, Ar);
+          }
+          A[m][r] = Ar;
+        } else {
+          const cf ab = ld_pf2(mt.ab + pm);
+#pragma unroll
+          for (int n = 0; n < R; ++n) x = cfma(ab, x, {acc[m][0][n][r], acc[m][1][n][r]});
+        }
+        z[m][r] = x;
+      }
+    }
+    // u tile i+1 into the buffer read by drive(i-1) before the last barrier
+    if (i + 1 < q.nck) stash_u<R, BF16, NB, NW8>(q, ust, lds + ((i + 1) & 1) * ut);
+    __syncthreads();
+    if (i + 2 < q.nck) fetch_u<R, BF16, NB, NW8>(q, b, qq, i + 2, ust);
+  }
+
+  // stream aggregates, then the range total over the 16 streams
+#pragma unroll
+  for (int m = 0; m < M8; ++m) {
+    const int j = ln.w + NW8 * m;
+    if (j >= NT) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * j + 4 * ln.g + r;
+      const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
+      q.sagg[si] = make_float2(z[m][r].re, z[m][r].im);
+      cf At;
+      if constexpr (TV) {
+        q.sagg_a[si] = make_float2(A[m][r].re, A[m][r].im);
+        At = A[m][r];
+      } else {
+        const float2 as = q.modes[pm].aseg;
+        At = {as.x, as.y};
+      }
+      cf Xt = z[m][r];
       row_scan(At, Xt);
       if (ln.t == kStreams - 1) {
         const size_t ti = static_cast<size_t>(bq) * q.Ppad + pm;
@@ -1238,11 +1410,19 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
 
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
-  auto kern = k_reduce<MPW, R, TV, BF16, KEEP>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_reduce, s, q);
+  if constexpr (KEEP) {
+    auto kern = k_reduce_ws<MPW, R, TV, BF16>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(2 * kThreads), p.lds_reduce_ws, s, q);
+  } else {
+    auto kern = k_reduce<MPW, R, TV, BF16, KEEP>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_reduce, s, q);
+  }
   return hipGetLastError();
 }
 
