@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,8 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 METRIC = "S5 layer fwd tokens/s (B·L/s) at L=16384,H=128,P=256; % HBM roofline"
+CSRC = os.path.join(ROOT, "diagonal_state_space_amd", "csrc")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_scan_traffic.json")
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0}   # fp32 io runs bf16x3 products
 CONFIG_INDEX = 3
@@ -68,6 +71,46 @@ class HipEvents:
 
     def destroy(self, e: int) -> None:
         self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP/C++ sources of the library (sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per k_scan launch from the committed counter record, if it was
+    taken on this workload with the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
+def calibrate_copy(mib: int, reps: int) -> int:
+    """Plain device-to-device copies of a known size (for scaling the HBM byte
+    counters): reads and writes mib MiB per copy."""
+    import torch
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
+    return 0
 
 
 def algorithmic_bytes(w) -> int:
@@ -120,9 +163,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=CONFIG_INDEX)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-repeats", type=int, default=3)
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--cpu-repeats", type=int, default=40)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, 5)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the S5 forward path here runs on a single "
@@ -206,6 +253,9 @@ def main() -> int:
         a_gbs = nbytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    workload = (f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
+                f"{'_timevarying' if w.time_varying else ''}")
+    roof["traffic"] = measured_traffic(workload)
     roof["kernel"] = "k_scan"
     roof["kernel_us"] = round(k_ms * 1e3, 2)
     roof["per_launch"] = {"flops": flops, "bytes": nbytes}
@@ -231,8 +281,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.io,
         "data": "synthetic",
-        "config": {"workload": f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
-                               f"{'_timevarying' if w.time_varying else ''}",
+        "config": {"workload": workload,
                    "B": w.B, "L": w.L, "H": w.H, "P": w.P, "io": w.io,
                    "time_varying": w.time_varying, "buffer_sets": n_sets},
         "roofline": roof,
