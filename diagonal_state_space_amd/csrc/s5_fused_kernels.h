@@ -29,6 +29,8 @@
 // term reads them too) and x tiles (two buffers).
 #pragma once
 
+#include <type_traits>
+
 #include "s5_common.h"
 #include "s5_fused.h"
 
@@ -45,6 +47,15 @@ constexpr int kKeepHT = 2;     // readout h-tiles per wave held in registers (H 
 // vmcnt) for the asynchronous global->LDS copies in flight.
 #define S5_LDS __attribute__((address_space(3)))
 typedef S5_LDS unsigned char lds_byte;
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS accesses only
+// (LDS-scoped fences), so global loads in flight (the next u tile) and stores
+// (y) are not waited for. Waves here exchange data only through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 struct pf2 {   // plain float pair, accessed member by member in LDS
   float x, y;
@@ -113,7 +124,7 @@ struct Lane {
 __device__ __forceinline__ Lane lane_ids() {
   Lane x;
   x.tid = threadIdx.x & (kThreads - 1);
-  x.w = x.tid >> 6;
+  x.w = __builtin_amdgcn_readfirstlane(x.tid >> 6);   // wave-uniform: scalar branches
   x.l = x.tid & 63;
   x.t = x.l & 15;
   x.g = x.l >> 4;
@@ -146,30 +157,53 @@ __device__ __forceinline__ uint32_t rel_row(const FusedParams& q, int t, int i, 
 // stash_u writes them to LDS before the barrier that publishes the tile.
 // (Copies straight from global memory to LDS were measured slower here: every
 // LDS access after one waits for it.)
+//
+// The loads are buffer loads through a descriptor that spans the rows of the
+// workgroup range: an element past the sequence end, past H, or of a chunk
+// that does not exist gets an offset beyond the descriptor's size, and the
+// hardware returns zeros for it. No branch and no select depends on the data
+// being there, so the compiler has no reason to wait for a load before its
+// value is stored to LDS.
 template <int NB>
 struct UStage {
   uint4 v[NB];
 };
 
-// registers per thread for the u tile: KS R NPU blocks over 4 waves
+// registers per thread for the u tile: KS R NPU blocks over NWV waves
 template <int R, bool BF16, bool KEEP, int NWV = kWaves>
 constexpr int u_stage_blocks() {
   return ((KEEP ? kKeepKS : 16) * R * (BF16 ? 1 : 2) + NWV - 1) / NWV;
 }
 
-template <int R, bool BF16, int NB, int NWV = kWaves>
-__device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int i, UStage<NB>& st) {
+// Whether every lane block of u is one whole 16-byte vector of a row (H a
+// multiple of 8 bf16 / 4 floats): then a block is one 16-byte load, else one
+// load per element. Kernels instantiate their chunk loops for both cases.
+__host__ __device__ inline bool u_rows_vectorized(int H, bool bf16) { return bf16 ? (H % 8 == 0) : (H % 4 == 0); }
+
+constexpr int kBufferOOB = static_cast<int>(0x80000000u);   // beyond any descriptor size here
+constexpr int kBufferWord3 = 0x00020000;                     // raw buffer, 32-bit data format
+
+// descriptor over the u rows of workgroup range (b, qq) (below 1 GiB, host-checked)
+template <bool BF16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t u_range_rsrc(const FusedParams& q, int b, int qq) {
+  constexpr int esz = BF16 ? 2 : 4;
+  const int tok0 = qq * kStreams * q.Lseg;
+  const int rows = min(q.L - tok0, kStreams * q.Lseg);
+  const char* base = static_cast<const char*>(q.u) + range_row0(q, b, qq) * q.H * esz;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * q.H * esz, kBufferWord3);
+}
+
+template <int R, bool BF16, int NB, int NWV, bool VEC>
+__device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rsrc_t rsrc, int qq, int i, UStage<NB>& st) {
   constexpr int NPU = BF16 ? 1 : 2;
+  constexpr int esz = BF16 ? 2 : 4;
   Lane ln = lane_ids();
-  if constexpr (NWV != kWaves) ln.w = threadIdx.x >> 6;
-  const int KS = q.Hpad >> 5;
-  const int nblk = KS * R * NPU;
-  const bool full = (q.H & 31) == 0 && tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L;
-  const size_t row0 = range_row0(q, b, qq);
-  const size_t rowb = static_cast<size_t>(b) * q.L;
+  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = (q.Hpad >> 5) * R * NPU;
+  const bool live = i < q.nck;   // chunk i exists (callers fetch unconditionally)
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
-    const int blk = ln.w + NWV * e;
+    const int blk = ln.w + NWV * e;   // wave-uniform
     if (blk >= nblk) continue;
     const int half = blk % NPU;
     const int f = blk / NPU;
@@ -177,44 +211,46 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, int b, int qq, int
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    if (full) {
-      const uint32_t o = rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0;
-      st.v[e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.u) + row0 * q.H + o)
-                     : *reinterpret_cast<const uint4*>(static_cast<const float*>(q.u) + row0 * q.H + o);
+    const bool row_ok = live && tok < q.L;
+    const int roff = static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H;
+    if constexpr (VEC) {
+      const int off = row_ok && h0 < q.H ? (roff + h0) * esz : kBufferOOB;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      st.v[e] = make_uint4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (BF16) {
+      uint32_t v4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int h = h0 + 2 * m;
+        const int olo = row_ok && h < q.H ? (roff + h) * esz : kBufferOOB;
+        const int ohi = row_ok && h + 1 < q.H ? (roff + h + 1) * esz : kBufferOOB;
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rsrc, olo, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rsrc, ohi, 0, 0);
+        v4[m] = lo | (hi << 16);
+      }
+      st.v[e] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
     } else {
-      const size_t off = (rowb + tok) * q.H;
-      // ragged chunk (tokens past L or H not a multiple of 32): zero fill
-      uint32_t v4[4] = {0u, 0u, 0u, 0u};
-      if (tok < q.L) {
-        if constexpr (BF16) {
-          const uint16_t* up = static_cast<const uint16_t*>(q.u) + off;
+      uint32_t v4[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int h = h0 + 2 * m;
-            const uint32_t lo = h < q.H ? up[h] : 0u;
-            const uint32_t hi = h + 1 < q.H ? up[h + 1] : 0u;
-            v4[m] = lo | (hi << 16);
-          }
-        } else {
-          const float* up = static_cast<const float*>(q.u) + off;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) v4[m] = h0 + m < q.H ? __float_as_uint(up[h0 + m]) : 0u;
-        }
+      for (int m = 0; m < 4; ++m) {
+        const int o = row_ok && h0 + m < q.H ? (roff + h0 + m) * esz : kBufferOOB;
+        v4[m] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, o, 0, 0);
       }
       st.v[e] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
     }
   }
 }
 
-template <int R, bool BF16, int NB, int NWV = kWaves>
+template <int R, bool BF16, int NB, int NWV>
 __device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& st, lds_byte* ub) {
   Lane ln = lane_ids();
-  if constexpr (NWV != kWaves) ln.w = threadIdx.x >> 6;
+  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = (q.Hpad >> 5) * R * (BF16 ? 1 : 2);
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
     const int blk = ln.w + NWV * e;
-    if (blk < nblk) lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
+    if (blk >= nblk) continue;
+    lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
   }
 }
 
@@ -435,13 +471,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  UStage<NB> ust;
+  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  auto chunks = [&](auto vec_c) {
+  constexpr bool VEC = decltype(vec_c)::value;
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
-  fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
-  stash_u<R, BF16, NB>(q, ust, lds);
-  __syncthreads();
-  if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
+  {
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds);
+  }
+  lds_barrier();
   for (int i = 0; i < q.nck; ++i) {
     // Delta of the next chunk is loaded before the next u tile is, so that
     // waiting for it (in-order vmcnt) never waits for the u loads
@@ -449,6 +489,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     if constexpr (TV) {
       if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dn);
     }
+    // u tile i+1 into registers now, into LDS before the barrier
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 1, ust);
     f32x4 acc[MPW][2][R];
     drive<MPW, R, BF16, KEEP>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
 #pragma unroll
@@ -478,15 +521,21 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
       }
     }
     // u tile i+1 into the buffer that drive(i-1) read before the last barrier
-    if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ((i + 1) & 1) * ut);
-    __syncthreads();
-    if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
+    __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after this chunk's work
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds + ((i + 1) & 1) * ut);
+    lds_barrier();
     if constexpr (TV) {
 #pragma unroll
       for (int jj = 0; jj < MPW; ++jj)
 #pragma unroll
         for (int n = 0; n < R; ++n) dl[jj][n] = dn[jj][n];
     }
+  }
+  };
+  if (u_rows_vectorized(q.H, BF16)) {
+    chunks(std::true_type{});
+  } else {
+    chunks(std::false_type{});
   }
 
   // stream aggregates, then the range total over the 16 streams
@@ -567,13 +616,21 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
-  UStage<NB> ust;
-  fetch_u<R, BF16, NB, NW8>(q, b, qq, 0, ust);
-  stash_u<R, BF16, NB, NW8>(q, ust, lds);
-  __syncthreads();   // mode table, u tile 0
-  if (q.nck > 1) fetch_u<R, BF16, NB, NW8>(q, b, qq, 1, ust);
+  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  auto chunks = [&](auto vec_c) {
+  constexpr bool VEC = decltype(vec_c)::value;
+  {
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, 0, ust);
+    stash_u<R, BF16, NB, NW8>(q, ust, lds);
+  }
+  lds_barrier();   // mode table, u tile 0
   for (int i = 0; i < q.nck; ++i) {
     const lds_byte* ub = lds + (i & 1) * ut;
+    // u tile i+1 into registers now, into LDS after this chunk's MFMAs and
+    // scan (not carried across iterations: no register shuffles, no early wait)
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, i + 1, ust);
     float4 dl[TV ? M8 : 1][TV ? R : 1];
     if constexpr (TV) {
 #pragma unroll
@@ -652,9 +709,15 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       }
     }
     // u tile i+1 into the buffer read by drive(i-1) before the last barrier
-    if (i + 1 < q.nck) stash_u<R, BF16, NB, NW8>(q, ust, lds + ((i + 1) & 1) * ut);
-    __syncthreads();
-    if (i + 2 < q.nck) fetch_u<R, BF16, NB, NW8>(q, b, qq, i + 2, ust);
+    __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after this chunk's work
+    stash_u<R, BF16, NB, NW8>(q, ust, lds + ((i + 1) & 1) * ut);
+    lds_barrier();
+  }
+  };
+  if (u_rows_vectorized(q.H, BF16)) {
+    chunks(std::true_type{});
+  } else {
+    chunks(std::false_type{});
   }
 
   // stream aggregates, then the range total over the 16 streams
@@ -914,27 +977,29 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
 // y of chunk i from the register-weight readout's accumulators: feedthrough
 // from u tile i in LDS and D from the LDS table
 template <int R, bool BF16>
-__device__ __forceinline__ void readout_store(const FusedParams& q, const S5_LDS float* s_d,
+__device__ __forceinline__ void readout_store(const FusedParams& q, const float4 (&dk)[kKeepHT],
                                               const f32x4 (&yacc)[kKeepHT][R], const lds_byte* ub, int HT,
                                               int HTv, int b, int qq, int i, const Lane& ln) {
   (void)HT;
   const bool full = tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L && (q.H & 15) == 0;
   if (full) {
     const size_t base = range_row0(q, b, qq) * q.H;   // uniform
+    float uv[kKeepHT][R][4];
+#pragma unroll
+    for (int e = 0; e < kKeepHT; ++e)
+#pragma unroll
+      for (int n = 0; n < R; ++n) u_for_y<R, BF16>(ub, ln.w + kWaves * e, n, ln, uv[e][n]);
 #pragma unroll
     for (int e = 0; e < kKeepHT; ++e) {
       const int ht = ln.w + kWaves * e;
       if (ht >= HTv) continue;
       const int h0 = 16 * ht + 4 * ln.g;
-      const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + h0));
 #pragma unroll
       for (int n = 0; n < R; ++n) {
-        float uv[4];
-        u_for_y<R, BF16>(ub, ht, n, ln, uv);
         const uint32_t o = rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0;
         store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + base + o)
                                 : static_cast<void*>(static_cast<float*>(q.y) + base + o),
-                           yacc[e][n], d4, uv);
+                           yacc[e][n], dk[e], uv[e][n]);
       }
     }
   } else {
@@ -942,7 +1007,7 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, const S5_LDS
     for (int e = 0; e < kKeepHT; ++e) {
       const int ht = ln.w + kWaves * e;
       if (ht >= HTv) continue;
-      const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + 16 * ht + 4 * ln.g));
+      const float4 d4 = dk[e];
       const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int n = 0; n < R; ++n) {
@@ -1021,7 +1086,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
     }
     st_pf2(s_c0 + ln.tid, c.re, c.im);
   }
-  __syncthreads();
+  lds_barrier();
 
   cf abar[KEEP ? 1 : MPW][4];   // register copy when the table is not in LDS
   cf st[MPW][4];
@@ -1051,13 +1116,19 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 
   // ---- chunk pipeline ----
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  UStage<NB> ust;
-  fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
-  stash_u<R, BF16, NB>(q, ust, lds);
-  __syncthreads();
+  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  auto chunks = [&](auto vec_c) {
+  constexpr bool VEC = decltype(vec_c)::value;
+  {
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 1, ust);
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds + ut);
+  }
+  lds_barrier();
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
-  if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
   f32x4 acc[MPW][2][R];
   drive<MPW, R, BF16, KEEP>(q, bk, lds, ln.w, ln.l, acc);
 
@@ -1131,20 +1202,32 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       lds_byte* xb = xlds + (i & 1) * xt;
 #pragma unroll
       for (int jj = 0; jj < MPW; ++jj) write_x(jj, xb);
-      // u tile i+1 into the buffer that held tile i-2 (its last reader, the
-      // feedthrough of readout(i-2), finished before the previous barrier)
-      if (i + 1 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui1 * ut);
-      __syncthreads();   // x tile i and u tile i+1 complete
+      lds_barrier();   // x tile i and u tile i+1 complete
       // Delta of chunk i+1 is loaded before u tile i+2, so that waiting for it
       // (in-order vmcnt) never waits for the u loads
       if constexpr (TV) {
         if (i + 1 < q.nck) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
       }
-      if (i + 2 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 2, ust);
+      // u tile i+2 into registers now, into LDS after the drive: into the
+      // buffer of tile i-1, whose last readers (drive(i-1), readout(i-1))
+      // finished before the previous barrier
+      UStage<NB> ust;
+      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 2, ust);
       drive<MPW, R, BF16, KEEP>(q, bk, lds + ui1 * ut, ln.w, ln.l, acc);
+      // (before the readout's y stores, so that waiting for the loads does
+      // not wait for them)
+      const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
+      __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the drive
+      stash_u<R, BF16, NB, kWaves>(q, ust, lds + ui2 * ut);
       readout<MPW, R, BF16, KEEP>(q, ck, mt.d, xb, lds + ui * ut, b, qq, i, ln);
       ui = ui1;
     }
+  }
+  };
+  if (u_rows_vectorized(q.H, BF16)) {
+    chunks(std::true_type{});
+  } else {
+    chunks(std::false_type{});
   }
 }
 
@@ -1212,10 +1295,13 @@ __device__ __forceinline__ void stream_start(const FusedParams& q, int bq, const
 
 // Drive, scan and x tile of the wave's mode tiles j0 .. j0 + JG - 1 (those
 // below MPW) for one chunk: the accumulators of JG tiles only are live.
-template <int MPW, int JG, int R, bool TV, bool BF16>
+// UA: the u fragments of all K-steps come in `ua` (bf16 I/O); otherwise each
+// K-step's fragments are read from the u tile `ub` right before its MFMAs.
+template <int MPW, int JG, int R, bool TV, bool BF16, bool UA>
 __device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk,
-                                                 const lds_byte* ub, const ModeTable& mt, const Lane& ln,
-                                                 const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
+                                                 const bf16x8 (&ua)[UA ? kKeepKS : 1][BF16 ? 1 : 2][R],
+                                                 const lds_byte* ub, const ModeTable& mt,
+                                                 const Lane& ln, const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
                                                  cf (&st)[MPW][4], lds_byte* xb) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
@@ -1228,8 +1314,15 @@ __device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW
       for (int n = 0; n < R; ++n) acc[jj][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < kKeepKS; ++s) {
-    bf16x8 uf[NP][R];
-    get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
+    bf16x8 uk[NP][R];
+    if constexpr (UA) {
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+        for (int n = 0; n < R; ++n) uk[pl][n] = ua[s][pl][n];
+    } else {
+      get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, uk);
+    }
 #pragma unroll
     for (int jj = 0; jj < JG; ++jj) {
       if (j0 + jj >= MPW) continue;
@@ -1237,10 +1330,10 @@ __device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int n = 0; n < R; ++n) {
-          acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uf[0][n], acc[jj][cc][n]);
+          acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uk[0][n], acc[jj][cc][n]);
           if constexpr (NP == 2) {
-            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uf[1][n], acc[jj][cc][n]);
-            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][1], uf[0][n], acc[jj][cc][n]);
+            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][0], uk[1][n], acc[jj][cc][n]);
+            acc[jj][cc][n] = mfma(bk.f[s][j0 + jj][cc][1], uk[0][n], acc[jj][cc][n]);
           }
         }
     }
@@ -1300,8 +1393,17 @@ __device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ?
                                                  const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
                                                  cf (&st)[MPW][4], lds_byte* xb) {
   constexpr int JG = MPW >= 4 ? 1 : (MPW < 2 ? MPW : 2);
+  // the chunk's u fragments (K-steps past KS repeat the last real one against
+  // zero weights): read from LDS once for all tile groups where registers
+  // allow, else again for each group
+  constexpr bool kOnce = BF16 && MPW < 4;
+  bf16x8 ua[kOnce ? kKeepKS : 1][BF16 ? 1 : 2][R];
+  if constexpr (kOnce) {
 #pragma unroll
-  for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16>(j0, KS, bk, ub, mt, ln, dl, st, xb);
+    for (int s = 0; s < kKeepKS; ++s) get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, ua[s]);
+  }
+#pragma unroll
+  for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16, kOnce>(j0, KS, bk, ua, ub, mt, ln, dl, st, xb);
 }
 
 template <int MPW, int R, bool TV, bool BF16>
@@ -1330,7 +1432,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   if (driver && ln.tid < q.Ppad) range_carry(q, b, qq, ln.tid, s_c0);
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
-  UStage<NB> ust;
+  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
   // one register array holds the role's weights: B_bar fragments [s][jj][cc][pl]
   // in drive waves, C' fragments [e][s][pl] in readout waves (16 MPW NP each)
   static_assert(sizeof(BKeep<MPW, NP>) == sizeof(CKeep<MPW, NP>), "both roles hold 16 MPW NP fragments");
@@ -1356,21 +1458,30 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
         }
       }
     }
-    fetch_u<R, BF16, NB>(q, b, qq, 0, ust);
-    stash_u<R, BF16, NB>(q, ust, lds);
-    if (q.nck > 1) fetch_u<R, BF16, NB>(q, b, qq, 1, ust);
   }
-  __syncthreads();   // carry, mode table, u tile 0
+  auto chunks = [&](auto vec_c) {
+  constexpr bool VEC = decltype(vec_c)::value;
+  if (!driver) {
+    UStage<NB> ust;
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 1, ust);
+    stash_u<R, BF16, NB, kWaves>(q, ust, lds + ut);
+  }
+  lds_barrier();   // carry, mode table, u tiles 0 and 1
+  float4 dk[kKeepHT];   // D of the readout wave's h-tiles: features 16 ht + 4 g + 0..3
+#pragma unroll
+  for (int e = 0; e < kKeepHT; ++e) {
+    const int h0 = 16 * (ln.w + kWaves * e) + 4 * ln.g;
+    dk[e] = h0 < q.Hpad ? lds_ld<float4>(reinterpret_cast<const lds_byte*>(mt.d + h0)) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if (driver) {
     stream_start<MPW, TV>(q, bq, ln, s_c0, st);
     if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
     drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds, mt, ln, dl, st, xlds);
-  } else {
-    if (q.nck > 1) stash_u<R, BF16, NB>(q, ust, lds + ut);
-    if (q.nck > 2) fetch_u<R, BF16, NB>(q, b, qq, 2, ust);
   }
-  __syncthreads();   // x tile 0, u tile 1
+  lds_barrier();   // x tile 0
 
   int ui = 0;   // i % 3
   for (int i = 0; i < q.nck; ++i) {
@@ -1382,27 +1493,42 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
         drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds + ui1 * ut, mt, ln, dl, st, xlds + ((i + 1) & 1) * xt);
       }
     } else {
+      // u tile i+2 into registers now, into LDS after this chunk's readout
+      // (not carried across iterations: no register shuffles, no early wait)
+      UStage<NB> ust2;
+      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 2, ust2);
       const lds_byte* xr = xlds + (i & 1) * xt;
       f32x4 yacc[kKeepHT][R];
 #pragma unroll
       for (int e = 0; e < kKeepHT; ++e)
 #pragma unroll
         for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      // x fragments read kAhead K-steps ahead of their MFMAs
+      constexpr int kAhead = NP == 2 ? 1 : 3;
+      bf16x8 xf[K2][NP][R];
+#pragma unroll
+      for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
 #pragma unroll
       for (int s = 0; s < K2; ++s) {
-        bf16x8 xf[NP][R];
-        get_x<R, NP>(xr, K2, s, ln.l, xf);
+        if (s + kAhead < K2) get_x<R, NP>(xr, K2, s + kAhead, ln.l, xf[s + kAhead]);
 #pragma unroll
-        for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(wts.c.f[e][s], xf, yacc[e]);
+        for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(wts.c.f[e][s], xf[s], yacc[e]);
       }
-      readout_store<R, BF16>(q, mt.d, yacc, lds + ui * ut, HT, HTv, b, qq, i, ln);
       // u tile i+2 into the buffer of tile i-1 (read by drive(i-1) and
-      // readout(i-1), both before the previous barrier)
-      if (i + 2 < q.nck) stash_u<R, BF16, NB>(q, ust, lds + ui2 * ut);
-      if (i + 3 < q.nck) fetch_u<R, BF16, NB>(q, b, qq, i + 3, ust);
+      // readout(i-1), both before the previous barrier); before this chunk's
+      // y stores, so that waiting for the loads does not wait for them
+      __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
+      stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
+      readout_store<R, BF16>(q, dk, yacc, lds + ui * ut, HT, HTv, b, qq, i, ln);
     }
-    __syncthreads();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
+    lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
     ui = ui1;
+  }
+  };
+  if (u_rows_vectorized(q.H, BF16)) {
+    chunks(std::true_type{});
+  } else {
+    chunks(std::false_type{});
   }
 }
 
