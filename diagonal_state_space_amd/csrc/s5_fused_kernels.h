@@ -183,13 +183,14 @@ __host__ __device__ inline bool u_rows_vectorized(int H, bool bf16) { return bf1
 constexpr int kBufferOOB = static_cast<int>(0x80000000u);   // beyond any descriptor size here
 constexpr int kBufferWord3 = 0x00020000;                     // raw buffer, 32-bit data format
 
-// descriptor over the u rows of workgroup range (b, qq) (below 1 GiB, host-checked)
+// descriptor over the rows (of H elements) of workgroup range (b, qq) of u or
+// y: rows past the sequence end are outside it (below 1 GiB, host-checked)
 template <bool BF16>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t u_range_rsrc(const FusedParams& q, int b, int qq) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, const FusedParams& q, int b, int qq) {
   constexpr int esz = BF16 ? 2 : 4;
   const int tok0 = qq * kStreams * q.Lseg;
   const int rows = min(q.L - tok0, kStreams * q.Lseg);
-  const char* base = static_cast<const char*>(q.u) + range_row0(q, b, qq) * q.H * esz;
+  const char* base = static_cast<const char*>(t) + range_row0(q, b, qq) * q.H * esz;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * q.H * esz, kBufferWord3);
 }
 
@@ -471,7 +472,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   float4 dl[TV ? MPW : 1][TV ? R : 1];
@@ -616,7 +617,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
-  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   {
@@ -775,37 +776,37 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
   }
 }
 
-// y = acc + D u for 4 consecutive features y[tok][h0..h0+3], tok < L and
-// h0 + 4 <= H known (complete chunk, H a multiple of 16): one vector store,
-// bf16 rounding by the hardware conversion (round to nearest even)
-template <bool BF16>
-__device__ __forceinline__ void store_y_full(void* yrow, const f32x4& acc, const float4& d4, const float (&uv)[4]) {
+// y = acc + D u for 4 consecutive features h0..h0+3 of one row (row offset
+// roff, in elements, inside the range descriptor yr); bf16 rounding by the
+// hardware conversion (round to nearest even). Rows past the sequence end
+// fall outside the descriptor and features >= H get an offset beyond it, so
+// the hardware drops those writes. VEC: H % 4 == 0, one vector store.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int h0, int H, const f32x4& acc,
+                                        const float4& d4, const float (&uv)[4]) {
+  constexpr int esz = BF16 ? 2 : 4;
   const f32x4 yv = {fmaf(d4.x, uv[0], acc[0]), fmaf(d4.y, uv[1], acc[1]), fmaf(d4.z, uv[2], acc[2]),
                     fmaf(d4.w, uv[3], acc[3])};
-  if constexpr (BF16) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<uint2*>(yrow) = __builtin_bit_cast(uint2, __builtin_convertvector(yv, bf16x4));
+  if constexpr (VEC) {
+    const int off = h0 < H ? (roff + h0) * esz : kBufferOOB;
+    if constexpr (BF16) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(yv, bf16x4)), yr, off,
+                                            0, 0);
+    } else {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yv), yr, off, 0, 0);
+    }
   } else {
-    *reinterpret_cast<float4*>(yrow) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-  }
-}
-
-// the same for a ragged chunk: per-lane bounds on the token and the features
-template <bool BF16>
-__device__ __forceinline__ void store_y(const FusedParams& q, int b, int tok, int h0, const f32x4& acc,
-                                        const float (&dv)[4], const float (&uv)[4]) {
-  float yv[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) yv[r] = fmaf(dv[r], uv[r], acc[r]);
-  if (tok >= q.L || h0 >= q.H) return;
-  const size_t row = (static_cast<size_t>(b) * q.L + tok) * q.H;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (h0 + r < q.H) {
+    for (int m = 0; m < 4; ++m) {
+      const int off = h0 + m < H ? (roff + h0 + m) * esz : kBufferOOB;
       if constexpr (BF16) {
-        static_cast<uint16_t*>(q.y)[row + h0 + r] = f32_to_bf16(yv[r]);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(yv[m])), yr, off,
+                                              0, 0);
       } else {
-        static_cast<float*>(q.y)[row + h0 + r] = yv[r];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[m]), yr, off, 0, 0);
       }
     }
   }
@@ -847,15 +848,13 @@ __device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s,
 }
 
 // y for chunk i of the workgroup's streams from the x tile and u tile in LDS
-template <int MPW, int R, bool BF16, bool KEEP>
-__device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, BF16 ? 1 : 2>& ck,
-                                        const S5_LDS float* s_d, const lds_byte* xb,
-                                        const lds_byte* ub, int b, int qq, int i, const Lane& ln) {
+template <int MPW, int R, bool BF16, bool KEEP, bool VEC>
+__device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rsrc_t yr,
+                                        const CKeep<MPW, BF16 ? 1 : 2>& ck, const S5_LDS float* s_d,
+                                        const lds_byte* xb, const lds_byte* ub, int i, const Lane& ln) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   const int HT = q.Hpad >> 4;
-  // complete chunk with whole 16-feature tiles: no per-lane bounds in the stores
-  const bool full = tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L && (q.H & 15) == 0;
   const int HTv = (q.H + 15) >> 4;   // h-tiles holding a feature < H
   if constexpr (KEEP) {
     f32x4 yacc[kKeepHT][R];
@@ -871,38 +870,17 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
 #pragma unroll
       for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(ck.f[e][s], xf, yacc[e]);
     }
-    if (full) {
-      // lane's token rows of this chunk: tok(t, i, n) = tok(t, i, 0) + n
-      const size_t row0 = (static_cast<size_t>(b) * q.L + tok_of<R>(q, qq, ln.t, i, 0)) * q.H;
 #pragma unroll
-      for (int e = 0; e < kKeepHT; ++e) {
-        const int ht = ln.w + kWaves * e;
-        if (ht >= HTv) continue;
-        const int h0 = 16 * ht + 4 * ln.g;
-        const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + h0));
+    for (int e = 0; e < kKeepHT; ++e) {
+      const int ht = ln.w + kWaves * e;
+      if (ht >= HTv) continue;   // wave-uniform
+      const int h0 = 16 * ht + 4 * ln.g;
+      const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + h0));
 #pragma unroll
-        for (int n = 0; n < R; ++n) {
-          float uv[4];
-          u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          const size_t off = row0 + static_cast<size_t>(n) * q.H + h0;
-          store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + off)
-                                  : static_cast<void*>(static_cast<float*>(q.y) + off),
-                             yacc[e][n], d4, uv);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kKeepHT; ++e) {
-        const int ht = ln.w + kWaves * e;
-        if (ht >= HTv) continue;
-        const float4 d4 = lds_ld<float4>(reinterpret_cast<const lds_byte*>(s_d + 16 * ht + 4 * ln.g));
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int n = 0; n < R; ++n) {
-          float uv[4];
-          u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dv, uv);
-        }
+      for (int n = 0; n < R; ++n) {
+        float uv[4];
+        u_for_y<R, BF16>(ub, ht, n, ln, uv);
+        store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], d4, uv);
       }
     }
   } else {
@@ -959,15 +937,8 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
         for (int n = 0; n < R; ++n) {
           float uv[4];
           u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          const int tok = tok_of<R>(q, qq, ln.t, i, n);
-          if (full) {
-            const size_t off = range_row0(q, b, qq) * q.H + (rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0);
-            store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + off)
-                                    : static_cast<void*>(static_cast<float*>(q.y) + off),
-                               yacc[e][n], make_float4(dv[0], dv[1], dv[2], dv[3]), uv);
-          } else {
-            store_y<BF16>(q, b, tok, h0, yacc[e][n], dv, uv);
-          }
+          store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n],
+                             make_float4(dv[0], dv[1], dv[2], dv[3]), uv);
         }
       }
     }
@@ -975,47 +946,24 @@ __device__ __forceinline__ void readout(const FusedParams& q, const CKeep<MPW, B
 }
 
 // y of chunk i from the register-weight readout's accumulators: feedthrough
-// from u tile i in LDS and D from the LDS table
-template <int R, bool BF16>
-__device__ __forceinline__ void readout_store(const FusedParams& q, const float4 (&dk)[kKeepHT],
-                                              const f32x4 (&yacc)[kKeepHT][R], const lds_byte* ub, int HT,
-                                              int HTv, int b, int qq, int i, const Lane& ln) {
-  (void)HT;
-  const bool full = tok_of<R>(q, qq, kStreams - 1, i, R - 1) < q.L && (q.H & 15) == 0;
-  if (full) {
-    const size_t base = range_row0(q, b, qq) * q.H;   // uniform
-    float uv[kKeepHT][R][4];
+// from u tile i in LDS and D from the LDS table (h-tiles past H: the stores
+// fall outside the descriptor and are dropped)
+template <int R, bool BF16, bool VEC>
+__device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buffer_rsrc_t yr,
+                                              const float4 (&dk)[kKeepHT], const f32x4 (&yacc)[kKeepHT][R],
+                                              const lds_byte* ub, int i, const Lane& ln) {
+  float uv[kKeepHT][R][4];
 #pragma unroll
-    for (int e = 0; e < kKeepHT; ++e)
+  for (int e = 0; e < kKeepHT; ++e)
 #pragma unroll
-      for (int n = 0; n < R; ++n) u_for_y<R, BF16>(ub, ln.w + kWaves * e, n, ln, uv[e][n]);
+    for (int n = 0; n < R; ++n) u_for_y<R, BF16>(ub, ln.w + kWaves * e, n, ln, uv[e][n]);
 #pragma unroll
-    for (int e = 0; e < kKeepHT; ++e) {
-      const int ht = ln.w + kWaves * e;
-      if (ht >= HTv) continue;
-      const int h0 = 16 * ht + 4 * ln.g;
+  for (int e = 0; e < kKeepHT; ++e) {
+    const int h0 = 16 * (ln.w + kWaves * e) + 4 * ln.g;
 #pragma unroll
-      for (int n = 0; n < R; ++n) {
-        const uint32_t o = rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.H) + h0;
-        store_y_full<BF16>(BF16 ? static_cast<void*>(static_cast<uint16_t*>(q.y) + base + o)
-                                : static_cast<void*>(static_cast<float*>(q.y) + base + o),
-                           yacc[e][n], dk[e], uv[e][n]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kKeepHT; ++e) {
-      const int ht = ln.w + kWaves * e;
-      if (ht >= HTv) continue;
-      const float4 d4 = dk[e];
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int n = 0; n < R; ++n) {
-        float uv[4];
-        u_for_y<R, BF16>(ub, ht, n, ln, uv);
-        store_y<BF16>(q, b, tok_of<R>(q, qq, ln.t, i, n), 16 * ht + 4 * ln.g, yacc[e][n], dv, uv);
-      }
-    }
+    for (int n = 0; n < R; ++n)
+      store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], dk[e],
+                         uv[e][n]);
   }
 }
 
@@ -1116,7 +1064,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 
   // ---- chunk pipeline ----
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
+  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq);
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   {
@@ -1219,7 +1168,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the drive
       stash_u<R, BF16, NB, kWaves>(q, ust, lds + ui2 * ut);
-      readout<MPW, R, BF16, KEEP>(q, ck, mt.d, xb, lds + ui * ut, b, qq, i, ln);
+      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, ck, mt.d, xb, lds + ui * ut, i, ln);
       ui = ui1;
     }
   }
@@ -1396,7 +1345,7 @@ __device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ?
   // the chunk's u fragments (K-steps past KS repeat the last real one against
   // zero weights): read from LDS once for all tile groups where registers
   // allow, else again for each group
-  constexpr bool kOnce = BF16 && MPW < 4;
+  constexpr bool kOnce = BF16;
   bf16x8 ua[kOnce ? kKeepKS : 1][BF16 ? 1 : 2][R];
   if constexpr (kOnce) {
 #pragma unroll
@@ -1419,7 +1368,6 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   const int qq = bq - b * q.Q;
   const int KS = q.Hpad >> 5;
   const int HT = q.Hpad >> 4;
-  const int HTv = (q.H + 15) >> 4;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   const int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
   // u tile i in buffer i % 3 (staged by the readout waves two chunks ahead,
@@ -1432,7 +1380,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   if (driver && ln.tid < q.Ppad) range_carry(q, b, qq, ln.tid, s_c0);
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
-  const __amdgpu_buffer_rsrc_t ursrc = u_range_rsrc<BF16>(q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
+  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq);
   // one register array holds the role's weights: B_bar fragments [s][jj][cc][pl]
   // in drive waves, C' fragments [e][s][pl] in readout waves (16 MPW NP each)
   static_assert(sizeof(BKeep<MPW, NP>) == sizeof(CKeep<MPW, NP>), "both roles hold 16 MPW NP fragments");
@@ -1483,17 +1432,27 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   }
   lds_barrier();   // x tile 0
 
-  int ui = 0;   // i % 3
-  for (int i = 0; i < q.nck; ++i) {
-    const int ui1 = ui == 2 ? 0 : ui + 1;
-    const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
-    if (driver) {
+  // One loop per role (each ends an iteration at the same barrier), so that
+  // neither role's registers are live in the other's code.
+  // Iteration i: drive waves scan chunk i+1 into x tile (i+1)&1 from u tile
+  // (i+1)%3; readout waves turn x tile i&1 into y and stage u tile i+2.
+  if (driver) {
+    int ui = 0;   // i % 3
+    for (int i = 0; i < q.nck; ++i) {
+      const int ui1 = ui == 2 ? 0 : ui + 1;
       if (i + 1 < q.nck) {
         if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
         drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds + ui1 * ut, mt, ln, dl, st, xlds + ((i + 1) & 1) * xt);
       }
-    } else {
-      // u tile i+2 into registers now, into LDS after this chunk's readout
+      lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
+      ui = ui1;
+    }
+  } else {
+    int ui = 0;   // i % 3
+    for (int i = 0; i < q.nck; ++i) {
+      const int ui1 = ui == 2 ? 0 : ui + 1;
+      const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
+      // u tile i+2 into registers now, into LDS after this chunk's MFMAs
       // (not carried across iterations: no register shuffles, no early wait)
       UStage<NB> ust2;
       fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 2, ust2);
@@ -1508,21 +1467,27 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       bf16x8 xf[K2][NP][R];
 #pragma unroll
       for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
+      // the reads stay kAhead K-steps ahead of their MFMAs in the schedule
+      // (left alone, the scheduler puts each read next to its use and the
+      // MFMAs wait for LDS latency)
+      __builtin_amdgcn_sched_group_barrier(0x100, (kAhead < K2 ? kAhead : K2) * NP * R, 0);
 #pragma unroll
       for (int s = 0; s < K2; ++s) {
         if (s + kAhead < K2) get_x<R, NP>(xr, K2, s + kAhead, ln.l, xf[s + kAhead]);
 #pragma unroll
         for (int e = 0; e < kKeepHT; ++e) mfma_read<R, NP>(wts.c.f[e][s], xf[s], yacc[e]);
+        if (s + kAhead < K2) __builtin_amdgcn_sched_group_barrier(0x100, NP * R, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kKeepHT * R * (NP == 2 ? 3 : 1), 0);
       }
       // u tile i+2 into the buffer of tile i-1 (read by drive(i-1) and
       // readout(i-1), both before the previous barrier); before this chunk's
       // y stores, so that waiting for the loads does not wait for them
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
       stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
-      readout_store<R, BF16>(q, dk, yacc, lds + ui * ut, HT, HTv, b, qq, i, ln);
+      readout_store<R, BF16, VEC>(q, yrsrc, dk, yacc, lds + ui * ut, i, ln);
+      lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
+      ui = ui1;
     }
-    lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
-    ui = ui1;
   }
   };
   if (u_rows_vectorized(q.H, BF16)) {
