@@ -38,13 +38,14 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
     const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
                       (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
-    // eight-wave pass 1: two u tiles and the mode table
-    const size_t lrw = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
+    // eight-wave pass 1: two groups of u tiles and the mode table
+    const size_t lrw = 2 * fused::reduce_group(bf16_io) * fused::u_tile_bytes(KS, R, bf16_io) +
                        fused::mode_table_bytes(Ppad, Hpad, time_varying, false);
     if (k && lrw > lds_max) continue;
     p.R = R;
     p.keep = k;
     p.keep_scan = ks;
+    p.group = k ? fused::reduce_group(bf16_io) : 1;
     p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;
     p.lds_scan = ls;
@@ -57,14 +58,16 @@ void fused_split(int B, int L, int H, int P, int ncu, FusedPlan& p) {
   const int chunks = (L + per - 1) / per;          // chunks with a single range
   int Q = std::max(1, (ncu + B - 1) / B);          // ranges per sequence to fill the CUs
   Q = std::max(1, std::min(Q, chunks));
-  p.nck = (L + Q * per - 1) / (Q * per);
+  const int g = std::max(1, p.group);
+  auto chunks_for = [&](int q) { return ((L + q * per - 1) / (q * per) + g - 1) / g * g; };
+  p.nck = chunks_for(Q);
   p.Lseg = p.R * p.nck;
   p.Q = (L + kStreams * p.Lseg - 1) / (kStreams * p.Lseg);
   // a range's rows of u, y and Delta stay below 1 GiB (32-bit lane offsets)
   const int64_t row_bytes = static_cast<int64_t>(std::max(H, P)) * 4;
-  while (static_cast<int64_t>(kStreams) * p.Lseg * row_bytes >= (int64_t{1} << 30) && p.nck > 1) {
+  while (static_cast<int64_t>(kStreams) * p.Lseg * row_bytes >= (int64_t{1} << 30) && p.nck > g) {
     Q = std::min(chunks, 2 * Q);
-    p.nck = (L + Q * per - 1) / (Q * per);
+    p.nck = chunks_for(Q);
     p.Lseg = p.R * p.nck;
     p.Q = (L + kStreams * p.Lseg - 1) / (kStreams * p.Lseg);
   }

@@ -23,6 +23,9 @@ __host__ __device__ constexpr size_t x_tile_bytes(int K2, int R, bool bf16) {
 __host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool tv, bool with_d) {
   return static_cast<size_t>(Ppad) * (tv ? 20 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
 }
+// chunks between two barriers of the eight-wave pass 1 (u tiles of two such
+// groups in LDS; the chunk count is padded to a multiple of it)
+__host__ __device__ constexpr int reduce_group(bool bf16) { return bf16 ? 4 : 2; }
 }  // namespace fused
 
 // Per-mode constants written by the packing kernel.
@@ -72,6 +75,7 @@ struct FusedPlan {
   int R = 0, nck = 0, Lseg = 0, Q = 0;
   bool keep = false;        // pass 1 holds B_bar in registers (eight-wave kernel)
   bool keep_scan = false;   // pass 2 holds B_bar and C' in registers (wave-specialized kernel)
+  int group = 1;            // nck is a multiple of this (reduce_group with `keep`)
   size_t lds_reduce = 0, lds_scan = 0, lds_reduce_ws = 0;
 };
 

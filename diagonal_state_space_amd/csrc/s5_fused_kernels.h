@@ -124,7 +124,8 @@ struct Lane {
 __device__ __forceinline__ Lane lane_ids() {
   Lane x;
   x.tid = threadIdx.x & (kThreads - 1);
-  x.w = __builtin_amdgcn_readfirstlane(x.tid >> 6);   // wave-uniform: scalar branches
+  // wave-uniform (scalar branches); the mask tells the compiler its range
+  x.w = __builtin_amdgcn_readfirstlane(x.tid >> 6) & (kWaves - 1);
   x.l = x.tid & 63;
   x.t = x.l & 15;
   x.g = x.l >> 4;
@@ -199,20 +200,19 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rs
   constexpr int NPU = BF16 ? 1 : 2;
   constexpr int esz = BF16 ? 2 : 4;
   Lane ln = lane_ids();
-  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NWV - 1);
   const int nblk = (q.Hpad >> 5) * R * NPU;
   const bool live = i < q.nck;   // chunk i exists (callers fetch unconditionally)
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
-    const int blk = ln.w + NWV * e;   // wave-uniform
-    if (blk >= nblk) continue;
+    const int blk = ln.w + NWV * e;   // wave-uniform; blocks past the tile load zeros (not stored)
     const int half = blk % NPU;
     const int f = blk / NPU;
     const int n = f % R;
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    const bool row_ok = live && tok < q.L;
+    const bool row_ok = live && blk < nblk && tok < q.L;
     const int roff = static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H;
     if constexpr (VEC) {
       const int off = row_ok && h0 < q.H ? (roff + h0) * esz : kBufferOOB;
@@ -245,12 +245,19 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rs
 template <int R, bool BF16, int NB, int NWV>
 __device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& st, lds_byte* ub) {
   Lane ln = lane_ids();
-  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NWV - 1);
   const int nblk = (q.Hpad >> 5) * R * (BF16 ? 1 : 2);
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
     const int blk = ln.w + NWV * e;
-    if (blk >= nblk) continue;
+    if (blk >= nblk) {
+      // This wave loaded nothing into v[e] (fetch_u skipped the same block),
+      // but the compiler cannot tell: without this (free) wait it assumes a
+      // load may still be writing v[e] at the next fetch and waits there for
+      // every outstanding load instead.
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      continue;
+    }
     lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
   }
 }
@@ -577,16 +584,16 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NT = 4 * MPW;                 // mode tiles
   constexpr int M8 = (NT + NW8 - 1) / NW8;    // tiles per wave, at most
   extern __shared__ __align__(16) unsigned char smem[];
-  if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
+  if (q.Ppad != 64 * MPW || q.R != R || q.nck % reduce_group(BF16) != 0) return;   // dispatch mismatch
   Lane ln = lane_ids();
-  ln.w = threadIdx.x >> 6;                      // 0..7
+  ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW8 - 1);   // 0..7
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
-  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * ut, false);
+  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16) * ut, false);
 
   // B_bar fragments of the wave's tiles, all K-steps: [s][m][cc][pl]
   bf16x8 bw[kKeepKS][M8][2][NP];
@@ -617,22 +624,11 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
+  constexpr int G = reduce_group(BF16);   // chunks per barrier (nck is a multiple of G)
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
-  auto chunks = [&](auto vec_c) {
-  constexpr bool VEC = decltype(vec_c)::value;
-  {
-    UStage<NB> ust;
-    fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, 0, ust);
-    stash_u<R, BF16, NB, NW8>(q, ust, lds);
-  }
-  lds_barrier();   // mode table, u tile 0
-  for (int i = 0; i < q.nck; ++i) {
-    const lds_byte* ub = lds + (i & 1) * ut;
-    // u tile i+1 into registers now, into LDS after this chunk's MFMAs and
-    // scan (not carried across iterations: no register shuffles, no early wait)
-    UStage<NB> ust;
-    fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, i + 1, ust);
-    float4 dl[TV ? M8 : 1][TV ? R : 1];
+
+  // Delta of chunk i (time-varying)
+  auto delta = [&](int i, float4 (&dl)[TV ? M8 : 1][TV ? R : 1]) __attribute__((always_inline)) {
     if constexpr (TV) {
 #pragma unroll
       for (int m = 0; m < M8; ++m) {
@@ -656,7 +652,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         }
       }
     }
-    f32x4 acc[M8][2][R];
+  };
+  // drive (B_bar u) of one chunk from its u tile ub
+  auto mma = [&](const lds_byte* ub, f32x4 (&acc)[M8][2][R]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < M8; ++m)
 #pragma unroll
@@ -680,6 +678,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
             }
           }
     }
+  };
+  // the stream states through one chunk's drive
+  auto scan = [&](const f32x4 (&acc)[M8][2][R], const float4 (&dl)[TV ? M8 : 1][TV ? R : 1])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < M8; ++m) {
       const int j = ln.w + NW8 * m;
@@ -709,16 +711,50 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         z[m][r] = x;
       }
     }
-    // u tile i+1 into the buffer read by drive(i-1) before the last barrier
-    __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after this chunk's work
-    stash_u<R, BF16, NB, NW8>(q, ust, lds + ((i + 1) & 1) * ut);
-    lds_barrier();
-  }
+  };
+
+  // Chunks in groups of G: group gi's u tiles sit in LDS half gi & 1 (G tiles
+  // each); the next group's tiles are loaded into registers at the top of a
+  // group and stored to the other half after its work, then one barrier.
+  // Between barriers the waves drift apart, so one wave's scan overlaps
+  // another's MFMAs, and a load has a whole group of work to arrive.
+  auto groups = [&](auto vec_c) {
+    constexpr bool VEC = decltype(vec_c)::value;
+    {
+      UStage<NB> ust[G];
+#pragma unroll
+      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, c, ust[c]);
+#pragma unroll
+      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8>(q, ust[c], lds + c * ut);
+    }
+    lds_barrier();   // mode table, u tiles of group 0
+    for (int i0 = 0; i0 < q.nck; i0 += G) {
+      const int half = (i0 / G) & 1;
+      UStage<NB> ust[G];
+#pragma unroll
+      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, i0 + G + c, ust[c]);
+      // a real loop: unrolled, the compiler hoists all G chunks' MFMAs ahead
+      // of the scans and runs out of registers
+#pragma unroll 1
+      for (int c = 0; c < G; ++c) {
+        f32x4 acc[M8][2][R];
+        float4 dl[TV ? M8 : 1][TV ? R : 1];
+        delta(i0 + c, dl);
+        mma(lds + (half * G + c) * ut, acc);
+        scan(acc, dl);
+      }
+      // the next group's tiles into the other half (read by the previous group
+      // before the last barrier)
+      __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the group's work
+#pragma unroll
+      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8>(q, ust[c], lds + ((1 - half) * G + c) * ut);
+      lds_barrier();
+    }
   };
   if (u_rows_vectorized(q.H, BF16)) {
-    chunks(std::true_type{});
+    groups(std::true_type{});
   } else {
-    chunks(std::false_type{});
+    groups(std::false_type{});
   }
 
   // stream aggregates, then the range total over the 16 streams
@@ -1467,9 +1503,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       bf16x8 xf[K2][NP][R];
 #pragma unroll
       for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
-      // the reads stay kAhead K-steps ahead of their MFMAs in the schedule
-      // (left alone, the scheduler puts each read next to its use and the
-      // MFMAs wait for LDS latency)
+      // the u loads first, then the x reads kAhead K-steps ahead of their
+      // MFMAs (left alone, the scheduler puts each load next to its use)
+      __builtin_amdgcn_sched_group_barrier(0x020, VEC ? NB : NB * (BF16 ? 8 : 4), 0);
       __builtin_amdgcn_sched_group_barrier(0x100, (kAhead < K2 ? kAhead : K2) * NP * R, 0);
 #pragma unroll
       for (int s = 0; s < K2; ++s) {
