@@ -758,6 +758,16 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   }
 
   // stream aggregates, then the range total over the 16 streams
+  float2 aseg[TV ? 1 : M8][4];   // loaded together (one round of latency)
+  if constexpr (!TV) {
+#pragma unroll
+    for (int m = 0; m < M8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = ln.w + NW8 * m;
+        aseg[m][r] = j < NT ? q.modes[16 * j + 4 * ln.g + r].aseg : make_float2(0.0f, 0.0f);
+      }
+  }
 #pragma unroll
   for (int m = 0; m < M8; ++m) {
     const int j = ln.w + NW8 * m;
@@ -772,8 +782,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         q.sagg_a[si] = make_float2(A[m][r].re, A[m][r].im);
         At = A[m][r];
       } else {
-        const float2 as = q.modes[pm].aseg;
-        At = {as.x, as.y};
+        At = {aseg[m][r].x, aseg[m][r].y};
       }
       cf Xt = z[m][r];
       row_scan(At, Xt);
@@ -1229,7 +1238,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq, int p, S5_LDS pf2* s_c0) {
   cf c = {0.0f, 0.0f};
   const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + p;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   for (int q0 = 0; q0 < qq; q0 += kBatch) {
     cf xs[kBatch], as[kBatch];
 #pragma unroll
@@ -1254,22 +1263,25 @@ __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq,
 template <int MPW, bool TV>
 __device__ __forceinline__ void stream_start(const FusedParams& q, int bq, const Lane& ln, const S5_LDS pf2* s_c0,
                                              cf (&st)[MPW][4]) {
+  // all loads first (one round of latency), then the scans
+  float2 xv[MPW][4], av[MPW][4];
 #pragma unroll
   for (int jj = 0; jj < MPW; ++jj) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
       const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
-      const float2 xv = q.sagg[si];
-      cf X = {xv.x, xv.y};
-      cf A;
-      if constexpr (TV) {
-        const float2 av = q.sagg_a[si];
-        A = {av.x, av.y};
-      } else {
-        const float2 as = q.modes[pm].aseg;
-        A = {as.x, as.y};
-      }
+      xv[jj][r] = q.sagg[si];
+      av[jj][r] = TV ? q.sagg_a[si] : q.modes[pm].aseg;
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      cf X = {xv[jj][r].x, xv[jj][r].y};
+      cf A = {av[jj][r].x, av[jj][r].y};
       row_scan(A, X);
       const cf Ae = {row_shr<1>(A.re, 1.0f), row_shr<1>(A.im, 0.0f)};
       const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
