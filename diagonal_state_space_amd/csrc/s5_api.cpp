@@ -6,6 +6,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "s5_internal.h"
 
@@ -31,6 +32,83 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 bool alloc_fail_hook() {
   const char* v = std::getenv("S5_TEST_FAIL_ALLOC");
   return v != nullptr && v[0] == '1';
+}
+
+// Scratch memory: a cache of device buffers owned by the library, reused
+// across calls. (Stream-ordered hipMallocAsync/hipFreeAsync per call would do,
+// but hipFreeAsync blocks the host until the stream has caught up, which
+// serialises the host's launches with the GPU's work.) A buffer is reused by a
+// later call on the stream that used it last (stream order makes that safe),
+// or by any call once the event recorded after its last use has completed;
+// otherwise a new buffer is allocated. Buffers are kept until the process
+// ends: at most the calls in flight on distinct streams at once, each no
+// larger than the largest scratch asked for so far.
+struct Scratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  int dev = -1;
+  hipStream_t last = nullptr;   // stream of the last use
+  hipEvent_t done = nullptr;    // recorded on `last` after the last use
+  bool busy = false;            // taken by a call that has not enqueued its release yet
+};
+std::mutex g_scratch_mu;
+Scratch* g_scratch[64] = {};
+int g_nscratch = 0;
+
+// A buffer of at least `bytes` on the current device for work on `stream`.
+hipError_t scratch_acquire(size_t bytes, hipStream_t stream, Scratch** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  Scratch* pick = nullptr;
+  for (int i = 0; i < g_nscratch && pick == nullptr; ++i) {
+    Scratch* s = g_scratch[i];
+    if (s->busy || s->dev != dev || s->bytes < bytes) continue;
+    if (s->last == stream || hipEventQuery(s->done) == hipSuccess) pick = s;
+  }
+  if (pick == nullptr) {
+    if (g_nscratch == 64) {
+      // full: drop an idle buffer (its last use has finished) to make room
+      int victim = -1;
+      for (int i = 0; i < g_nscratch && victim < 0; ++i)
+        if (!g_scratch[i]->busy && hipEventQuery(g_scratch[i]->done) == hipSuccess) victim = i;
+      if (victim < 0) return hipErrorOutOfMemory;
+      Scratch* v = g_scratch[victim];
+      (void)hipFree(v->ptr);
+      (void)hipEventDestroy(v->done);
+      delete v;
+      g_scratch[victim] = g_scratch[--g_nscratch];
+    }
+    Scratch* s = new Scratch();
+    e = hipMalloc(&s->ptr, bytes);
+    if (e != hipSuccess) {
+      delete s;
+      return e;
+    }
+    e = hipEventCreateWithFlags(&s->done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipFree(s->ptr);
+      delete s;
+      return e;
+    }
+    s->bytes = bytes;
+    s->dev = dev;
+    g_scratch[g_nscratch++] = s;
+    pick = s;
+  }
+  pick->busy = true;
+  *out = pick;
+  return hipSuccess;
+}
+
+// The call's work on `stream` is enqueued: the buffer is free once it is done.
+hipError_t scratch_release(Scratch* s, hipStream_t stream) {
+  const hipError_t e = hipEventRecord(s->done, stream);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  s->last = stream;
+  s->busy = false;
+  return e;
 }
 
 s5_status check_sizes(int64_t P, int64_t H) {
@@ -91,12 +169,12 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (!s5::forward_supported(a)) return S5_ERR_UNSUPPORTED;
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
   const size_t bytes = s5::forward_workspace_bytes(a);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  Scratch* ws = nullptr;
+  hipError_t e = scratch_acquire(bytes, stream, &ws);
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
-  e = s5::launch_forward(a, ws, stream, tl_events, tl_nevents);
-  const hipError_t ef = hipFreeAsync(ws, stream);
+  e = s5::launch_forward(a, ws->ptr, stream, tl_events, tl_nevents);
+  const hipError_t ef = scratch_release(ws, stream);
   if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
   return S5_OK;
 }

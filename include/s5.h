@@ -28,8 +28,13 @@
  * - Complex values are interleaved (re, im) float32 pairs: `s5_c64`, the
  *   layout of torch.complex64 and numpy.complex64.
  * - Every call is asynchronous on `stream` (NULL = the null stream) and does
- *   not synchronise the host. Internal scratch memory is taken from HIP's
- *   stream-ordered allocator on `stream` and released on it.
+ *   not synchronise the host (except when it allocates scratch, below).
+ *   Internal scratch memory comes from buffers the library keeps for reuse:
+ *   a later call on the same stream, or any call once the earlier call's
+ *   work has finished, reuses a buffer; otherwise hipMalloc adds one (which
+ *   may synchronise). Buffers live until the process ends: one per stream
+ *   with calls in flight, each as large as the largest scratch asked for so
+ *   far (a few MB at the benchmark sizes).
  * - Arguments are validated on the host before anything is enqueued; a call
  *   that returns an error has enqueued nothing. Errors of kernels that run
  *   later surface at the caller's next synchronisation with the stream.
