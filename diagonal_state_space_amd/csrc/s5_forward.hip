@@ -39,13 +39,13 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
                       (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
     // eight-wave pass 1: two groups of u tiles and the mode table
-    const size_t lrw = 2 * fused::reduce_group(bf16_io) * fused::u_tile_bytes(KS, R, bf16_io) +
+    const size_t lrw = 2 * fused::reduce_group(bf16_io, time_varying) * fused::u_tile_bytes(KS, R, bf16_io) +
                        fused::mode_table_bytes(Ppad, Hpad, time_varying, false);
     if (k && lrw > lds_max) continue;
     p.R = R;
     p.keep = k;
     p.keep_scan = ks;
-    p.group = k ? fused::reduce_group(bf16_io) : 1;
+    p.group = k ? fused::reduce_group(bf16_io, time_varying) : 1;
     p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;
     p.lds_scan = ls;

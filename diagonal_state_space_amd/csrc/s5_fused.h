@@ -24,8 +24,9 @@ __host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool t
   return static_cast<size_t>(Ppad) * (tv ? 20 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
 }
 // chunks between two barriers of the eight-wave pass 1 (u tiles of two such
-// groups in LDS; the chunk count is padded to a multiple of it)
-__host__ __device__ constexpr int reduce_group(bool bf16) { return bf16 ? 4 : 2; }
+// groups in LDS; the chunk count is padded to a multiple of it). Smaller for
+// the time-varying step, whose per-token constants leave fewer registers.
+__host__ __device__ constexpr int reduce_group(bool bf16, bool tv) { return tv ? (bf16 ? 1 : 2) : (bf16 ? 4 : 2); }
 }  // namespace fused
 
 // Per-mode constants written by the packing kernel.

@@ -584,7 +584,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NT = 4 * MPW;                 // mode tiles
   constexpr int M8 = (NT + NW8 - 1) / NW8;    // tiles per wave, at most
   extern __shared__ __align__(16) unsigned char smem[];
-  if (q.Ppad != 64 * MPW || q.R != R || q.nck % reduce_group(BF16) != 0) return;   // dispatch mismatch
+  if (q.Ppad != 64 * MPW || q.R != R || q.nck % reduce_group(BF16, TV) != 0) return;   // dispatch mismatch
   Lane ln = lane_ids();
   ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW8 - 1);   // 0..7
   const int bq = blockIdx.x;
@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
-  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16) * ut, false);
+  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16, TV) * ut, false);
 
   // B_bar fragments of the wave's tiles, all K-steps: [s][m][cc][pl]
   bf16x8 bw[kKeepKS][M8][2][NP];
@@ -624,7 +624,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
-  constexpr int G = reduce_group(BF16);   // chunks per barrier (nck is a multiple of G)
+  constexpr int G = reduce_group(BF16, TV);   // chunks per barrier (nck is a multiple of G)
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
 
   // Delta of chunk i (time-varying)
