@@ -27,6 +27,13 @@ O4  x_{-1} = 0, x_k = Lambda_bar_k * x_{k-1} + b_k, one step at a time.
 O5  y_k = Re(C~ x_k) + D * u_k, full spectrum (factor 1).
     [App. A `apply_ssm` readout; abhik.ai review, row 4: the factor two applies
     only to half-spectrum storage]
+O6  stateful form: the recurrence of O4 started from a given state x0 instead
+    of zero (x_{-1} = x0), returning the state after the last step as well, so
+    that a sequence can be processed in pieces with the state carried between
+    them. A nonzero initial state enters every prefix through its transition
+    part. [abhik.ai review, "Associative scans preserve the recurrence" (paper
+    Sec. 2.2, App. H) and its note that streaming keeps only the current state
+    (Sec. 2.2, 3.4); papercache notes Sec. 3.3, online generation]
 
 Every function is pinned by the checks in tests/test_oracle_pins.py against
 closed forms, an ODE solve, the convolution-kernel form, impulse responses,
@@ -49,6 +56,8 @@ __all__ = [
     "readout",
     "forward",
     "forward_timevarying",
+    "forward_state",
+    "forward_timevarying_state",
     "compose",
 ]
 
@@ -101,15 +110,19 @@ def drive(u, b_mat):
     return np.asarray(u, dtype=np.float64) @ np.asarray(b_mat, dtype=np.complex128).T
 
 
-def scan_sequential(lam_bar, bu):
-    """O4: x_k = a_k * x_{k-1} + b_k from x_{-1} = 0, explicit loop over k.
+def scan_sequential(lam_bar, bu, x0=None):
+    """O4: x_k = a_k * x_{k-1} + b_k from x_{-1} = 0 (O6: from x_{-1} = x0
+    when given), explicit loop over k.
 
-    ``bu`` is [B, L, P]; ``lam_bar`` is [P] (time-invariant) or [B, L, P]."""
+    ``bu`` is [B, L, P]; ``lam_bar`` is [P] (time-invariant) or [B, L, P];
+    ``x0`` is [B, P] complex or None."""
     bu = np.asarray(bu, dtype=np.complex128)
     lam_bar = np.asarray(lam_bar, dtype=np.complex128)
     Bn, L, P = bu.shape
     tv = lam_bar.ndim == 3
     x = np.zeros((Bn, P), dtype=np.complex128)
+    if x0 is not None:
+        x[...] = np.asarray(x0, dtype=np.complex128).reshape(Bn, P)
     out = np.empty_like(bu)
     for k in range(L):
         a = lam_bar[:, k, :] if tv else lam_bar
@@ -148,6 +161,36 @@ def forward_timevarying(u, lam, b_tilde, c_tilde, d, delta):
     bu = gain * drive(u, b_tilde)                                     # O3
     x = scan_sequential(lam_bar, bu)                                  # O4
     return readout(x, c_tilde, d, u)                                  # O5
+
+
+def forward_state(u, lam, b_tilde, c_tilde, d, log_delta, x0=None):
+    """O6, time-invariant: y as in ``forward`` with the scan started from x0
+    ([B, P] complex, None = zero), and the state after the last step.
+    Returns (y [B, L, H], x_last [B, P]); x_last = x0 when L = 0."""
+    u = np.asarray(u, dtype=np.float64)
+    Bn, L, _ = u.shape
+    P = np.asarray(lam).shape[0]
+    delta = np.exp(np.asarray(log_delta, dtype=np.float64))          # O1
+    lam_bar, b_bar = discretize(lam, b_tilde, delta)                  # O2
+    bu = drive(u, b_bar)                                              # O3
+    x = scan_sequential(lam_bar, bu, x0)                              # O4, O6
+    x_last = x[:, -1, :] if L > 0 else (np.zeros((Bn, P), np.complex128) if x0 is None
+                                        else np.asarray(x0, dtype=np.complex128).reshape(Bn, P))
+    return readout(x, c_tilde, d, u), x_last                          # O5
+
+
+def forward_timevarying_state(u, lam, b_tilde, c_tilde, d, delta, x0=None):
+    """O6, time-varying: as ``forward_timevarying`` from x0, with the final state."""
+    u = np.asarray(u, dtype=np.float64)
+    Bn, L, _ = u.shape
+    P = np.asarray(lam).shape[0]
+    delta = check_intervals(delta)                                    # O1
+    lam_bar, gain = zoh(np.asarray(lam)[None, None, :], delta)        # O2
+    bu = gain * drive(u, b_tilde)                                     # O3
+    x = scan_sequential(lam_bar, bu, x0)                              # O4, O6
+    x_last = x[:, -1, :] if L > 0 else (np.zeros((Bn, P), np.complex128) if x0 is None
+                                        else np.asarray(x0, dtype=np.complex128).reshape(Bn, P))
+    return readout(x, c_tilde, d, u), x_last                          # O5
 
 
 def compose(earlier, later):

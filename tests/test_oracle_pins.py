@@ -292,6 +292,61 @@ def pin_tv_zero_interval():
     return _rel(y[0, 6] - d * u[0, 6], y[0, 5] - d * u[0, 5])
 
 
+# ---------------------------------------------------------------------------
+# Stateful form (O6): initial state in, final state out
+# ---------------------------------------------------------------------------
+
+def pin_state_free_response():
+    # u = 0 from a given state: x_k = Lambda_bar^(k+1) x0 in closed form, so
+    # y_k = Re(C~ Lambda_bar^(k+1) x0) and the final state Lambda_bar^L x0
+    rng = _rng(11)
+    H, P, L, B = 3, 5, 9, 2
+    lam, bt, ct, d, logd = _rand_params(rng, H, P)
+    x0 = rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))
+    u = np.zeros((B, L, H))
+    y, xl = orc.forward_state(u, lam, bt, ct, d, logd, x0)
+    lb = np.exp(lam * np.exp(logd))
+    powers = lb[None, :] ** np.arange(1, L + 1)[:, None]             # [L, P]
+    xk = x0[:, None, :] * powers[None]                               # [B, L, P]
+    y_ref = (xk @ ct.T).real
+    return max(_rel(y, y_ref), _rel(xl, x0 * lb ** L))
+
+
+def pin_state_split_run():
+    # a sequence processed in two pieces with the state carried between them
+    # equals one run, time-invariant and time-varying
+    rng = _rng(12)
+    H, P, L, B, L1 = 4, 6, 23, 2, 9
+    lam, bt, ct, d, logd = _rand_params(rng, H, P)
+    u = rng.normal(size=(B, L, H))
+    x0 = rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))
+    y, xl = orc.forward_state(u, lam, bt, ct, d, logd, x0)
+    ya, xm = orc.forward_state(u[:, :L1], lam, bt, ct, d, logd, x0)
+    yb, xl2 = orc.forward_state(u[:, L1:], lam, bt, ct, d, logd, xm)
+    err = max(_rel(np.concatenate([ya, yb], axis=1), y), _rel(xl2, xl))
+    delta = np.exp(logd)[None, None, :] * rng.exponential(1.0, size=(B, L, 1))
+    y, xl = orc.forward_timevarying_state(u, lam, bt, ct, d, delta, x0)
+    ya, xm = orc.forward_timevarying_state(u[:, :L1], lam, bt, ct, d, delta[:, :L1], x0)
+    yb, xl2 = orc.forward_timevarying_state(u[:, L1:], lam, bt, ct, d, delta[:, L1:], xm)
+    return max(err, _rel(np.concatenate([ya, yb], axis=1), y), _rel(xl2, xl))
+
+
+def pin_state_superposition():
+    # the layer is affine in (u, x0): the output from (u, x0) is the output
+    # from (u, 0) plus the free response from x0 with zero input
+    rng = _rng(13)
+    H, P, L, B = 3, 4, 12, 1
+    lam, bt, ct, d, logd = _rand_params(rng, H, P)
+    u = rng.normal(size=(B, L, H))
+    x0 = rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))
+    y, xl = orc.forward_state(u, lam, bt, ct, d, logd, x0)
+    y_u = orc.forward(u, lam, bt, ct, d, logd)
+    y0, xl0 = orc.forward_state(np.zeros_like(u), lam, bt, ct, d, logd, x0)
+    _, xl_u = orc.forward_state(u, lam, bt, ct, d, logd, None)
+    # (the feedthrough D u is in y_u only: y0 has zero input)
+    return max(_rel(y, y_u + y0), _rel(xl, xl_u + xl0))
+
+
 ALL_PINS = {
     "zoh_expm": (pin_zoh_expm, 1e-12),
     "constant_input": (pin_constant_input_closed_form, 1e-12),
@@ -304,6 +359,9 @@ ALL_PINS = {
     "tv_equals_ti": (pin_tv_equals_ti, 1e-13),
     "tv_semigroup": (pin_tv_semigroup, 1e-12),
     "tv_zero_interval": (pin_tv_zero_interval, 1e-13),
+    "state_free_response": (pin_state_free_response, 1e-12),
+    "state_split_run": (pin_state_split_run, 1e-12),
+    "state_superposition": (pin_state_superposition, 1e-12),
 }
 
 
@@ -552,3 +610,32 @@ def test_planted_series_guard_wrong(monkeypatch):
     monkeypatch.setattr(orc, "zoh", bad)
     with pytest.raises(AssertionError):
         test_zero_pole_limit()
+
+
+def test_planted_initial_state_not_advanced(monkeypatch):
+    # the initial state taken as the state after step 0's transition (x_0 =
+    # x0 + b_0 instead of a_0 x0 + b_0)
+    def wrong(lam_bar, bu, x0=None):
+        bu = np.asarray(bu, np.complex128)
+        lam_bar = np.asarray(lam_bar, np.complex128)
+        tv = lam_bar.ndim == 3
+        x = np.zeros((bu.shape[0], bu.shape[2]), np.complex128)
+        out = np.empty_like(bu)
+        for k in range(bu.shape[1]):
+            a = lam_bar[:, k, :] if tv else lam_bar
+            if k == 0 and x0 is not None:
+                x = np.asarray(x0, np.complex128) + bu[:, 0, :]
+            else:
+                x = a * x + bu[:, k, :]
+            out[:, k, :] = x
+        return out
+
+    monkeypatch.setattr(orc, "scan_sequential", wrong)
+    assert _fails("state_free_response") and _fails("state_split_run")
+
+
+def test_planted_initial_state_ignored(monkeypatch):
+    good = orc.scan_sequential
+    monkeypatch.setattr(orc, "scan_sequential", lambda lam_bar, bu, x0=None: good(lam_bar, bu))
+    # (superposition holds trivially when x0 has no effect)
+    assert _fails("state_free_response") and _fails("state_split_run")
