@@ -26,6 +26,8 @@ __all__ = [
     "discretize",
     "forward",
     "forward_timevarying",
+    "forward_stateful",
+    "forward_timevarying_stateful",
     "set_profiling_events",
     "status_string",
 ]
@@ -39,8 +41,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libs5.so")
 _lib = None
 
-EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_status_string",
-           "s5_set_profiling_events")
+EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_forward_stateful",
+           "s5_forward_timevarying_stateful", "s5_status_string", "s5_set_profiling_events")
 
 
 class S5Error(RuntimeError):
@@ -65,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.s5_forward_timevarying.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
                                              vp, vp, vp, vp]
         L.s5_forward_timevarying.restype = st
+        L.s5_forward_stateful.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp]
+        L.s5_forward_stateful.restype = st
+        L.s5_forward_timevarying_stateful.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp,
+                                                      vp, vp, vp, vp, vp, vp, vp]
+        L.s5_forward_timevarying_stateful.restype = st
         L.s5_status_string.argtypes = [st]
         L.s5_status_string.restype = ctypes.c_char_p
         L.s5_set_profiling_events.argtypes = [vp, ctypes.c_int]
@@ -170,6 +178,46 @@ def forward_timevarying(u, lam, b_tilde, c_tilde, d, delta, y=None, stream=None)
                                         delta.data_ptr(), y.data_ptr(), _stream_handle(stream)),
            "s5_forward_timevarying")
     return y
+
+
+def _state_args(x0, x_last, B, P, device):
+    import torch
+    if x0 is not None:
+        _dev_tensor(x0, "x0", torch.complex64, (B, P))
+    if x_last is None:
+        x_last = torch.empty(B, P, dtype=torch.complex64, device=device)
+    _dev_tensor(x_last, "x_last", torch.complex64, (B, P))
+    return (x0.data_ptr() if x0 is not None else None), x_last
+
+
+def forward_stateful(u, lam, b_tilde, c_tilde, d, log_delta, x0=None, y=None, x_last=None,
+                     stream=None):
+    """Time-invariant forward from the state x0 ([B, P] complex64, None = zero);
+    returns (y, x_last) with x_last [B, P] the state after the last step."""
+    import torch
+    B, L, H, P, io, y = _forward_args(u, lam, b_tilde, c_tilde, d, y)
+    _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    x0p, x_last = _state_args(x0, x_last, B, P, u.device)
+    _check(lib().s5_forward_stateful(B, L, H, P, io, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
+                                     c_tilde.data_ptr(), d.data_ptr(), log_delta.data_ptr(), x0p,
+                                     y.data_ptr(), x_last.data_ptr(), _stream_handle(stream)),
+           "s5_forward_stateful")
+    return y, x_last
+
+
+def forward_timevarying_stateful(u, lam, b_tilde, c_tilde, d, delta, x0=None, y=None, x_last=None,
+                                 stream=None):
+    """Time-varying forward from the state x0; returns (y, x_last)."""
+    import torch
+    B, L, H, P, io, y = _forward_args(u, lam, b_tilde, c_tilde, d, y)
+    _dev_tensor(delta, "delta", torch.float32, (B, L, P))
+    x0p, x_last = _state_args(x0, x_last, B, P, u.device)
+    _check(lib().s5_forward_timevarying_stateful(B, L, H, P, io, u.data_ptr(), lam.data_ptr(),
+                                                 b_tilde.data_ptr(), c_tilde.data_ptr(), d.data_ptr(),
+                                                 delta.data_ptr(), x0p, y.data_ptr(),
+                                                 x_last.data_ptr(), _stream_handle(stream)),
+           "s5_forward_timevarying_stateful")
+    return y, x_last
 
 
 def set_profiling_events(events) -> None:

@@ -120,7 +120,7 @@ s5_status check_sizes(int64_t P, int64_t H) {
 s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
                          const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
                          const float* d, const float* log_delta, const float* delta, void* y,
-                         bool time_varying, hipStream_t stream) {
+                         bool time_varying, const s5_c64* x0, s5_c64* x_last, hipStream_t stream) {
   if (B < 0 || L < 0) return S5_ERR_INVALID_ARGUMENT;
   s5_status st = check_sizes(P, H);
   if (st != S5_OK) return st;
@@ -130,7 +130,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (!lambda || !b_tilde || !c_tilde || !d) return S5_ERR_INVALID_ARGUMENT;
   if (time_varying ? false : !log_delta) return S5_ERR_INVALID_ARGUMENT;
   if (tokens > 0 && (!u || !y || (time_varying && !delta))) return S5_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y};
+  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y, x0, x_last};
   for (const void* p : ptrs) {
     if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
   }
@@ -143,12 +143,37 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
                             range_of(c_tilde, H * P * 8),
                             range_of(d, H * 4),
                             log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
-                            delta ? range_of(delta, tokens * P * 4) : Range{0, 0}};
+                            delta ? range_of(delta, tokens * P * 4) : Range{0, 0},
+                            x0 ? range_of(x0, B * P * 8) : Range{0, 0}};
     for (const Range& r : inputs) {
       if (overlaps(ry, r)) return S5_ERR_INVALID_ARGUMENT;
     }
   }
-  if (tokens == 0) return S5_OK;
+  if (x_last && B > 0) {
+    // the final state is written while other workgroups still read x0 and the
+    // inputs: it may overlap none of them, nor y
+    const Range rx = range_of(x_last, B * P * 8);
+    const Range others[] = {tokens > 0 ? range_of(u, tokens * H * es) : Range{0, 0},
+                            range_of(lambda, P * 8),
+                            range_of(b_tilde, P * H * 8),
+                            range_of(c_tilde, H * P * 8),
+                            range_of(d, H * 4),
+                            log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
+                            delta && tokens > 0 ? range_of(delta, tokens * P * 4) : Range{0, 0},
+                            tokens > 0 ? range_of(y, tokens * H * es) : Range{0, 0},
+                            x0 ? range_of(x0, B * P * 8) : Range{0, 0}};
+    for (const Range& r : others) {
+      if (overlaps(rx, r)) return S5_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (tokens == 0) {
+    if (B > 0 && L == 0 && x_last) {
+      const hipError_t e = s5::launch_state_passthrough(reinterpret_cast<const float2*>(x0),
+                                                        reinterpret_cast<float2*>(x_last), B * P, stream);
+      return e == hipSuccess ? S5_OK : S5_ERR_HIP;
+    }
+    return S5_OK;
+  }
 
   s5::ForwardArgs a{};
   a.B = static_cast<int>(B);
@@ -165,6 +190,8 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.log_delta = log_delta;
   a.delta = delta;
   a.y = y;
+  a.x0 = reinterpret_cast<const float2*>(x0);
+  a.xlast = reinterpret_cast<float2*>(x_last);
 
   if (!s5::forward_supported(a)) return S5_ERR_UNSUPPORTED;
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
@@ -213,7 +240,15 @@ s5_status s5_forward(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, co
                      const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
                      const float* d, const float* log_delta, void* y, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
-                        false, stream);
+                        false, nullptr, nullptr, stream);
+}
+
+s5_status s5_forward_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                              const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                              const float* d, const float* log_delta, const s5_c64* x0, void* y,
+                              s5_c64* x_last, hipStream_t stream) {
+  return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
+                        false, x0, x_last, stream);
 }
 
 s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
@@ -221,7 +256,15 @@ s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_
                                  const s5_c64* c_tilde, const float* d, const float* delta,
                                  void* y, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, nullptr, delta, y, true,
-                        stream);
+                        nullptr, nullptr, stream);
+}
+
+s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
+                                          const void* u, const s5_c64* lambda, const s5_c64* b_tilde,
+                                          const s5_c64* c_tilde, const float* d, const float* delta,
+                                          const s5_c64* x0, void* y, s5_c64* x_last, hipStream_t stream) {
+  return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, nullptr, delta, y, true, x0,
+                        x_last, stream);
 }
 
 const char* s5_status_string(s5_status s) {

@@ -80,7 +80,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Layout {
   FusedPlan plan;
   int Ppad, Hpad;
-  size_t bpack, cpack, modes, sagg, sagg_a, tot, tot_a, total;
+  size_t bpack, cpack, modes, sagg, sagg_a, tot, tot_a, cap, total;
 };
 
 int device_cus() {
@@ -110,6 +110,7 @@ Layout layout(const ForwardArgs& a) {
   l.sagg_a = off; off += a.time_varying ? align_up(nranges * kStreams * l.Ppad * sizeof(float2)) : 0;
   l.tot = off;    off += align_up(nranges * l.Ppad * sizeof(float2));
   l.tot_a = off;  off += align_up(nranges * l.Ppad * sizeof(float2));
+  l.cap = off;    off += align_up(static_cast<size_t>(a.B) * 2 * l.Ppad * sizeof(float2));
   l.total = off;
   return l;
 }
@@ -150,6 +151,21 @@ bool forward_supported(const ForwardArgs& a) {
   return p.R != 0;
 }
 
+namespace {
+__global__ void __launch_bounds__(256) k_state_passthrough(const float2* x0, float2* xlast, int64_t n) {
+  for (int64_t k = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; k < n;
+       k += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    xlast[k] = x0 != nullptr ? x0[k] : make_float2(0.0f, 0.0f);
+}
+}  // namespace
+
+hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(k_state_passthrough, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, x0, xlast, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, const hipEvent_t* ev, int nev) {
   const Layout l = layout(a);
   if (l.plan.R == 0) return hipErrorInvalidValue;
@@ -163,6 +179,7 @@ hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, co
   q.u = a.u; q.y = a.y;
   q.lam = a.lam; q.b_tilde = a.b_tilde; q.c_tilde = a.c_tilde;
   q.d = a.d; q.log_delta = a.log_delta; q.delta = a.delta;
+  q.x0 = a.x0; q.xlast = a.xlast;
   q.bpack = reinterpret_cast<uint4*>(base + l.bpack);
   q.cpack = reinterpret_cast<uint4*>(base + l.cpack);
   q.modes = reinterpret_cast<ModeParams*>(base + l.modes);
@@ -170,6 +187,7 @@ hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, co
   q.sagg_a = a.time_varying ? reinterpret_cast<float2*>(base + l.sagg_a) : nullptr;
   q.tot = reinterpret_cast<float2*>(base + l.tot);
   q.tot_a = reinterpret_cast<float2*>(base + l.tot_a);
+  q.cap = reinterpret_cast<float2*>(base + l.cap);
   hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
   if (e != hipSuccess) return e;
   e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);

@@ -61,6 +61,8 @@ struct FusedParams {
   const float* d;
   const float* log_delta;
   const float* delta;
+  const float2* x0;   // [B, P] state before step 0, or null (zero)
+  float2* xlast;      // [B, P] out: state after step L-1, or null
   // workspace
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O)
   uint4* cpack;       // readout operand fragments (hi, then lo)
@@ -69,6 +71,8 @@ struct FusedParams {
   float2* sagg_a;     // [B*Q][16][Ppad] stream transition product (time-varying)
   float2* tot;        // [B*Q][Ppad] workgroup range state from a zero start
   float2* tot_a;      // [B*Q][Ppad] workgroup range transition product
+  float2* cap;        // [B][2][Ppad] state (from zero) and transition product of the
+                      // stream holding token L-1, from its first token through L-1
 };
 
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.

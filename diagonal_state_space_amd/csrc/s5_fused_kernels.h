@@ -151,6 +151,68 @@ __device__ __forceinline__ uint32_t rel_row(const FusedParams& q, int t, int i, 
   return static_cast<uint32_t>(t * q.Lseg + i * R + n);
 }
 
+// ---- state before the first step and after the last ---------------------------------
+// Token L-1 of every sequence lies in workgroup range `qq`, stream `t`, chunk
+// `i`, step `n`. When the caller asks for the final state, pass 1 records that
+// stream's state from a zero start through token L-1 (and, time-varying, the
+// product of its transitions), and pass 2 applies them to the stream's start
+// state: x_{L-1} = A x_start + X. (The scan itself runs on past L-1 over the
+// zero input of the padding tokens, which would decay the state.)
+struct LastTok {
+  int qq, t, i, n;
+};
+template <int R>
+__device__ __forceinline__ LastTok last_token(const FusedParams& q) {
+  const int k = q.L - 1;
+  const int span = kStreams * q.Lseg;
+  LastTok lt;
+  lt.qq = k / span;
+  const int rem = k - lt.qq * span;
+  lt.t = rem / q.Lseg;
+  const int r2 = rem - lt.t * q.Lseg;
+  lt.i = r2 / R;
+  lt.n = r2 - lt.i * R;
+  return lt;
+}
+
+// pass 1, in the lane of stream lt.t after step lt.n of chunk lt.i
+__device__ __forceinline__ void record_partial(const FusedParams& q, int b, int pm, const cf& x, const cf& a) {
+  float2* c = q.cap + static_cast<size_t>(b) * 2 * q.Ppad;
+  c[pm] = make_float2(x.re, x.im);
+  c[q.Ppad + pm] = make_float2(a.re, a.im);
+}
+
+// pass 2, in the lanes of stream lt.t of range lt.qq right after their start
+// state is known: the state after token L-1 for the lane's modes. The
+// time-invariant transition over the m steps is exp(m lambda Delta), in float64.
+template <int R, int MPW, bool TV>
+__device__ __forceinline__ void write_final_state(const FusedParams& q, int b, const LastTok& lt, const Lane& ln,
+                                                  const cf (&st)[MPW][4]) {
+  if (ln.t != lt.t) return;
+  const float2* c = q.cap + static_cast<size_t>(b) * 2 * q.Ppad;
+  const double m = static_cast<double>(lt.i * R + lt.n + 1);
+#pragma unroll
+  for (int jj = 0; jj < MPW; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+      if (pm >= q.P) continue;
+      const cf X = {c[pm].x, c[pm].y};
+      cf A;
+      if constexpr (TV) {
+        A = {c[q.Ppad + pm].x, c[q.Ppad + pm].y};
+      } else {
+        const double dt = exp(static_cast<double>(q.log_delta[pm])) * m;
+        const double mag = exp(static_cast<double>(q.lam[pm].x) * dt);
+        double sn, cs;
+        sincos(static_cast<double>(q.lam[pm].y) * dt, &sn, &cs);
+        A = {static_cast<float>(mag * cs), static_cast<float>(mag * sn)};
+      }
+      const cf x = cfma(A, st[jj][r], X);
+      q.xlast[static_cast<size_t>(b) * q.P + pm] = make_float2(x.re, x.im);
+    }
+}
+
 // ---- u tile: global -> registers -> LDS in fragment order -----------------------------
 // Block (s, n[, half]) holds, in lane (t, g), u[tok(t, i, n)][32 s + 8 g + ...]:
 // 8 bf16, or 4 floats per half (halves 0 and 1 = elements 0-3 and 4-7). Wave w
@@ -446,7 +508,7 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
 // ---- pass 1 --------------------------------------------------------------------------
 
 // MPW: mode tiles per wave (Ppad = 64 MPW); R: tokens per stream per chunk.
-template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool ST>
 __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -455,6 +517,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const LastTok lt = last_token<R>(q);
+  const int cap_chunk = ST && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
   const int KS = q.Hpad >> 5;
   lds_byte* lds = (lds_byte*)smem;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
@@ -502,13 +566,15 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 1, ust);
     f32x4 acc[MPW][2][R];
     drive<MPW, R, BF16, KEEP>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
+    const bool rec = cap_chunk == i;   // this chunk holds token L-1 (uniform)
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         cf x = z[jj][r];
+        const int pmr = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
         if constexpr (TV) {
-          const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
+          const int pm = pmr;
           const cf lam = ld_pf2(mt.ab + pm);
           const cf inv = ld_pf2(mt.il + pm);
           const float hrev = mt.hr[pm];
@@ -519,11 +585,15 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
             zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
             Ar = cmul(a, Ar);
+            if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pmr, x, Ar);
           }
           A[jj][r] = Ar;
         } else {
 #pragma unroll
-          for (int n = 0; n < R; ++n) x = cfma(abar[jj][r], x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+          for (int n = 0; n < R; ++n) {
+            x = cfma(abar[jj][r], x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+            if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pmr, x, cf{1.0f, 0.0f});
+          }
         }
         z[jj][r] = x;
       }
@@ -577,7 +647,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 // Wave w (0..7) owns mode tiles j = w + 8 jj (j < 4 MPW): half the weights
 // and states of a four-wave split, so two waves fit on each SIMD and one
 // wave's scan overlaps the other's MFMAs. All waves share each u tile.
-template <int MPW, int R, bool TV, bool BF16>
+template <int MPW, int R, bool TV, bool BF16, bool ST>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int NW8 = 2 * kWaves;
@@ -590,6 +660,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const LastTok lt = last_token<R>(q);
+  const int cap_chunk = ST && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
@@ -680,8 +752,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
   };
   // the stream states through one chunk's drive
-  auto scan = [&](const f32x4 (&acc)[M8][2][R], const float4 (&dl)[TV ? M8 : 1][TV ? R : 1])
+  auto scan = [&](int i, const f32x4 (&acc)[M8][2][R], const float4 (&dl)[TV ? M8 : 1][TV ? R : 1])
       __attribute__((always_inline)) {
+    const bool rec = cap_chunk == i;   // this chunk holds token L-1 (uniform)
 #pragma unroll
     for (int m = 0; m < M8; ++m) {
       const int j = ln.w + NW8 * m;
@@ -701,12 +774,16 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
             zoh_step(lam, inv, hrev, f4_at(dl[m][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[m][0][n][r], acc[m][1][n][r]}));
             Ar = cmul(a, Ar);
+            if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, Ar);
           }
           A[m][r] = Ar;
         } else {
           const cf ab = ld_pf2(mt.ab + pm);
 #pragma unroll
-          for (int n = 0; n < R; ++n) x = cfma(ab, x, {acc[m][0][n][r], acc[m][1][n][r]});
+          for (int n = 0; n < R; ++n) {
+            x = cfma(ab, x, {acc[m][0][n][r], acc[m][1][n][r]});
+            if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, cf{1.0f, 0.0f});
+          }
         }
         z[m][r] = x;
       }
@@ -741,7 +818,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         float4 dl[TV ? M8 : 1][TV ? R : 1];
         delta(i0 + c, dl);
         mma(lds + (half * G + c) * ut, acc);
-        scan(acc, dl);
+        scan(i0 + c, acc, dl);
       }
       // the next group's tiles into the other half (read by the previous group
       // before the last barrier)
@@ -1012,7 +1089,7 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
   }
 }
 
-template <int MPW, int R, bool TV, bool BF16, bool KEEP>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool ST>
 __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
@@ -1058,7 +1135,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   // order; it waits in LDS (the second x buffer is not written before the loop).
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);
   if (ln.tid < q.Ppad) {
-    cf c = {0.0f, 0.0f};
+    cf c = {0.0f, 0.0f};   // the state before step 0: zero, or the caller's
+    if (ST && q.x0 != nullptr && ln.tid < q.P) {
+      const float2 v = q.x0[static_cast<size_t>(b) * q.P + ln.tid];
+      c = {v.x, v.y};
+    }
     const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + ln.tid;
     constexpr int kBatch = 8;
     for (int q0 = 0; q0 < qq; q0 += kBatch) {
@@ -1105,6 +1186,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
       st[jj][r] = cfma(Ae, ld_pf2(s_c0 + pm), Xe);
     }
+  }
+  if (ST && q.xlast != nullptr) {
+    const LastTok lt = last_token<R>(q);
+    if (qq == lt.qq) write_final_state<R, MPW, TV>(q, b, lt, ln, st);
   }
 
   // ---- chunk pipeline ----
@@ -1235,8 +1320,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 
 // carry into the workgroup's range: the totals of the sequence's earlier
 // ranges folded in order (one thread per mode)
+template <bool ST>
 __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq, int p, S5_LDS pf2* s_c0) {
-  cf c = {0.0f, 0.0f};
+  cf c = {0.0f, 0.0f};   // the state before step 0: zero, or the caller's
+  if (ST && q.x0 != nullptr && p < q.P) {
+    const float2 v = q.x0[static_cast<size_t>(b) * q.P + p];
+    c = {v.x, v.y};
+  }
   const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + p;
   constexpr int kBatch = 16;
   for (int q0 = 0; q0 < qq; q0 += kBatch) {
@@ -1403,7 +1493,7 @@ __device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ?
   for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16, kOnce>(j0, KS, bk, ua, ub, mt, ln, dl, st, xb);
 }
 
-template <int MPW, int R, bool TV, bool BF16>
+template <int MPW, int R, bool TV, bool BF16, bool ST>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
@@ -1425,7 +1515,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   lds_byte* xlds = lds + 3 * ut;
   const ModeTable mt = fill_mode_table<TV>(q, lds + 3 * ut + 2 * xt, true);
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
-  if (driver && ln.tid < q.Ppad) range_carry(q, b, qq, ln.tid, s_c0);
+  if (driver && ln.tid < q.Ppad) range_carry<ST>(q, b, qq, ln.tid, s_c0);
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
@@ -1475,6 +1565,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if (driver) {
     stream_start<MPW, TV>(q, bq, ln, s_c0, st);
+    if (ST && q.xlast != nullptr) {
+      const LastTok lt = last_token<R>(q);
+      if (qq == lt.qq) write_final_state<R, MPW, TV>(q, b, lt, ln, st);
+    }
     if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
     drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds, mt, ln, dl, st, xlds);
   }
@@ -1547,40 +1641,42 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
 
 // ---- launch -----------------------------------------------------------------------------
 
+template <auto Kern>
+hipError_t launch_one(int blocks, int threads, size_t lds, hipStream_t s, const FusedParams& q) {
+  // the first launch of each instance lifts its dynamic LDS limit
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(Kern, dim3(blocks), dim3(threads), lds, s, q);
+  return hipGetLastError();
+}
+
+// ST: instances that take an initial state or return the final one; the
+// stateless calls run kernels with that code compiled out
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  const int blocks = q.B * q.Q;
+  const bool st = q.x0 != nullptr || q.xlast != nullptr;
   if constexpr (KEEP) {
-    auto kern = k_reduce_ws<MPW, R, TV, BF16>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(2 * kThreads), p.lds_reduce_ws, s, q);
+    return st ? launch_one<k_reduce_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q)
+              : launch_one<k_reduce_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
   } else {
-    auto kern = k_reduce<MPW, R, TV, BF16, KEEP>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_reduce, s, q);
+    return st ? launch_one<k_reduce<MPW, R, TV, BF16, KEEP, true>>(blocks, kThreads, p.lds_reduce, s, q)
+              : launch_one<k_reduce<MPW, R, TV, BF16, KEEP, false>>(blocks, kThreads, p.lds_reduce, s, q);
   }
-  return hipGetLastError();
 }
 
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  const int blocks = q.B * q.Q;
+  const bool st = q.x0 != nullptr || q.xlast != nullptr;
   if constexpr (KEEP) {
-    auto kern = k_scan_ws<MPW, R, TV, BF16>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(2 * kThreads), p.lds_scan, s, q);
+    return st ? launch_one<k_scan_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_scan, s, q)
+              : launch_one<k_scan_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_scan, s, q);
   } else {
-    auto kern = k_scan<MPW, R, TV, BF16, KEEP>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(q.B * q.Q), dim3(kThreads), p.lds_scan, s, q);
+    return st ? launch_one<k_scan<MPW, R, TV, BF16, KEEP, true>>(blocks, kThreads, p.lds_scan, s, q)
+              : launch_one<k_scan<MPW, R, TV, BF16, KEEP, false>>(blocks, kThreads, p.lds_scan, s, q);
   }
-  return hipGetLastError();
 }
 
 }  // namespace fused

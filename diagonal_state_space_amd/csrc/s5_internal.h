@@ -26,6 +26,8 @@ struct ForwardArgs {
   const float* log_delta;  // time-invariant
   const float* delta;      // time-varying [B, L, P]
   void* y;
+  const float2* x0 = nullptr;   // [B, P] state before step 0 (null: zero)
+  float2* xlast = nullptr;      // [B, P] out: state after step L-1 (null: not written)
 };
 
 // Bytes of stream-ordered scratch the forward path needs for these sizes.
@@ -33,6 +35,10 @@ size_t forward_workspace_bytes(const ForwardArgs& a);
 
 // Whether a compiled kernel instance covers these sizes.
 bool forward_supported(const ForwardArgs& a);
+
+// Zero-length sequences: the final state is the initial one (x0, or zero when
+// x0 is null); n = B*P complex values.
+hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, hipStream_t stream);
 
 // Enqueue the whole forward path on `stream` using `ws` (forward_workspace_bytes
 // bytes, 256-byte aligned). ev[2k] / ev[2k+1] are recorded around the k-th

@@ -143,6 +143,37 @@ s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_
                                  const s5_c64* c_tilde, const float* d, const float* delta,
                                  void* y, hipStream_t stream);
 
+/*
+ * s5_forward_stateful / s5_forward_timevarying_stateful - the forward passes
+ * above, started from a given state and reporting the state after the last
+ * step, so that a long sequence can be processed in pieces (or step by step)
+ * with the state carried between calls: running [0, L1) and then [L1, L) with
+ * the first call's x_last as the second call's x0 gives the outputs of one
+ * run over [0, L), up to rounding. (abhik.ai review, "Associative scans
+ * preserve the recurrence": a nonzero initial state enters every prefix
+ * through its transition part; streaming keeps only the current state,
+ * paper Sec. 2.2 and 3.4; papercache notes Sec. 3.3, online generation.)
+ *
+ * Arguments as s5_forward / s5_forward_timevarying, plus
+ *   x0          [B,P] state before step 0 (x_{-1}); NULL = zero state
+ *   x_last      [B,P] out: the state after step L-1 (x_{L-1}); NULL = not
+ *               written. L = 0 copies x0 (or zeros) to it.
+ * Both complex64, 16-byte aligned. x_last may overlap no input, not y and
+ * not x0 (update a state in place by alternating two buffers); x0 may not
+ * overlap y.
+ * Precision: as s5_forward; x_last is float32 (time-invariant: the
+ * transition over the last stream's steps is evaluated in float64).
+ * Errors: as s5_forward.
+ */
+s5_status s5_forward_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                              const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                              const float* d, const float* log_delta, const s5_c64* x0, void* y,
+                              s5_c64* x_last, hipStream_t stream);
+s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
+                                          const void* u, const s5_c64* lambda, const s5_c64* b_tilde,
+                                          const s5_c64* c_tilde, const float* d, const float* delta,
+                                          const s5_c64* x0, void* y, s5_c64* x_last, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* s5_status_string(s5_status s);
 

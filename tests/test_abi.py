@@ -138,3 +138,28 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         s5.forward(u, torch.zeros(3, dtype=torch.complex64), torch.zeros(3, 2, dtype=torch.complex64),
                    torch.zeros(2, 3, dtype=torch.complex64), torch.zeros(2), torch.zeros(3))
+
+
+def _fwd_state(B=2, L=8, H=4, P=3, io=0, u=FAKE, y=FAKE + 0x100000, x0=FAKE + 0x7000,
+               xl=FAKE + 0x8000, tv=False):
+    L_ = s5.lib()
+    if tv:
+        return L_.s5_forward_timevarying_stateful(B, L, H, P, io, u, FAKE + 0x1000, FAKE + 0x2000,
+                                                  FAKE + 0x3000, FAKE + 0x4000, FAKE + 0x6000, x0, y,
+                                                  xl, None)
+    return L_.s5_forward_stateful(B, L, H, P, io, u, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                                  FAKE + 0x4000, FAKE + 0x5000, x0, y, xl, None)
+
+
+@pytest.mark.parametrize("tv", [False, True])
+def test_stateful_validation(tv):
+    assert _fwd_state(x0=FAKE + 0x7004, tv=tv) == UNSUPPORTED       # misaligned state
+    assert _fwd_state(xl=FAKE + 0x8008, tv=tv) == UNSUPPORTED
+    assert _fwd_state(xl=FAKE + 16, tv=tv) == INVALID               # final state overlaps u
+    assert _fwd_state(xl=FAKE + 0x100000, tv=tv) == INVALID         # ... y
+    assert _fwd_state(xl=FAKE + 0x7000, tv=tv) == INVALID           # ... x0 (no in-place update)
+    assert _fwd_state(xl=FAKE + 0x1000, tv=tv) == INVALID           # ... a parameter
+    assert _fwd_state(y=FAKE + 0x7000 - 32, tv=tv) == INVALID       # y overlaps x0
+    assert _fwd_state(B=-1, tv=tv) == INVALID
+    assert _fwd_state(B=0, tv=tv) == OK                              # nothing to do
+    assert _fwd_state(L=0, x0=None, xl=None, tv=tv) == OK           # nothing asked for

@@ -1,0 +1,156 @@
+"""GPU parity of the stateful forward (initial state in, final state out)
+against the float64 oracle, through the C ABI.
+
+y uses the bounds of test_parity_gpu (2e-4 of rms for float32 I/O, 2e-2 of
+rms plus the bf16 output rounding for bf16 I/O). The final state is float32
+in both I/O types; its error comes from the bf16 matrix-core operands (bf16
+I/O) or the bf16x3 split (float32 I/O): max |x_gpu - x_oracle| / rms(x_oracle)
+<= 2e-2 (bf16) and 2e-4 (float32)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.s5_oracle as orc
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diagonal_state_space_amd  # noqa: F401  (fails loudly if libs5.so is missing)
+
+
+def _dev(w):
+    cuda = torch.device("cuda:0")
+    if w.io == "bf16":
+        u = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(cuda)
+    else:
+        u = torch.from_numpy(w.u).to(cuda)
+    t = {"u": u}
+    for k in ("lam", "b_tilde", "c_tilde", "d", "log_delta"):
+        t[k] = torch.from_numpy(getattr(w, k)).to(cuda)
+    if w.delta is not None:
+        t["delta"] = torch.from_numpy(w.delta).to(cuda)
+    return t
+
+
+def _run_gpu(w, t, u=None, delta=None, x0=None):
+    import diagonal_state_space_amd as s5
+    u = t["u"] if u is None else u
+    x0d = None if x0 is None else torch.from_numpy(np.ascontiguousarray(x0).astype(np.complex64)).cuda()
+    if w.time_varying:
+        delta = t["delta"] if delta is None else delta
+        y, xl = s5.forward_timevarying_stateful(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"],
+                                                delta, x0=x0d)
+    else:
+        y, xl = s5.forward_stateful(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["log_delta"],
+                                    x0=x0d)
+    torch.cuda.synchronize()
+    return y, xl
+
+
+def _run_oracle(w, x0):
+    if w.time_varying:
+        return orc.forward_timevarying_state(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.delta, x0)
+    return orc.forward_state(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.log_delta, x0)
+
+
+def _y_ok(w, y, yo):
+    yg = y.float().cpu().numpy().astype(np.float64)
+    rms = math.sqrt(float(np.mean(yo ** 2)))
+    excess = np.abs(yg - yo)
+    if w.io == "bf16":
+        excess = excess - BF16_UNIT_ROUNDOFF * np.abs(yo)
+    return float(np.max(excess)) / rms
+
+
+def _x_err(xg, xo):
+    xg = xg.cpu().numpy().astype(np.complex128)
+    rms = math.sqrt(float(np.mean(np.abs(xo) ** 2)))
+    return float(np.max(np.abs(xg - xo))) / rms
+
+
+SHAPES = [
+    # B, L, H, P, io, tv
+    (1, 1, 5, 3, "f32", False),
+    (2, 97, 24, 40, "f32", False),
+    (2, 97, 24, 40, "bf16", False),
+    (3, 100, 64, 64, "f32", True),
+    (1, 257, 16, 8, "bf16", True),
+    (2, 513, 96, 128, "f32", True),
+    (2, 1000, 256, 192, "f32", False),     # weights streamed from L2 (four-wave kernels)
+    (1, 5001, 128, 256, "bf16", False),    # weights in registers, many ranges, ragged end
+    (2, 4097, 128, 256, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_stateful_parity(shape):
+    B, L, H, P, io, tv = shape
+    w = wl.make_random(B, L, H, P, io=io, tv=tv, seed=31 + L, kind="random_walk" if tv else "normal")
+    rng = np.random.default_rng(L)
+    x0 = (rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))) * 0.5
+    print(f"[state] {w.name}", flush=True)
+    t = _dev(w)
+    y, xl = _run_gpu(w, t, x0=x0)
+    yo, xo = _run_oracle(w, x0)
+    ey, ex = _y_ok(w, y, yo), _x_err(xl, xo)
+    print(f"[state]   y {ey:.3e}  x_last {ex:.3e}  (tol {w.tol:.0e})", flush=True)
+    assert ey <= w.tol
+    assert ex <= w.tol
+    # with no initial state the final state is the zero-start one
+    y0, xl0 = _run_gpu(w, t, x0=None)
+    yo0, xo0 = _run_oracle(w, None)
+    assert _y_ok(w, y0, yo0) <= w.tol
+    assert _x_err(xl0, xo0) <= w.tol
+
+
+@pytest.mark.parametrize("io,tv", [("bf16", False), ("f32", True)])
+def test_split_run_equals_one_run(io, tv):
+    # [0, L1) then [L1, L) with the state carried: the outputs of one run
+    B, L, H, P, L1 = 2, 3000, 128, 128, 1234
+    w = wl.make_random(B, L, H, P, io=io, tv=tv, seed=5, kind="random_walk" if tv else "normal")
+    rng = np.random.default_rng(1)
+    x0 = rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))
+    t = _dev(w)
+    print(f"[state] split {w.name} at {L1}", flush=True)
+    y, xl = _run_gpu(w, t, x0=x0)
+    u1, u2 = t["u"][:, :L1].contiguous(), t["u"][:, L1:].contiguous()
+    d1 = d2 = None
+    if tv:
+        d1, d2 = t["delta"][:, :L1].contiguous(), t["delta"][:, L1:].contiguous()
+    y1, xm = _run_gpu(w, t, u=u1, delta=d1, x0=x0)
+    y2, xl2 = _run_gpu(w, t, u=u2, delta=d2, x0=xm.cpu().numpy())
+    yo, xo = _run_oracle(w, x0)
+    ys = torch.cat([y1, y2], dim=1)
+    print(f"[state]   one run {_y_ok(w, y, yo):.3e}, split {_y_ok(w, ys, yo):.3e}, "
+          f"x_last {_x_err(xl2, xo):.3e}", flush=True)
+    assert _y_ok(w, ys, yo) <= w.tol
+    assert _x_err(xl2, xo) <= w.tol
+    assert _x_err(xl2, xl.cpu().numpy().astype(np.complex128)) <= w.tol
+
+
+def test_zero_length_passes_the_state_through():
+    import diagonal_state_space_amd as s5
+    B, H, P = 3, 8, 16
+    w = wl.make_random(B, 4, H, P, seed=2)
+    t = _dev(w)
+    u = t["u"][:, :0].contiguous()
+    x0 = (torch.randn(B, P, dtype=torch.complex64)).cuda()
+    y, xl = s5.forward_stateful(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["log_delta"], x0=x0)
+    torch.cuda.synchronize()
+    assert y.shape == (B, 0, H)
+    assert torch.equal(xl, x0)
+    xl2 = torch.full((B, P), 7.0 + 7.0j, dtype=torch.complex64, device="cuda")
+    s5.forward_stateful(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["log_delta"], x_last=xl2)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(xl2).item() == 0
