@@ -34,6 +34,28 @@ O6  stateful form: the recurrence of O4 started from a given state x0 instead
     part. [abhik.ai review, "Associative scans preserve the recurrence" (paper
     Sec. 2.2, App. H) and its note that streaming keeps only the current state
     (Sec. 2.2, 3.4); papercache notes Sec. 3.3, online generation]
+O7  half-spectrum storage: when the stored modes are one partner of each
+    conjugate pair, y_k = 2 Re(C+ x_k) + D * u_k; the feedthrough is not
+    doubled. [abhik.ai review, row 4 "Reconstruct real outputs and keep the
+    direct path"; wikillm notes, "Paper vs code", readout factor 2]
+O8  bilinear (trapezoid-rule) discretisation as the alternative to O2: with
+    z = lambda*Delta, Lambda_bar = (1 + z/2)/(1 - z/2) and gain =
+    Delta/(1 - z/2), the diagonal case of the bilinear transform.
+    [intuitivepapers S4 notes, "Discretization and the step size" (the
+    equation group with the forward and backward half-steps); abhik.ai
+    review, "Discretization controls both retention and input gain": the
+    official code offers it as an option]
+O9  GELU epilogue: y -> y * Phi(y), Phi the standard normal distribution
+    function (written with erf), applied to the pre-activation output.
+    [papercache notes, App. A `apply_S5_layer`; wikillm notes, gated
+    activation step; the plain reading of "GELU" is the exact form]
+O10 bidirectional form: a second, backward scan over the same
+    Lambda_bar and B_bar, x'_k = Lambda_bar * x'_{k+1} + B_bar u_k from
+    x'_L = 0 (inclusive of step k), read out by the second half of a
+    C~ with 2P columns: y_k = Re(C~[:, :P] x_k) + Re(C~[:, P:] x'_k) + D u_k
+    (factor 2 on both terms under O7). Time-invariant only; no state in or
+    out. [wikillm notes, "Paper vs code", bidirectional scans; abhik.ai
+    review, offline bidirectional use]
 
 Every function is pinned by the checks in tests/test_oracle_pins.py against
 closed forms, an ODE solve, the convolution-kernel form, impulse responses,
@@ -45,6 +67,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import scipy.special
 
 __all__ = [
     "SERIES_RADIUS",
@@ -59,6 +82,11 @@ __all__ = [
     "forward_state",
     "forward_timevarying_state",
     "compose",
+    "bilinear",
+    "readout_half",
+    "gelu",
+    "scan_reverse",
+    "forward_ex",
 ]
 
 # |z| below which the gain uses the Taylor series of phi1 (abhik.ai review, row 2)
@@ -200,3 +228,88 @@ def compose(earlier, later):
     a_e, b_e = earlier
     a_l, b_l = later
     return a_l * a_e, a_l * b_e + b_l
+
+
+def bilinear(lam, delta):
+    """O8: bilinear discretisation of a diagonal mode. ``lam`` and ``delta``
+    broadcast against each other. Returns (Lambda_bar, gain), complex128."""
+    lam = np.asarray(lam, dtype=np.complex128)
+    d = check_intervals(delta)
+    lam, d = np.broadcast_arrays(lam, d)
+    half = 0.5 * lam * d
+    back = 1.0 - half                 # backward half-step (I - Delta/2 A)
+    return (1.0 + half) / back, d / back
+
+
+def readout_half(x, c_tilde, d, u):
+    """O7: y_k = 2 Re(C+ x_k) + D * u_k for half-spectrum storage."""
+    cx = np.asarray(x, dtype=np.complex128) @ np.asarray(c_tilde, dtype=np.complex128).T
+    return 2.0 * cx.real + np.asarray(d, dtype=np.float64) * np.asarray(u, dtype=np.float64)
+
+
+def gelu(y):
+    """O9: GELU(y) = y * Phi(y) with Phi(y) = (1 + erf(y / sqrt 2)) / 2."""
+    y = np.asarray(y, dtype=np.float64)
+    return y * 0.5 * (1.0 + scipy.special.erf(y / math.sqrt(2.0)))
+
+
+def scan_reverse(lam_bar, bu):
+    """O10: x'_k = a * x'_{k+1} + b_k from x'_L = 0, explicit loop from
+    k = L-1 down to 0. ``bu`` [B, L, P]; ``lam_bar`` [P]."""
+    bu = np.asarray(bu, dtype=np.complex128)
+    lam_bar = np.asarray(lam_bar, dtype=np.complex128)
+    Bn, L, P = bu.shape
+    x = np.zeros((Bn, P), dtype=np.complex128)
+    out = np.empty_like(bu)
+    for k in range(L - 1, -1, -1):
+        x = lam_bar * x + bu[:, k, :]
+        out[:, k, :] = x
+    return out
+
+
+def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None, *,
+               conj_sym=False, method="zoh", activation=None, bidirectional=False):
+    """The forward path with its options: time-invariant (``log_delta`` [P])
+    or time-varying (``delta`` [B, L, P]) intervals, ZOH (O2) or bilinear
+    (O8) discretisation, optional initial state (O6), half-spectrum readout
+    (O7), bidirectional scans (O10, ``c_tilde`` [H, 2P]) and a GELU epilogue
+    (O9, ``activation="gelu"``).
+
+    Returns (y [B, L, H] float64, x_last [B, P] complex128, or None for the
+    bidirectional form)."""
+    u = np.asarray(u, dtype=np.float64)
+    Bn, L, H = u.shape
+    lam = np.asarray(lam, dtype=np.complex128)
+    P = lam.shape[0]
+    disc = {"zoh": zoh, "bilinear": bilinear}[method]
+    tv = delta is not None
+    if tv == (log_delta is not None):
+        raise ValueError("give exactly one of log_delta and delta")
+    if bidirectional and (tv or x0 is not None):
+        raise ValueError("the bidirectional form is time-invariant and stateless")
+    if activation not in (None, "gelu"):
+        raise ValueError("activation must be None or 'gelu'")
+    if tv:
+        lam_bar, gain = disc(lam[None, None, :], delta)               # O1, O2/O8
+        bu = gain * drive(u, b_tilde)                                 # O3
+    else:
+        lam_bar, gain = disc(lam, np.exp(np.asarray(log_delta, dtype=np.float64)))
+        bu = drive(u, gain[:, None] * np.asarray(b_tilde, dtype=np.complex128))
+    x = scan_sequential(lam_bar, bu, x0)                              # O4, O6
+    c = np.asarray(c_tilde, dtype=np.complex128)
+    read = readout_half if conj_sym else readout                      # O7 / O5
+    if bidirectional:
+        xb = scan_reverse(lam_bar, bu)                                # O10
+        y = read(x, c[:, :P], d, u) + read(xb, c[:, P:], np.zeros(H), u)
+        x_last = None
+    else:
+        y = read(x, c, d, u)
+        if L > 0:
+            x_last = x[:, -1, :]
+        elif x0 is None:
+            x_last = np.zeros((Bn, P), np.complex128)
+        else:
+            x_last = np.asarray(x0, dtype=np.complex128).reshape(Bn, P)
+    if activation == "gelu":
+        y = gelu(y)                                                   # O9
+    return y, x_last

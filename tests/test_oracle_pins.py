@@ -11,6 +11,7 @@ import os
 import numpy as np
 import pytest
 import scipy.integrate
+import scipy.special
 import scipy.linalg
 
 import oracle.s5_oracle as orc
@@ -347,6 +348,152 @@ def pin_state_superposition():
     return max(_rel(y, y_u + y0), _rel(xl, xl_u + xl0))
 
 
+
+# ---- options of the forward path (O7-O10) -----------------------------------
+
+def pin_bilinear_trapezoid():
+    """O8 is the trapezoid rule: its states satisfy
+    x_k - x_{k-1} = (lambda Delta_k / 2)(x_k + x_{k-1}) + Delta_k B~ u_k
+    (derivative averaged over both ends of the step, input held at u_k),
+    time-invariant and (through forward_ex's final state) time-varying."""
+    rng = _rng(40)
+    H, P, L = 3, 5, 12
+    lam, bt, ct, d, logd = _rand_params(rng, H, P)
+    delta = np.exp(logd) * 5.0
+    lb, g = orc.bilinear(lam, delta)
+    u = rng.normal(size=(2, L, H))
+    x = orc.scan_sequential(lb, orc.drive(u, g[:, None] * bt))
+    xprev = np.concatenate([np.zeros((2, 1, P)), x[:, :-1]], axis=1)
+    res = x - xprev - 0.5 * lam * delta * (x + xprev) - delta * orc.drive(u, bt)
+    err = float(np.max(np.abs(res)) / np.max(np.abs(x)))
+    # time-varying, through the public form: x_k from prefix runs
+    dtv = rng.uniform(0.01, 0.5, size=(2, L, P))
+    xs = np.stack([orc.forward_ex(u[:, :k + 1], lam, bt, ct, d, delta=dtv[:, :k + 1],
+                                  method="bilinear")[1] for k in range(L)], axis=1)
+    xprev = np.concatenate([np.zeros((2, 1, P)), xs[:, :-1]], axis=1)
+    res = xs - xprev - 0.5 * lam * dtv * (xs + xprev) - dtv * orc.drive(u, bt)
+    return max(err, float(np.max(np.abs(res)) / np.max(np.abs(xs))))
+
+
+def pin_bilinear_equilibrium():
+    """Under a constant input both discretisations settle at the continuous
+    system's equilibrium x* = -B~ u / lambda, so y -> Re(C~ x*) + D u."""
+    rng = _rng(41)
+    H, P, L = 3, 6, 400
+    lam = -rng.uniform(1.0, 3.0, P) + 1j * rng.uniform(-5, 5, P)
+    _, bt, ct, d, _ = _rand_params(rng, H, P, lam=lam)
+    logd = rng.uniform(math.log(0.2), math.log(1.0), P)
+    u0 = rng.normal(size=(2, H))
+    u = np.repeat(u0[:, None, :], L, axis=1)
+    xs = -(u0 @ bt.T) / lam
+    y_inf = (xs @ ct.T).real + d * u0
+    err = 0.0
+    for method in ("bilinear", "zoh"):
+        y, _ = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd, method=method)
+        err = max(err, _rel(y[:, -1], y_inf))
+    return err
+
+
+def pin_bilinear_map():
+    """The bilinear map sends the open left half-plane into the open unit disk
+    and the imaginary axis onto the unit circle, for every Delta > 0; against
+    ZOH its one-step error is z^3/12 for small z = lambda Delta."""
+    rng = _rng(42)
+    lam = -rng.uniform(1e-6, 50, 2000) + 1j * rng.uniform(-500, 500, 2000)
+    delta = np.exp(rng.uniform(math.log(1e-3), math.log(100.0), 2000))
+    lb, _ = orc.bilinear(lam, delta)
+    err = max(0.0, float(np.max(np.abs(lb))) - 1.0 + 1e-15)
+    lb_axis, _ = orc.bilinear(1j * lam.imag, delta)
+    err = max(err, float(np.max(np.abs(np.abs(lb_axis) - 1.0))))
+    z = 1e-3 * np.exp(1j * np.linspace(0.3, 2.8, 7))
+    lbz, _ = orc.bilinear(z, 1.0)
+    ratio = np.abs(lbz - np.exp(z)) / (np.abs(z) ** 3 / 12.0)
+    return max(err, float(np.max(np.abs(ratio - 1.0))) * 1e-2)   # ratio within 1 % of 1
+
+
+def _conjugate_completed(rng, H, Ph):
+    lam_h, bt_h, ct_h, d, logd_h = _rand_params(rng, H, Ph)
+    full = (np.concatenate([lam_h, lam_h.conj()]), np.concatenate([bt_h, bt_h.conj()], axis=0),
+            np.concatenate([ct_h, ct_h.conj()], axis=1), d, np.concatenate([logd_h, logd_h]))
+    return (lam_h, bt_h, ct_h, d, logd_h), full
+
+
+def pin_half_spectrum_ex():
+    """O7 through forward_ex: the half-spectrum form equals the full-spectrum
+    O5 output of the conjugate-completed system (feedthrough once), for
+    time-invariant, time-varying and bidirectional forms."""
+    rng = _rng(43)
+    H, Ph, L = 3, 4, 25
+    (lam_h, bt_h, ct_h, d, logd_h), (lam, bt, ct, _, logd) = _conjugate_completed(rng, H, Ph)
+    u = rng.normal(size=(2, L, H))
+    err = _rel(orc.forward_ex(u, lam_h, bt_h, ct_h, d, log_delta=logd_h, conj_sym=True)[0],
+               orc.forward(u, lam, bt, ct, d, logd))
+    dt = rng.uniform(0.0, 0.2, size=(2, L, Ph))
+    err = max(err, _rel(orc.forward_ex(u, lam_h, bt_h, ct_h, d, delta=dt, conj_sym=True)[0],
+                        orc.forward_timevarying(u, lam, bt, ct, d, np.concatenate([dt, dt], axis=2))))
+    ct2_h = (rng.normal(size=(H, 2 * Ph)) + 1j * rng.normal(size=(H, 2 * Ph))) / math.sqrt(2 * H)
+    ct2 = np.concatenate([ct2_h[:, :Ph], ct2_h[:, :Ph].conj(), ct2_h[:, Ph:], ct2_h[:, Ph:].conj()], axis=1)
+    yh = orc.forward_ex(u, lam_h, bt_h, ct2_h, d, log_delta=logd_h, conj_sym=True, bidirectional=True)[0]
+    yf = orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, bidirectional=True)[0]
+    return max(err, _rel(yh, yf))
+
+
+def pin_gelu_values():
+    """O9 against the normal distribution function integrated numerically
+    (Phi(x) = 1/2 + int_0^x exp(-t^2/2)/sqrt(2 pi) dt), the table value
+    Phi(1) = 0.8413447460685429, and GELU(x) - GELU(-x) = x."""
+    xs = np.array([-4.0, -1.7, -1.0, -0.25, 0.0, 0.3, 1.0, 2.5, 6.0])
+    phi = np.array([0.5 + scipy.integrate.quad(lambda t: math.exp(-0.5 * t * t), 0.0, x,
+                                               epsabs=1e-14, epsrel=1e-13)[0] / math.sqrt(2 * math.pi)
+                    for x in xs])
+    err = float(np.max(np.abs(orc.gelu(xs) - xs * phi)))
+    err = max(err, abs(float(orc.gelu(1.0)) - 0.8413447460685429))
+    err = max(err, float(np.max(np.abs(orc.gelu(xs) - orc.gelu(-xs) - xs))))
+    return err
+
+
+def _conv_bidirectional(u, lam, bt, ct2, d, logd):
+    """Two-sided convolution: y_k = sum_{j<=k} Kf_{k-j} u_j + sum_{j>=k} Kb_{j-k} u_j
+    + D u_k, Kf_i = Re(C_f Lb^i B_bar), Kb_i = Re(C_b Lb^i B_bar), with the
+    discretisation from the augmented-matrix exponential and direct powers."""
+    P = lam.shape[0]
+    lb, g = _zoh_expm(lam, np.exp(logd))
+    z = np.log(lb)
+    bb = g[:, None] * bt
+    B, L, H = u.shape
+    pw = np.exp(np.outer(np.arange(L), z))
+    kf = np.einsum("hp,ip,pq->ihq", ct2[:, :P], pw, bb).real
+    kb = np.einsum("hp,ip,pq->ihq", ct2[:, P:], pw, bb).real
+    y = np.zeros((B, L, H))
+    for k in range(L):
+        y[:, k] = np.einsum("jhq,bjq->bh", kf[k::-1], u[:, :k + 1]) + \
+                  np.einsum("jhq,bjq->bh", kb[:L - k], u[:, k:])
+    return y + d * u
+
+
+def pin_bidirectional_convolution():
+    rng = _rng(44)
+    H, P, L = 3, 5, 30
+    lam, bt, _, d, logd = _rand_params(rng, H, P)
+    ct2 = (rng.normal(size=(H, 2 * P)) + 1j * rng.normal(size=(H, 2 * P))) / math.sqrt(2 * H)
+    u = rng.normal(size=(2, L, H))
+    y = orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, bidirectional=True)[0]
+    return _rel(y, _conv_bidirectional(u, lam, bt, ct2, d, logd))
+
+
+def pin_bidirectional_reversal():
+    """Reversing time and swapping the two readout halves reverses the output."""
+    rng = _rng(45)
+    H, P, L = 4, 6, 33
+    lam, bt, _, d, logd = _rand_params(rng, H, P)
+    ct2 = (rng.normal(size=(H, 2 * P)) + 1j * rng.normal(size=(H, 2 * P))) / math.sqrt(2 * H)
+    u = rng.normal(size=(2, L, H))
+    y = orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, bidirectional=True)[0]
+    swapped = np.concatenate([ct2[:, P:], ct2[:, :P]], axis=1)
+    yr = orc.forward_ex(u[:, ::-1], lam, bt, swapped, d, log_delta=logd, bidirectional=True)[0]
+    return _rel(y, yr[:, ::-1])
+
+
 ALL_PINS = {
     "zoh_expm": (pin_zoh_expm, 1e-12),
     "constant_input": (pin_constant_input_closed_form, 1e-12),
@@ -362,6 +509,13 @@ ALL_PINS = {
     "state_free_response": (pin_state_free_response, 1e-12),
     "state_split_run": (pin_state_split_run, 1e-12),
     "state_superposition": (pin_state_superposition, 1e-12),
+    "bilinear_trapezoid": (pin_bilinear_trapezoid, 1e-12),
+    "bilinear_equilibrium": (pin_bilinear_equilibrium, 1e-10),
+    "bilinear_map": (pin_bilinear_map, 1e-4),
+    "half_spectrum_ex": (pin_half_spectrum_ex, 1e-12),
+    "gelu_values": (pin_gelu_values, 1e-13),
+    "bidirectional_convolution": (pin_bidirectional_convolution, 1e-10),
+    "bidirectional_reversal": (pin_bidirectional_reversal, 1e-12),
 }
 
 
@@ -385,6 +539,12 @@ def test_golden_hippo_n8_eigenvalues():
     lam = wl.hippo_n_eigenvalues(8)
     assert np.all(lam.real == -0.5)
     assert np.max(np.abs(np.sort(lam.imag) - np.sort(ref[:, 1]))) < 5e-4
+
+
+def test_golden_bilinear_scalar():
+    for lre, lim, dt, expect, dec in _load_golden("bilinear_scalar.txt"):
+        lb, _ = orc.bilinear(lre + 1j * lim, dt)
+        assert abs(lb.real - expect) <= 0.5 * 10.0 ** (-dec) and abs(lb.imag) < 1e-15
 
 
 def test_golden_zoh_scalar():
@@ -639,3 +799,64 @@ def test_planted_initial_state_ignored(monkeypatch):
     monkeypatch.setattr(orc, "scan_sequential", lambda lam_bar, bu, x0=None: good(lam_bar, bu))
     # (superposition holds trivially when x0 has no effect)
     assert _fails("state_free_response") and _fails("state_split_run")
+
+
+def test_planted_bilinear_inverted(monkeypatch):
+    good = orc.bilinear
+    monkeypatch.setattr(orc, "bilinear", lambda lam, delta: (1.0 / good(lam, delta)[0], good(lam, delta)[1]))
+    assert _fails("bilinear_trapezoid") and _fails("bilinear_map") and _fails("bilinear_equilibrium")
+
+
+def test_planted_bilinear_gain_without_backward_step(monkeypatch):
+    good = orc.bilinear
+    monkeypatch.setattr(orc, "bilinear", lambda lam, delta: (good(lam, delta)[0],
+                                                             np.broadcast_to(orc.check_intervals(delta), np.shape(good(lam, delta)[1])).astype(np.complex128)))
+    assert _fails("bilinear_trapezoid") and _fails("bilinear_equilibrium")
+
+
+def test_planted_backward_scan_exclusive(monkeypatch):
+    def exclusive(lam_bar, bu):
+        bu = np.asarray(bu, np.complex128)
+        x = np.zeros((bu.shape[0], bu.shape[2]), np.complex128)
+        out = np.empty_like(bu)
+        for k in range(bu.shape[1] - 1, -1, -1):
+            out[:, k] = x
+            x = lam_bar * x + bu[:, k]
+        return out
+    monkeypatch.setattr(orc, "scan_reverse", exclusive)
+    assert _fails("bidirectional_convolution") and _fails("bidirectional_reversal")
+
+
+def test_planted_half_spectrum_doubles_feedthrough(monkeypatch):
+    monkeypatch.setattr(orc, "readout_half", lambda x, c, d, u: 2.0 * orc.readout(x, c, d, u))
+    assert _fails("half_spectrum_ex")
+
+
+def test_planted_gelu_tanh_form(monkeypatch):
+    def tanh_gelu(y):
+        y = np.asarray(y, np.float64)
+        return 0.5 * y * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (y + 0.044715 * y ** 3)))
+    monkeypatch.setattr(orc, "gelu", tanh_gelu)
+    assert _fails("gelu_values")
+
+
+def test_forward_ex_reduces_to_the_plain_forms():
+    rng = _rng(46)
+    H, P, L = 3, 5, 20
+    lam, bt, ct, d, logd = _rand_params(rng, H, P)
+    u = rng.normal(size=(2, L, H))
+    x0 = rng.normal(size=(2, P)) + 1j * rng.normal(size=(2, P))
+    y, xl = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd, x0=x0)
+    yo, xo = orc.forward_state(u, lam, bt, ct, d, logd, x0)
+    assert _rel(y, yo) < 1e-15 and _rel(xl, xo) < 1e-15
+    dt = rng.uniform(0, 0.1, size=(2, L, P))
+    assert _rel(orc.forward_ex(u, lam, bt, ct, d, delta=dt)[0], orc.forward_timevarying(u, lam, bt, ct, d, dt)) < 1e-15
+    ct2 = np.concatenate([ct, np.zeros_like(ct)], axis=1)
+    assert _rel(orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, bidirectional=True)[0],
+                orc.forward(u, lam, bt, ct, d, logd)) < 1e-15
+    yg = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd, activation="gelu")[0]
+    assert _rel(yg, orc.gelu(orc.forward(u, lam, bt, ct, d, logd))) < 1e-15
+    with pytest.raises(ValueError):
+        orc.forward_ex(u, lam, bt, ct2, d, delta=dt, bidirectional=True)
+    with pytest.raises(ValueError):
+        orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, x0=x0, bidirectional=True)
