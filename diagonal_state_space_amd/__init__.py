@@ -42,7 +42,24 @@ lib_path = os.path.join(_PKG, "libs5.so")
 _lib = None
 
 EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_forward_stateful",
-           "s5_forward_timevarying_stateful", "s5_status_string", "s5_set_profiling_events")
+           "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_status_string",
+           "s5_set_profiling_events")
+
+# option bits of s5_forward_ex (include/s5.h)
+FLAG_HALF_SPECTRUM = 1 << 0
+FLAG_BILINEAR = 1 << 1
+FLAG_GELU = 1 << 2
+FLAG_BIDIRECTIONAL = 1 << 3
+
+
+class ForwardDesc(ctypes.Structure):
+    """s5_forward_desc of include/s5.h."""
+    _fields_ = [("size", ctypes.c_uint32), ("flags", ctypes.c_uint32), ("io", ctypes.c_int),
+                ("B", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64), ("P", ctypes.c_int64),
+                ("u", ctypes.c_void_p), ("lam", ctypes.c_void_p), ("b_tilde", ctypes.c_void_p),
+                ("c_tilde", ctypes.c_void_p), ("d", ctypes.c_void_p), ("log_delta", ctypes.c_void_p),
+                ("delta", ctypes.c_void_p), ("x0", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("x_last", ctypes.c_void_p)]
 
 
 class S5Error(RuntimeError):
@@ -73,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.s5_forward_timevarying_stateful.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp,
                                                       vp, vp, vp, vp, vp, vp, vp]
         L.s5_forward_timevarying_stateful.restype = st
+        L.s5_forward_ex.argtypes = [ctypes.POINTER(ForwardDesc), vp]
+        L.s5_forward_ex.restype = st
         L.s5_status_string.argtypes = [st]
         L.s5_status_string.restype = ctypes.c_char_p
         L.s5_set_profiling_events.argtypes = [vp, ctypes.c_int]
@@ -217,6 +236,51 @@ def forward_timevarying_stateful(u, lam, b_tilde, c_tilde, d, delta, x0=None, y=
                                                  delta.data_ptr(), x0p, y.data_ptr(),
                                                  x_last.data_ptr(), _stream_handle(stream)),
            "s5_forward_timevarying_stateful")
+    return y, x_last
+
+
+def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None, *,
+               half_spectrum=False, bilinear=False, gelu=False, bidirectional=False,
+               final_state=False, y=None, x_last=None, stream=None):
+    """The forward pass with its options (s5_forward_ex): exactly one of
+    log_delta [P] (time-invariant) and delta [B, L, P] (time-varying);
+    c_tilde [H, 2P] when bidirectional. Returns (y, x_last), x_last None
+    unless final_state is set or an x_last buffer is given."""
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be [B, L, H]")
+    B, L, H = u.shape
+    P = lam.shape[0]
+    io = _io_code(u.dtype)
+    _dev_tensor(u, "u", u.dtype, (B, L, H))
+    _dev_tensor(lam, "lam", torch.complex64, (P,))
+    _dev_tensor(b_tilde, "b_tilde", torch.complex64, (P, H))
+    _dev_tensor(c_tilde, "c_tilde", torch.complex64, (H, 2 * P if bidirectional else P))
+    _dev_tensor(d, "d", torch.float32, (H,))
+    if (log_delta is None) == (delta is None):
+        raise ValueError("give exactly one of log_delta and delta")
+    if log_delta is not None:
+        _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    if delta is not None:
+        _dev_tensor(delta, "delta", torch.float32, (B, L, P))
+    if y is None:
+        y = torch.empty_like(u)
+    _dev_tensor(y, "y", u.dtype, (B, L, H))
+    x0p = None
+    if x0 is not None:
+        x0p = _dev_tensor(x0, "x0", torch.complex64, (B, P)).data_ptr()
+    if final_state and x_last is None:
+        x_last = torch.empty(B, P, dtype=torch.complex64, device=u.device)
+    if x_last is not None:
+        _dev_tensor(x_last, "x_last", torch.complex64, (B, P))
+    flags = ((FLAG_HALF_SPECTRUM if half_spectrum else 0) | (FLAG_BILINEAR if bilinear else 0) |
+             (FLAG_GELU if gelu else 0) | (FLAG_BIDIRECTIONAL if bidirectional else 0))
+    desc = ForwardDesc(ctypes.sizeof(ForwardDesc), flags, io, B, L, H, P, u.data_ptr(), lam.data_ptr(),
+                       b_tilde.data_ptr(), c_tilde.data_ptr(), d.data_ptr(),
+                       log_delta.data_ptr() if log_delta is not None else None,
+                       delta.data_ptr() if delta is not None else None, x0p, y.data_ptr(),
+                       x_last.data_ptr() if x_last is not None else None)
+    _check(lib().s5_forward_ex(ctypes.byref(desc), _stream_handle(stream)), "s5_forward_ex")
     return y, x_last
 
 

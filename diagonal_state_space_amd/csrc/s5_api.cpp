@@ -117,10 +117,19 @@ s5_status check_sizes(int64_t P, int64_t H) {
   return S5_OK;
 }
 
+// Options of the extended entry point (defaults: the plain forward pass).
+struct Options {
+  float c_scale = 1.0f;    // readout factor: 2 for half-spectrum storage
+  bool bilinear = false;   // bilinear discretisation
+  bool gelu = false;       // GELU epilogue
+  bool bidir = false;      // forward and backward scans, C~ with 2P columns
+};
+
 s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
                          const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
                          const float* d, const float* log_delta, const float* delta, void* y,
-                         bool time_varying, const s5_c64* x0, s5_c64* x_last, hipStream_t stream) {
+                         bool time_varying, const s5_c64* x0, s5_c64* x_last, const Options& opt,
+                         hipStream_t stream) {
   if (B < 0 || L < 0) return S5_ERR_INVALID_ARGUMENT;
   s5_status st = check_sizes(P, H);
   if (st != S5_OK) return st;
@@ -130,6 +139,9 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (!lambda || !b_tilde || !c_tilde || !d) return S5_ERR_INVALID_ARGUMENT;
   if (time_varying ? false : !log_delta) return S5_ERR_INVALID_ARGUMENT;
   if (tokens > 0 && (!u || !y || (time_varying && !delta))) return S5_ERR_INVALID_ARGUMENT;
+  // the backward scan is defined for the time-invariant, stateless form only
+  if (opt.bidir && (time_varying || x0 || x_last)) return S5_ERR_INVALID_ARGUMENT;
+  const int64_t c_cols = opt.bidir ? 2 * P : P;
   const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y, x0, x_last};
   for (const void* p : ptrs) {
     if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
@@ -140,7 +152,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
     const Range inputs[] = {range_of(u, tokens * H * es),
                             range_of(lambda, P * 8),
                             range_of(b_tilde, P * H * 8),
-                            range_of(c_tilde, H * P * 8),
+                            range_of(c_tilde, H * c_cols * 8),
                             range_of(d, H * 4),
                             log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
                             delta ? range_of(delta, tokens * P * 4) : Range{0, 0},
@@ -156,7 +168,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
     const Range others[] = {tokens > 0 ? range_of(u, tokens * H * es) : Range{0, 0},
                             range_of(lambda, P * 8),
                             range_of(b_tilde, P * H * 8),
-                            range_of(c_tilde, H * P * 8),
+                            range_of(c_tilde, H * c_cols * 8),
                             range_of(d, H * 4),
                             log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
                             delta && tokens > 0 ? range_of(delta, tokens * P * 4) : Range{0, 0},
@@ -192,6 +204,10 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.y = y;
   a.x0 = reinterpret_cast<const float2*>(x0);
   a.xlast = reinterpret_cast<float2*>(x_last);
+  a.c_scale = opt.c_scale;
+  a.bilinear = opt.bilinear;
+  a.gelu = opt.gelu && !opt.bidir;
+  a.c_ld = static_cast<int>(c_cols);
 
   if (!s5::forward_supported(a)) return S5_ERR_UNSUPPORTED;
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
@@ -201,6 +217,19 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
   e = s5::launch_forward(a, ws->ptr, stream, tl_events, tl_nevents);
+  if (e == hipSuccess && opt.bidir) {
+    // backward scan: reverse time, second half of C~, no feedthrough (the
+    // forward pass added it), added to the forward pass's y; then GELU
+    s5::ForwardArgs r = a;
+    r.c_off = static_cast<int>(P);
+    r.d = nullptr;
+    r.rev = true;
+    r.accum = true;
+    r.gelu = opt.gelu;
+    const int skip = 6;   // events of the forward pass's three launches
+    e = s5::launch_forward(r, ws->ptr, stream, tl_nevents > skip ? tl_events + skip : nullptr,
+                           tl_nevents > skip ? tl_nevents - skip : 0);
+  }
   const hipError_t ef = scratch_release(ws, stream);
   if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
   return S5_OK;
@@ -240,7 +269,7 @@ s5_status s5_forward(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, co
                      const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
                      const float* d, const float* log_delta, void* y, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
-                        false, nullptr, nullptr, stream);
+                        false, nullptr, nullptr, Options{}, stream);
 }
 
 s5_status s5_forward_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
@@ -248,7 +277,7 @@ s5_status s5_forward_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dty
                               const float* d, const float* log_delta, const s5_c64* x0, void* y,
                               s5_c64* x_last, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
-                        false, x0, x_last, stream);
+                        false, x0, x_last, Options{}, stream);
 }
 
 s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
@@ -256,7 +285,7 @@ s5_status s5_forward_timevarying(int64_t B, int64_t L, int64_t H, int64_t P, s5_
                                  const s5_c64* c_tilde, const float* d, const float* delta,
                                  void* y, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, nullptr, delta, y, true,
-                        nullptr, nullptr, stream);
+                        nullptr, nullptr, Options{}, stream);
 }
 
 s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io,
@@ -264,7 +293,21 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
                                           const s5_c64* c_tilde, const float* d, const float* delta,
                                           const s5_c64* x0, void* y, s5_c64* x_last, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, nullptr, delta, y, true, x0,
-                        x_last, stream);
+                        x_last, Options{}, stream);
+}
+
+s5_status s5_forward_ex(const s5_forward_desc* x, hipStream_t stream) {
+  if (x == nullptr || x->size != sizeof(s5_forward_desc)) return S5_ERR_INVALID_ARGUMENT;
+  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_BIDIRECTIONAL;
+  if ((x->flags & ~known) != 0) return S5_ERR_INVALID_ARGUMENT;
+  if ((x->log_delta == nullptr) == (x->delta == nullptr)) return S5_ERR_INVALID_ARGUMENT;
+  Options o;
+  o.c_scale = (x->flags & S5_FLAG_HALF_SPECTRUM) ? 2.0f : 1.0f;
+  o.bilinear = (x->flags & S5_FLAG_BILINEAR) != 0;
+  o.gelu = (x->flags & S5_FLAG_GELU) != 0;
+  o.bidir = (x->flags & S5_FLAG_BIDIRECTIONAL) != 0;
+  return forward_common(x->B, x->L, x->H, x->P, x->io, x->u, x->lambda, x->b_tilde, x->c_tilde, x->d,
+                        x->log_delta, x->delta, x->y, x->delta != nullptr, x->x0, x->x_last, o, stream);
 }
 
 const char* s5_status_string(s5_status s) {

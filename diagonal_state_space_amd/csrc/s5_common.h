@@ -97,6 +97,27 @@ __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float d
   }
 }
 
+// Bilinear map of one mode for a per-step interval dt >= 0, z = lam dt:
+// w = 1/(1 - z/2), abar = (1 + z/2)/(1 - z/2) = 2 w - 1, gain = dt w.
+// (|1 - z/2| >= 1 for Re lam <= 0.)
+__device__ __forceinline__ void bilinear_step(cf lam, float dt, cf& abar, cf& gain) {
+  const float br = fmaf(-0.5f * dt, lam.re, 1.0f);
+  const float bi = -0.5f * dt * lam.im;
+  const float inv = 1.0f / fmaf(br, br, bi * bi);
+  const cf w = {br * inv, -bi * inv};
+  abar = {fmaf(2.0f, w.re, -1.0f), 2.0f * w.im};
+  gain = {dt * w.re, dt * w.im};
+}
+
+// one per-step discretisation: bilinear when `bil`, else zero-order hold
+__device__ __forceinline__ void disc_step(bool bil, cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
+  if (bil) {
+    bilinear_step(lam, dt, abar, gain);
+  } else {
+    zoh_step(lam, inv_lam, hrev, dt, abar, gain);
+  }
+}
+
 // ---- MFMA operand types and helpers ----------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -180,6 +180,13 @@ hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, co
   q.lam = a.lam; q.b_tilde = a.b_tilde; q.c_tilde = a.c_tilde;
   q.d = a.d; q.log_delta = a.log_delta; q.delta = a.delta;
   q.x0 = a.x0; q.xlast = a.xlast;
+  q.c_ld = a.c_ld > 0 ? a.c_ld : a.P;
+  q.c_off = a.c_off;
+  q.c_scale = a.c_scale;
+  q.bilinear = a.bilinear;
+  q.rev = a.rev;
+  q.accum = a.accum;
+  q.gelu = a.gelu;
   q.bpack = reinterpret_cast<uint4*>(base + l.bpack);
   q.cpack = reinterpret_cast<uint4*>(base + l.cpack);
   q.modes = reinterpret_cast<ModeParams*>(base + l.modes);

@@ -58,11 +58,18 @@ struct FusedParams {
   const float2* lam;
   const float2* b_tilde;
   const float2* c_tilde;
-  const float* d;
+  const float* d;     // [H], or null: no feedthrough
   const float* log_delta;
   const float* delta;
   const float2* x0;   // [B, P] state before step 0, or null (zero)
   float2* xlast;      // [B, P] out: state after step L-1, or null
+  // options (the last four only in the extended kernel instances)
+  int c_ld, c_off;    // C~ row stride and first column (bidirectional halves)
+  float c_scale;      // 2 for half-spectrum storage, else 1
+  int bilinear;       // bilinear instead of zero-order hold discretisation
+  int rev;            // reverse time: token k is row L-1-k of u and y
+  int accum;          // y += the readout (D u included when d is given)
+  int gelu;           // y = GELU(y) after the sum
   // workspace
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O)
   uint4* cpack;       // readout operand fragments (hi, then lo)

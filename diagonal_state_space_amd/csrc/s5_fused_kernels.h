@@ -184,7 +184,7 @@ __device__ __forceinline__ void record_partial(const FusedParams& q, int b, int 
 
 // pass 2, in the lanes of stream lt.t of range lt.qq right after their start
 // state is known: the state after token L-1 for the lane's modes. The
-// time-invariant transition over the m steps is exp(m lambda Delta), in float64.
+// time-invariant transition over the m steps is Lambda_bar^m, in float64.
 template <int R, int MPW, bool TV>
 __device__ __forceinline__ void write_final_state(const FusedParams& q, int b, const LastTok& lt, const Lane& ln,
                                                   const cf (&st)[MPW][4]) {
@@ -202,10 +202,19 @@ __device__ __forceinline__ void write_final_state(const FusedParams& q, int b, c
       if constexpr (TV) {
         A = {c[q.Ppad + pm].x, c[q.Ppad + pm].y};
       } else {
-        const double dt = exp(static_cast<double>(q.log_delta[pm])) * m;
-        const double mag = exp(static_cast<double>(q.lam[pm].x) * dt);
+        // Lambda_bar^m = exp(m log Lambda_bar); log Lambda_bar = lambda Delta
+        // for zero-order hold
+        const double dt = exp(static_cast<double>(q.log_delta[pm]));
+        double zr = static_cast<double>(q.lam[pm].x) * dt, zi = static_cast<double>(q.lam[pm].y) * dt;
+        if (q.bilinear) {
+          const double br = 1.0 - 0.5 * zr, bi = -0.5 * zi, den = br * br + bi * bi;
+          const double ar = 2.0 * br / den - 1.0, ai = 2.0 * -bi / den;
+          zr = 0.5 * log(ar * ar + ai * ai);
+          zi = atan2(ai, ar);
+        }
+        const double mag = exp(zr * m);
         double sn, cs;
-        sincos(static_cast<double>(q.lam[pm].y) * dt, &sn, &cs);
+        sincos(zi * m, &sn, &cs);
         A = {static_cast<float>(mag * cs), static_cast<float>(mag * sn)};
       }
       const cf x = cfma(A, st[jj][r], X);
@@ -247,18 +256,53 @@ constexpr int kBufferOOB = static_cast<int>(0x80000000u);   // beyond any descri
 constexpr int kBufferWord3 = 0x00020000;                     // raw buffer, 32-bit data format
 
 // descriptor over the rows (of H elements) of workgroup range (b, qq) of u or
-// y: rows past the sequence end are outside it (below 1 GiB, host-checked)
+// y: rows past the sequence end are outside it (below 1 GiB, host-checked).
+// In reverse time the range's tokens are the rows just before the first
+// tokens of the earlier ranges, counted from the end of the sequence.
 template <bool BF16>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, const FusedParams& q, int b, int qq) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, const FusedParams& q, int b, int qq,
+                                                             bool rev) {
   constexpr int esz = BF16 ? 2 : 4;
   const int tok0 = qq * kStreams * q.Lseg;
   const int rows = min(q.L - tok0, kStreams * q.Lseg);
-  const char* base = static_cast<const char*>(t) + range_row0(q, b, qq) * q.H * esz;
+  const size_t row0 = rev ? static_cast<size_t>(b) * q.L + (q.L - tok0 - rows) : range_row0(q, b, qq);
+  const char* base = static_cast<const char*>(t) + row0 * q.H * esz;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * q.H * esz, kBufferWord3);
 }
 
+// Memory row, relative to the range descriptor's base, of relative token row
+// r: r in forward time. In reverse time (the backward scan) the range's tokens
+// run backward from its last row, so row last - r; token rows past the
+// sequence end (r > last) go to last + 1, outside the descriptor.
+struct RowMap {
+  bool rev;
+  int last;   // rows of the range - 1
+  __device__ __forceinline__ int operator()(uint32_t r) const {
+    const int ri = static_cast<int>(r);
+    return !rev ? ri : (ri <= last ? last - ri : last + 1);
+  }
+};
+
+template <bool EXT>
+__device__ __forceinline__ RowMap row_map(const FusedParams& q, int qq) {
+  if (EXT && q.rev) return {true, min(q.L - qq * kStreams * q.Lseg, kStreams * q.Lseg) - 1};
+  return {false, 0};
+}
+
+// epilogue options of the extended instances: add to y, GELU
+struct Epi {
+  bool accum;
+  bool gelu;
+};
+
+template <bool EXT>
+__device__ __forceinline__ Epi epilogue(const FusedParams& q) {
+  return {EXT && q.accum != 0, EXT && q.gelu != 0};
+}
+
 template <int R, bool BF16, int NB, int NWV, bool VEC>
-__device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rsrc_t rsrc, int qq, int i, UStage<NB>& st) {
+__device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rsrc_t rsrc, const RowMap& rm, int qq,
+                                        int i, UStage<NB>& st) {
   constexpr int NPU = BF16 ? 1 : 2;
   constexpr int esz = BF16 ? 2 : 4;
   Lane ln = lane_ids();
@@ -275,7 +319,7 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rs
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
     const bool row_ok = live && blk < nblk && tok < q.L;
-    const int roff = static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H;
+    const int roff = rm(rel_row<R>(q, ln.t, i, n)) * q.H;
     if constexpr (VEC) {
       const int off = row_ok && h0 < q.H ? (roff + h0) * esz : kBufferOOB;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
@@ -500,7 +544,7 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
     }
   }
   if (with_d) {
-    for (int h = threadIdx.x; h < q.Hpad; h += kThreads) mt.d[h] = h < q.H ? q.d[h] : 0.0f;
+    for (int h = threadIdx.x; h < q.Hpad; h += kThreads) mt.d[h] = h < q.H && q.d != nullptr ? q.d[h] : 0.0f;
   }
   return mt;   // visible after the caller's next barrier
 }
@@ -508,7 +552,7 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
 // ---- pass 1 --------------------------------------------------------------------------
 
 // MPW: mode tiles per wave (Ppad = 64 MPW); R: tokens per stream per chunk.
-template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool ST>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool EXT>
 __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -517,8 +561,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
+  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
   const LastTok lt = last_token<R>(q);
-  const int cap_chunk = ST && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
+  const int cap_chunk = EXT && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
   const int KS = q.Hpad >> 5;
   lds_byte* lds = (lds_byte*)smem;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
@@ -543,14 +589,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     }
 
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
   {
     UStage<NB> ust;
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 0, ust);
     stash_u<R, BF16, NB, kWaves>(q, ust, lds);
   }
   lds_barrier();
@@ -563,7 +609,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     }
     // u tile i+1 into registers now, into LDS before the barrier
     UStage<NB> ust;
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 1, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 1, ust);
     f32x4 acc[MPW][2][R];
     drive<MPW, R, BF16, KEEP>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
     const bool rec = cap_chunk == i;   // this chunk holds token L-1 (uniform)
@@ -582,7 +628,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
+            disc_step(bil, lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
             Ar = cmul(a, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pmr, x, Ar);
@@ -647,7 +693,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 // Wave w (0..7) owns mode tiles j = w + 8 jj (j < 4 MPW): half the weights
 // and states of a four-wave split, so two waves fit on each SIMD and one
 // wave's scan overlaps the other's MFMAs. All waves share each u tile.
-template <int MPW, int R, bool TV, bool BF16, bool ST>
+template <int MPW, int R, bool TV, bool BF16, bool EXT>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int NW8 = 2 * kWaves;
@@ -660,8 +706,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
+  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
   const LastTok lt = last_token<R>(q);
-  const int cap_chunk = ST && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
+  const int cap_chunk = EXT && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
@@ -697,7 +745,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 
   constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
   constexpr int G = reduce_group(BF16, TV);   // chunks per barrier (nck is a multiple of G)
-  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
 
   // Delta of chunk i (time-varying)
   auto delta = [&](int i, float4 (&dl)[TV ? M8 : 1][TV ? R : 1]) __attribute__((always_inline)) {
@@ -771,7 +819,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            zoh_step(lam, inv, hrev, f4_at(dl[m][n], r), a, gn);
+            disc_step(bil, lam, inv, hrev, f4_at(dl[m][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[m][0][n][r], acc[m][1][n][r]}));
             Ar = cmul(a, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, Ar);
@@ -800,7 +848,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     {
       UStage<NB> ust[G];
 #pragma unroll
-      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, c, ust[c]);
+      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, rmap, qq, c, ust[c]);
 #pragma unroll
       for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8>(q, ust[c], lds + c * ut);
     }
@@ -809,7 +857,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       const int half = (i0 / G) & 1;
       UStage<NB> ust[G];
 #pragma unroll
-      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, qq, i0 + G + c, ust[c]);
+      for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, rmap, qq, i0 + G + c, ust[c]);
       // a real loop: unrolled, the compiler hoists all G chunks' MFMAs ahead
       // of the scans and runs out of registers
 #pragma unroll 1
@@ -903,14 +951,29 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
 // hardware conversion (round to nearest even). Rows past the sequence end
 // fall outside the descriptor and features >= H get an offset beyond it, so
 // the hardware drops those writes. VEC: H % 4 == 0, one vector store.
+__device__ __forceinline__ float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int h0, int H, const f32x4& acc,
-                                        const float4& d4, const float (&uv)[4]) {
+                                        const float4& d4, const float (&uv)[4], const Epi& ep) {
   constexpr int esz = BF16 ? 2 : 4;
-  const f32x4 yv = {fmaf(d4.x, uv[0], acc[0]), fmaf(d4.y, uv[1], acc[1]), fmaf(d4.z, uv[2], acc[2]),
-                    fmaf(d4.w, uv[3], acc[3])};
+  f32x4 yv = {fmaf(d4.x, uv[0], acc[0]), fmaf(d4.y, uv[1], acc[1]), fmaf(d4.z, uv[2], acc[2]),
+              fmaf(d4.w, uv[3], acc[3])};
   if constexpr (VEC) {
     const int off = h0 < H ? (roff + h0) * esz : kBufferOOB;
+    if (ep.accum) {
+      if constexpr (BF16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const auto o = __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0);
+        yv += __builtin_convertvector(__builtin_bit_cast(bf16x4, o), f32x4);
+      } else {
+        yv += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+      }
+    }
+    if (ep.gelu) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) yv[m] = gelu_exact(yv[m]);
+    }
     if constexpr (BF16) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -924,6 +987,14 @@ __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int off = h0 + m < H ? (roff + h0 + m) * esz : kBufferOOB;
+      if (ep.accum) {
+        if constexpr (BF16) {
+          yv[m] += __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(yr, off, 0, 0)) << 16);
+        } else {
+          yv[m] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(yr, off, 0, 0));
+        }
+      }
+      if (ep.gelu) yv[m] = gelu_exact(yv[m]);
       if constexpr (BF16) {
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(yv[m])), yr, off,
                                               0, 0);
@@ -936,7 +1007,7 @@ __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int
 
 __device__ __forceinline__ void load_d(const FusedParams& q, int h0, float (&dv)[4]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) dv[r] = h0 + r < q.H ? q.d[h0 + r] : 0.0f;
+  for (int r = 0; r < 4; ++r) dv[r] = h0 + r < q.H && q.d != nullptr ? q.d[h0 + r] : 0.0f;
 }
 
 // readout operand fragments of K-step s from the x tile: [plane][n]
@@ -971,7 +1042,8 @@ __device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s,
 
 // y for chunk i of the workgroup's streams from the x tile and u tile in LDS
 template <int MPW, int R, bool BF16, bool KEEP, bool VEC>
-__device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rsrc_t yr,
+__device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm,
+                                        const Epi& ep,
                                         const CKeep<MPW, BF16 ? 1 : 2>& ck, const S5_LDS float* s_d,
                                         const lds_byte* xb, const lds_byte* ub, int i, const Lane& ln) {
   constexpr int NP = BF16 ? 1 : 2;
@@ -1002,7 +1074,7 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
       for (int n = 0; n < R; ++n) {
         float uv[4];
         u_for_y<R, BF16>(ub, ht, n, ln, uv);
-        store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], d4, uv);
+        store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], d4, uv, ep);
       }
     }
   } else {
@@ -1059,8 +1131,8 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
         for (int n = 0; n < R; ++n) {
           float uv[4];
           u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n],
-                             make_float4(dv[0], dv[1], dv[2], dv[3]), uv);
+          store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n],
+                             make_float4(dv[0], dv[1], dv[2], dv[3]), uv, ep);
         }
       }
     }
@@ -1071,7 +1143,8 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
 // from u tile i in LDS and D from the LDS table (h-tiles past H: the stores
 // fall outside the descriptor and are dropped)
 template <int R, bool BF16, bool VEC>
-__device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buffer_rsrc_t yr,
+__device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm,
+                                              const Epi& ep,
                                               const float4 (&dk)[kKeepHT], const f32x4 (&yacc)[kKeepHT][R],
                                               const lds_byte* ub, int i, const Lane& ln) {
   float uv[kKeepHT][R][4];
@@ -1084,12 +1157,11 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
     const int h0 = 16 * (ln.w + kWaves * e) + 4 * ln.g;
 #pragma unroll
     for (int n = 0; n < R; ++n)
-      store_y<BF16, VEC>(yr, static_cast<int>(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], dk[e],
-                         uv[e][n]);
+      store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], dk[e], uv[e][n], ep);
   }
 }
 
-template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool ST>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool EXT>
 __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
@@ -1099,6 +1171,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
+  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   const int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
@@ -1136,7 +1210,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);
   if (ln.tid < q.Ppad) {
     cf c = {0.0f, 0.0f};   // the state before step 0: zero, or the caller's
-    if (ST && q.x0 != nullptr && ln.tid < q.P) {
+    if (EXT && q.x0 != nullptr && ln.tid < q.P) {
       const float2 v = q.x0[static_cast<size_t>(b) * q.P + ln.tid];
       c = {v.x, v.y};
     }
@@ -1187,22 +1261,22 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       st[jj][r] = cfma(Ae, ld_pf2(s_c0 + pm), Xe);
     }
   }
-  if (ST && q.xlast != nullptr) {
+  if (EXT && q.xlast != nullptr) {
     const LastTok lt = last_token<R>(q);
     if (qq == lt.qq) write_final_state<R, MPW, TV>(q, b, lt, ln, st);
   }
 
   // ---- chunk pipeline ----
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
-  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
-  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   {
     UStage<NB> ust;
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 0, ust);
     stash_u<R, BF16, NB, kWaves>(q, ust, lds);
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 1, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 1, ust);
     stash_u<R, BF16, NB, kWaves>(q, ust, lds + ut);
   }
   lds_barrier();
@@ -1231,7 +1305,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 #pragma unroll
       for (int n = 0; n < R; ++n) {
         cf a, gn;
-        zoh_step(lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
+        disc_step(bil, lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
         x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
         acc[jj][0][n][r] = x.re;
         acc[jj][1][n][r] = x.im;
@@ -1291,14 +1365,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       // buffer of tile i-1, whose last readers (drive(i-1), readout(i-1))
       // finished before the previous barrier
       UStage<NB> ust;
-      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 2, ust);
+      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 2, ust);
       drive<MPW, R, BF16, KEEP>(q, bk, lds + ui1 * ut, ln.w, ln.l, acc);
       // (before the readout's y stores, so that waiting for the loads does
       // not wait for them)
       const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the drive
       stash_u<R, BF16, NB, kWaves>(q, ust, lds + ui2 * ut);
-      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, ck, mt.d, xb, lds + ui * ut, i, ln);
+      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, rmap, epilogue<EXT>(q), ck, mt.d, xb, lds + ui * ut, i, ln);
       ui = ui1;
     }
   }
@@ -1320,10 +1394,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 
 // carry into the workgroup's range: the totals of the sequence's earlier
 // ranges folded in order (one thread per mode)
-template <bool ST>
+template <bool EXT>
 __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq, int p, S5_LDS pf2* s_c0) {
   cf c = {0.0f, 0.0f};   // the state before step 0: zero, or the caller's
-  if (ST && q.x0 != nullptr && p < q.P) {
+  if (EXT && q.x0 != nullptr && p < q.P) {
     const float2 v = q.x0[static_cast<size_t>(b) * q.P + p];
     c = {v.x, v.y};
   }
@@ -1385,7 +1459,7 @@ __device__ __forceinline__ void stream_start(const FusedParams& q, int bq, const
 // UA: the u fragments of all K-steps come in `ua` (bf16 I/O); otherwise each
 // K-step's fragments are read from the u tile `ub` right before its MFMAs.
 template <int MPW, int JG, int R, bool TV, bool BF16, bool UA>
-__device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk,
+__device__ __forceinline__ void drive_scan_tiles(bool bil, int j0, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk,
                                                  const bf16x8 (&ua)[UA ? kKeepKS : 1][BF16 ? 1 : 2][R],
                                                  const lds_byte* ub, const ModeTable& mt,
                                                  const Lane& ln, const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
@@ -1440,7 +1514,7 @@ __device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW
 #pragma unroll
         for (int n = 0; n < R; ++n) {
           cf a, gn;
-          zoh_step(lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
+          disc_step(bil, lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
           x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
           acc[jj][0][n][r] = x.re;
           acc[jj][1][n][r] = x.im;
@@ -1475,7 +1549,7 @@ __device__ __forceinline__ void drive_scan_tiles(int j0, int KS, const BKeep<MPW
 
 // one chunk of a drive wave, JG mode tiles at a time
 template <int MPW, int R, bool TV, bool BF16>
-__device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk, const lds_byte* ub,
+__device__ __forceinline__ void drive_scan_chunk(bool bil, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk, const lds_byte* ub,
                                                  const ModeTable& mt, const Lane& ln,
                                                  const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
                                                  cf (&st)[MPW][4], lds_byte* xb) {
@@ -1490,10 +1564,10 @@ __device__ __forceinline__ void drive_scan_chunk(int KS, const BKeep<MPW, BF16 ?
     for (int s = 0; s < kKeepKS; ++s) get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, ua[s]);
   }
 #pragma unroll
-  for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16, kOnce>(j0, KS, bk, ua, ub, mt, ln, dl, st, xb);
+  for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16, kOnce>(bil, j0, KS, bk, ua, ub, mt, ln, dl, st, xb);
 }
 
-template <int MPW, int R, bool TV, bool BF16, bool ST>
+template <int MPW, int R, bool TV, bool BF16, bool EXT>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
@@ -1504,6 +1578,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   const int bq = blockIdx.x;
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
+  const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
+  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
   const int KS = q.Hpad >> 5;
   const int HT = q.Hpad >> 4;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
@@ -1515,11 +1591,11 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   lds_byte* xlds = lds + 3 * ut;
   const ModeTable mt = fill_mode_table<TV>(q, lds + 3 * ut + 2 * xt, true);
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
-  if (driver && ln.tid < q.Ppad) range_carry<ST>(q, b, qq, ln.tid, s_c0);
+  if (driver && ln.tid < q.Ppad) range_carry<EXT>(q, b, qq, ln.tid, s_c0);
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
-  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq);
-  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq);
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
   // one register array holds the role's weights: B_bar fragments [s][jj][cc][pl]
   // in drive waves, C' fragments [e][s][pl] in readout waves (16 MPW NP each)
   static_assert(sizeof(BKeep<MPW, NP>) == sizeof(CKeep<MPW, NP>), "both roles hold 16 MPW NP fragments");
@@ -1550,9 +1626,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   constexpr bool VEC = decltype(vec_c)::value;
   if (!driver) {
     UStage<NB> ust;
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 0, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 0, ust);
     stash_u<R, BF16, NB, kWaves>(q, ust, lds);
-    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, 1, ust);
+    fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 1, ust);
     stash_u<R, BF16, NB, kWaves>(q, ust, lds + ut);
   }
   lds_barrier();   // carry, mode table, u tiles 0 and 1
@@ -1565,12 +1641,12 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   float4 dl[TV ? MPW : 1][TV ? R : 1];
   if (driver) {
     stream_start<MPW, TV>(q, bq, ln, s_c0, st);
-    if (ST && q.xlast != nullptr) {
+    if (EXT && q.xlast != nullptr) {
       const LastTok lt = last_token<R>(q);
       if (qq == lt.qq) write_final_state<R, MPW, TV>(q, b, lt, ln, st);
     }
     if constexpr (TV) load_delta<MPW, R>(q, b, qq, 0, ln, dl);
-    drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds, mt, ln, dl, st, xlds);
+    drive_scan_chunk<MPW, R, TV, BF16>(EXT && q.bilinear, KS, wts.b, lds, mt, ln, dl, st, xlds);
   }
   lds_barrier();   // x tile 0
 
@@ -1584,7 +1660,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       const int ui1 = ui == 2 ? 0 : ui + 1;
       if (i + 1 < q.nck) {
         if constexpr (TV) load_delta<MPW, R>(q, b, qq, i + 1, ln, dl);
-        drive_scan_chunk<MPW, R, TV, BF16>(KS, wts.b, lds + ui1 * ut, mt, ln, dl, st, xlds + ((i + 1) & 1) * xt);
+        drive_scan_chunk<MPW, R, TV, BF16>(EXT && q.bilinear, KS, wts.b, lds + ui1 * ut, mt, ln, dl, st, xlds + ((i + 1) & 1) * xt);
       }
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
       ui = ui1;
@@ -1597,7 +1673,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // u tile i+2 into registers now, into LDS after this chunk's MFMAs
       // (not carried across iterations: no register shuffles, no early wait)
       UStage<NB> ust2;
-      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, qq, i + 2, ust2);
+      fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 2, ust2);
       const lds_byte* xr = xlds + (i & 1) * xt;
       f32x4 yacc[kKeepHT][R];
 #pragma unroll
@@ -1626,7 +1702,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // y stores, so that waiting for the loads does not wait for them
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
       stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
-      readout_store<R, BF16, VEC>(q, yrsrc, dk, yacc, lds + ui * ut, i, ln);
+      readout_store<R, BF16, VEC>(q, yrsrc, rmap, epilogue<EXT>(q), dk, yacc, lds + ui * ut, i, ln);
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
       ui = ui1;
     }
@@ -1651,12 +1727,13 @@ hipError_t launch_one(int blocks, int threads, size_t lds, hipStream_t s, const 
   return hipGetLastError();
 }
 
-// ST: instances that take an initial state or return the final one; the
-// stateless calls run kernels with that code compiled out
+// EXT: instances with the options of the extended entry point (initial and
+// final state, reverse time, accumulate into y, GELU, bilinear steps); the
+// plain calls run kernels with that code compiled out
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
-  const bool st = q.x0 != nullptr || q.xlast != nullptr;
+  const bool st = q.x0 != nullptr || q.xlast != nullptr || q.rev || q.accum || q.gelu || (q.bilinear && TV);
   if constexpr (KEEP) {
     return st ? launch_one<k_reduce_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q)
               : launch_one<k_reduce_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
@@ -1669,7 +1746,7 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
-  const bool st = q.x0 != nullptr || q.xlast != nullptr;
+  const bool st = q.x0 != nullptr || q.xlast != nullptr || q.rev || q.accum || q.gelu || (q.bilinear && TV);
   if constexpr (KEEP) {
     return st ? launch_one<k_scan_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_scan, s, q)
               : launch_one<k_scan_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_scan, s, q);

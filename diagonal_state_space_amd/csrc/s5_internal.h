@@ -22,12 +22,19 @@ struct ForwardArgs {
   const float2* lam;
   const float2* b_tilde;
   const float2* c_tilde;
-  const float* d;
+  const float* d;          // [H], or null (no feedthrough)
   const float* log_delta;  // time-invariant
   const float* delta;      // time-varying [B, L, P]
   void* y;
   const float2* x0 = nullptr;   // [B, P] state before step 0 (null: zero)
   float2* xlast = nullptr;      // [B, P] out: state after step L-1 (null: not written)
+  int c_ld = 0;                 // row stride of c_tilde (0: P)
+  int c_off = 0;                // first column of c_tilde read
+  float c_scale = 1.0f;         // readout factor (2: half-spectrum storage)
+  bool bilinear = false;        // bilinear discretisation
+  bool rev = false;             // reverse time (the backward scan)
+  bool accum = false;           // add the result to y
+  bool gelu = false;            // GELU of the final y
 };
 
 // Bytes of stream-ordered scratch the forward path needs for these sizes.

@@ -1,6 +1,7 @@
-// Parameter packing for the fused S5 forward kernels: zero-order-hold
-// discretisation in float64 (paper eq. 6; App. A `discretize`; abhik.ai
-// review, row 2), the MFMA operand layouts of B_bar and C', and the per-mode
+// Parameter packing for the fused S5 forward kernels: discretisation in
+// float64 (zero-order hold: paper eq. 6, App. A `discretize`, abhik.ai review
+// row 2; or bilinear: intuitivepapers S4 notes, "Discretization and the step
+// size"), the MFMA operand layouts of B_bar and C', and the per-mode
 // constants.
 #include "s5_common.h"
 #include "s5_fused.h"
@@ -42,6 +43,14 @@ __device__ zd gain64(zd lam, double delta) {
   return zdiv({e.re - 1.0, e.im}, lam);
 }
 
+__device__ __forceinline__ zd zlog(zd z) { return {log(sqrt(z.re * z.re + z.im * z.im)), atan2(z.im, z.re)}; }
+
+// bilinear map of one mode: z = lambda*delta, Lambda_bar = (1 + z/2)/(1 - z/2)
+// = 2 w - 1 and gain = delta w, with w = 1/(1 - z/2)
+__device__ zd bilinear_w64(zd lam, double delta) {
+  return zdiv({1.0, 0.0}, {1.0 - 0.5 * lam.re * delta, -0.5 * lam.im * delta});
+}
+
 __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int KS = q.Hpad / 32;
   const int K2 = 2 * q.Ppad / 32;
@@ -62,7 +71,17 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       zd g = {0.0, 0.0};
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
-        g = q.time_varying ? zd{1.0, 0.0} : gain64(lam, exp(static_cast<double>(q.log_delta[p])));
+        if (!q.time_varying) {
+          const double dt = exp(static_cast<double>(q.log_delta[p]));
+          if (q.bilinear) {
+            const zd w = bilinear_w64(lam, dt);
+            g = {dt * w.re, dt * w.im};
+          } else {
+            g = gain64(lam, dt);
+          }
+        } else {
+          g = {1.0, 0.0};
+        }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -92,8 +111,8 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         const int p = k >> 1;
         float val = 0.0f;
         if (h < q.H && p < q.P) {
-          const float2 ct = q.c_tilde[static_cast<size_t>(h) * q.P + p];
-          val = (k & 1) ? -ct.y : ct.x;
+          const float2 ct = q.c_tilde[static_cast<size_t>(h) * q.c_ld + q.c_off + p];
+          val = q.c_scale * ((k & 1) ? -ct.y : ct.x);
         }
         v[i] = val;
       }
@@ -109,7 +128,12 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
         if (!q.time_varying) {
           const double dt = exp(static_cast<double>(q.log_delta[p]));
-          const zd z = {lam.re * dt, lam.im * dt};
+          // log of Lambda_bar: z itself for zero-order hold
+          zd z = {lam.re * dt, lam.im * dt};
+          if (q.bilinear) {
+            const zd w = bilinear_w64(lam, dt);
+            z = zlog({2.0 * w.re - 1.0, 2.0 * w.im});
+          }
           const zd a = zexp(z);
           const zd as = zexp({z.re * q.Lseg, z.im * q.Lseg});
           mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));

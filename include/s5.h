@@ -174,6 +174,70 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
                                           const s5_c64* c_tilde, const float* d, const float* delta,
                                           const s5_c64* x0, void* y, s5_c64* x_last, hipStream_t stream);
 
+/*
+ * s5_forward_ex - the forward pass with its options, described by one struct
+ * (all entry points above are special cases of it).
+ *
+ * Options (desc->flags, any combination unless noted):
+ *   S5_FLAG_HALF_SPECTRUM  the P stored modes are one partner of each
+ *       conjugate pair: y_k = 2 Re(C~ x_k) + D u_k, the feedthrough not
+ *       doubled (abhik.ai review, row 4 "Reconstruct real outputs and keep
+ *       the direct path"; wikillm notes, "Paper vs code", readout factor 2).
+ *   S5_FLAG_BILINEAR  bilinear discretisation instead of zero-order hold:
+ *       with z = Lambda*Delta, Lambda_bar = (1 + z/2)/(1 - z/2) and
+ *       B_bar = Delta/(1 - z/2) * B~ (intuitivepapers S4 notes,
+ *       "Discretization and the step size"; abhik.ai review: the official
+ *       code offers it as an alternative). Time-invariant or time-varying.
+ *   S5_FLAG_GELU  y is GELU of the pre-activation, y * Phi(y) with the
+ *       standard normal distribution function Phi (exact form, float32;
+ *       papercache notes App. A `apply_S5_layer`).
+ *   S5_FLAG_BIDIRECTIONAL  a second, backward scan over the same Lambda_bar
+ *       and B_bar, x'_k = Lambda_bar x'_{k+1} + B_bar u_k from x'_L = 0,
+ *       read out by the second half of C~, which then has 2P columns:
+ *       y_k = Re(C~[:, :P] x_k) + Re(C~[:, P:] x'_k) + D u_k (wikillm
+ *       notes, "Paper vs code", bidirectional scans). Time-invariant only,
+ *       without x0/x_last. For bf16 io the forward half of y is rounded to
+ *       bf16 once before the backward half is added.
+ *
+ * Fields of s5_forward_desc:
+ *   size        sizeof(s5_forward_desc) (for later extension)
+ *   flags       S5_FLAG_* bits; unknown bits are rejected
+ *   io, B, L, H, P, u, lambda, b_tilde, d, y   as s5_forward
+ *   c_tilde     [H,P], or [H,2P] with S5_FLAG_BIDIRECTIONAL
+ *   log_delta   [P] per-mode log interval (time-invariant), or NULL
+ *   delta       [B,L,P] per-step interval (time-varying), or NULL;
+ *               exactly one of log_delta and delta is given
+ *   x0, x_last  as s5_forward_stateful (NULL: zero / not written)
+ * Errors: as s5_forward_stateful; S5_ERR_INVALID_ARGUMENT for a wrong size
+ * field, unknown flags, both or neither interval arrays, or
+ * S5_FLAG_BIDIRECTIONAL with delta, x0 or x_last.
+ */
+enum {
+  S5_FLAG_HALF_SPECTRUM = 1u << 0,
+  S5_FLAG_BILINEAR = 1u << 1,
+  S5_FLAG_GELU = 1u << 2,
+  S5_FLAG_BIDIRECTIONAL = 1u << 3
+};
+
+typedef struct {
+  uint32_t size;
+  uint32_t flags;
+  s5_dtype io;
+  int64_t B, L, H, P;
+  const void* u;
+  const s5_c64* lambda;
+  const s5_c64* b_tilde;
+  const s5_c64* c_tilde;
+  const float* d;
+  const float* log_delta;
+  const float* delta;
+  const s5_c64* x0;
+  void* y;
+  s5_c64* x_last;
+} s5_forward_desc;
+
+s5_status s5_forward_ex(const s5_forward_desc* desc, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* s5_status_string(s5_status s);
 

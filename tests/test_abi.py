@@ -163,3 +163,31 @@ def test_stateful_validation(tv):
     assert _fwd_state(B=-1, tv=tv) == INVALID
     assert _fwd_state(B=0, tv=tv) == OK                              # nothing to do
     assert _fwd_state(L=0, x0=None, xl=None, tv=tv) == OK           # nothing asked for
+
+
+def _fwd_ex(flags=0, B=2, L=8, H=4, P=3, io=0, ct=FAKE + 0x3000, logd=FAKE + 0x5000, delta=None,
+            x0=None, x_last=None, y=FAKE + 0x100000, size=None):
+    desc = s5.ForwardDesc(ctypes.sizeof(s5.ForwardDesc) if size is None else size, flags, io, B, L, H, P,
+                          FAKE, FAKE + 0x1000, FAKE + 0x2000, ct, FAKE + 0x4000, logd, delta, x0, y, x_last)
+    return s5.lib().s5_forward_ex(ctypes.byref(desc), None)
+
+
+def test_forward_ex_validation():
+    assert s5.lib().s5_forward_ex(None, None) == INVALID
+    assert _fwd_ex(size=64) == INVALID                                   # wrong struct size
+    assert _fwd_ex(flags=1 << 7) == INVALID                              # unknown option bit
+    assert _fwd_ex(logd=None) == INVALID                                 # no intervals
+    assert _fwd_ex(delta=FAKE + 0x6000) == INVALID                       # both kinds of intervals
+    bidir = s5.FLAG_BIDIRECTIONAL
+    assert _fwd_ex(flags=bidir, logd=None, delta=FAKE + 0x6000) == INVALID   # backward scan: time-invariant
+    assert _fwd_ex(flags=bidir, x0=FAKE + 0x7000) == INVALID             # ... and stateless
+    assert _fwd_ex(flags=bidir, x_last=FAKE + 0x7000) == INVALID
+    # C~ of 2P columns ending inside y (P columns would end before it)
+    H, P = 4, 3
+    y = FAKE + 0x100000
+    ct = y - H * P * 8 - 16
+    assert _fwd_ex(flags=bidir, ct=ct, y=y) == INVALID
+    assert _fwd_ex(flags=bidir, ct=FAKE + 0x3004) == UNSUPPORTED         # misaligned
+    assert _fwd_ex(flags=bidir | s5.FLAG_GELU | s5.FLAG_HALF_SPECTRUM, B=0) == OK   # empty: no-op
+    assert _fwd_ex(flags=s5.FLAG_BILINEAR, L=0) == OK
+    assert _fwd_ex(P=0) == INVALID and _fwd_ex(H=1000) == UNSUPPORTED

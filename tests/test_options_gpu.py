@@ -1,0 +1,167 @@
+"""GPU parity of the forward pass's options (s5_forward_ex) against the
+float64 oracle's forward_ex, through the C ABI: half-spectrum readout,
+bilinear discretisation, GELU epilogue, bidirectional scans, and their
+combinations with each other and with the initial/final state.
+
+Bounds as test_parity_gpu: max |y_gpu - y_oracle| / rms(y_oracle) <= 2e-4
+for float32 I/O; for bf16 I/O the excess over the bf16 output rounding
+(2^-8 |y|) <= 2e-2 of rms. The bidirectional form rounds the forward half of
+y to bf16 once before adding the backward half: for bf16 I/O that rounding
+(at most 2^-9 of the forward half, times GELU's largest slope when the
+epilogue follows) is excluded from the excess like the output's own.
+Final states: <= the same fraction of rms(x)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.s5_oracle as orc
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diagonal_state_space_amd  # noqa: F401  (fails loudly if libs5.so is missing)
+
+
+def _c_tilde2(H, P, seed):
+    """[H, 2P] output matrix of the bidirectional form (complex N(0, 1/H)),
+    rounded to complex64 as the GPU receives it."""
+    rng = np.random.default_rng(seed)
+    c = (rng.normal(size=(H, 2 * P)) + 1j * rng.normal(size=(H, 2 * P))) / math.sqrt(2 * H)
+    return c.astype(np.complex64)
+
+
+# largest slope of GELU (at about x = 2.4): bounds how far it moves a rounding
+GELU_MAX_SLOPE = 1.13
+
+
+def _y_err(io, y, yo, y_first=None, gelu=False):
+    """max excess / rms(y_oracle); bf16: the excess over the output's own
+    rounding and, for the bidirectional form, over the one bf16 rounding of
+    the forward half ``y_first`` (oracle values) before the backward half is
+    added (carried through the GELU epilogue's slope)."""
+    yg = y.float().cpu().numpy().astype(np.float64)
+    rms = math.sqrt(float(np.mean(yo ** 2)))
+    excess = np.abs(yg - yo)
+    if io == "bf16":
+        excess = excess - BF16_UNIT_ROUNDOFF * np.abs(yo)
+        if y_first is not None:
+            excess = excess - 0.5 * BF16_UNIT_ROUNDOFF * np.abs(y_first) * (GELU_MAX_SLOPE if gelu else 1.0)
+    return float(np.max(excess)) / rms
+
+
+def _x_err(xg, xo):
+    xg = xg.cpu().numpy().astype(np.complex128)
+    rms = math.sqrt(float(np.mean(np.abs(xo) ** 2)))
+    return float(np.max(np.abs(xg - xo))) / rms
+
+
+def _run(w, opts, c2=None, x0=None):
+    import diagonal_state_space_amd as s5
+    cuda = torch.device("cuda:0")
+    if w.io == "bf16":
+        u = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(cuda)
+    else:
+        u = torch.from_numpy(w.u).to(cuda)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(cuda)
+           for k in ("lam", "b_tilde", "c_tilde", "d", "log_delta")}
+    ct = torch.from_numpy(c2).to(cuda) if c2 is not None else dev["c_tilde"]
+    kw = {}
+    if w.time_varying:
+        kw["delta"] = torch.from_numpy(w.delta).to(cuda)
+    else:
+        kw["log_delta"] = dev["log_delta"]
+    x0d = None if x0 is None else torch.from_numpy(x0.astype(np.complex64)).to(cuda)
+    y, xl = s5.forward_ex(u, dev["lam"], dev["b_tilde"], ct, dev["d"], x0=x0d,
+                          final_state=opts.get("state", False), half_spectrum=opts.get("half", False),
+                          bilinear=opts.get("bilinear", False), gelu=opts.get("gelu", False),
+                          bidirectional=opts.get("bidir", False), **kw)
+    torch.cuda.synchronize()
+    return y, xl
+
+
+def _oracle(w, opts, c2=None, x0=None):
+    kw = {"delta": w.delta} if w.time_varying else {"log_delta": w.log_delta}
+    return orc.forward_ex(w.u, w.lam, w.b_tilde, c2 if c2 is not None else w.c_tilde, w.d, x0=x0,
+                          conj_sym=opts.get("half", False), method="bilinear" if opts.get("bilinear") else "zoh",
+                          activation="gelu" if opts.get("gelu") else None,
+                          bidirectional=opts.get("bidir", False), **kw)
+
+
+CASES = [
+    # (B, L, H, P, io, tv), options
+    ((2, 300, 24, 40, "f32", False), {"half": True}),
+    ((2, 1000, 128, 256, "bf16", False), {"half": True}),
+    ((2, 513, 96, 128, "f32", True), {"half": True}),
+    ((2, 700, 64, 64, "f32", False), {"bilinear": True}),
+    ((1, 5001, 128, 256, "bf16", False), {"bilinear": True}),
+    ((2, 513, 96, 128, "f32", True), {"bilinear": True}),
+    ((2, 4097, 128, 256, "bf16", True), {"bilinear": True}),
+    ((2, 800, 64, 64, "f32", False), {"bilinear": True, "state": True}),
+    ((2, 513, 96, 128, "f32", True), {"bilinear": True, "state": True}),
+    ((2, 300, 24, 40, "f32", False), {"gelu": True}),
+    ((2, 1000, 128, 256, "bf16", False), {"gelu": True}),
+    ((2, 513, 96, 128, "f32", True), {"gelu": True, "state": True}),
+    ((1, 1, 5, 3, "f32", False), {"bidir": True}),
+    ((2, 97, 24, 40, "f32", False), {"bidir": True}),
+    ((2, 97, 24, 40, "bf16", False), {"bidir": True}),
+    ((2, 1000, 256, 192, "f32", False), {"bidir": True}),           # four-wave kernels
+    ((1, 5001, 128, 256, "bf16", False), {"bidir": True}),          # many ranges, ragged end
+    ((2, 3000, 128, 128, "bf16", False), {"bidir": True, "half": True, "gelu": True, "bilinear": True}),
+    ((2, 2000, 96, 128, "f32", False), {"bidir": True, "gelu": True}),
+]
+
+
+def _name(case):
+    (B, L, H, P, io, tv), o = case
+    return f"B{B}_L{L}_H{H}_P{P}_{io}{'_tv' if tv else ''}_" + "+".join(sorted(k for k, v in o.items() if v))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_name(c) for c in CASES])
+def test_option_parity(case):
+    (B, L, H, P, io, tv), opts = case
+    w = wl.make_random(B, L, H, P, io=io, tv=tv, seed=101 + L + P, kind="random_walk" if tv else "normal")
+    c2 = _c_tilde2(H, P, seed=L) if opts.get("bidir") else None
+    x0 = None
+    if opts.get("state"):
+        rng = np.random.default_rng(P)
+        x0 = (rng.normal(size=(B, P)) + 1j * rng.normal(size=(B, P))) * 0.5
+    print(f"[options] {_name(case)}", flush=True)
+    y, xl = _run(w, opts, c2, x0)
+    yo, xo = _oracle(w, opts, c2, x0)
+    y_first = None
+    if opts.get("bidir") and io == "bf16":
+        first = dict(opts, bidir=False, gelu=False)
+        y_first, _ = _oracle(w, first, np.ascontiguousarray(c2[:, :P]), None)
+    ey = _y_err(io, y, yo, y_first, opts.get("gelu", False))
+    msg = f"[options]   y {ey:.3e} (tol {w.tol:.0e})"
+    if opts.get("state"):
+        ex = _x_err(xl, xo)
+        msg += f"  x_last {ex:.3e}"
+        assert ex <= w.tol
+    print(msg, flush=True)
+    assert ey <= w.tol
+
+
+def test_plain_options_match_plain_entry_point():
+    """forward_ex with no options gives the bits of s5_forward."""
+    import diagonal_state_space_amd as s5
+    w = wl.make_random(2, 1000, 128, 256, io="bf16", seed=3)
+    cuda = torch.device("cuda:0")
+    u = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(cuda)
+    t = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(cuda)
+         for k in ("lam", "b_tilde", "c_tilde", "d", "log_delta")}
+    y1 = s5.forward(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["log_delta"])
+    y2, _ = s5.forward_ex(u, t["lam"], t["b_tilde"], t["c_tilde"], t["d"], log_delta=t["log_delta"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
