@@ -18,6 +18,11 @@ Prints one JSON line with the contract fields plus
                 summed duration of the three launches
   cpu_baseline  the float64 oracle timed on this host's cores
   parity        max |y - y_oracle| / rms(y_oracle) of the benchmark's output
+
+--variant times the same workload through s5_forward_ex with one option
+(initial/final state, half spectrum, bilinear, GELU, bidirectional) or as a
+stream of chunks with the state carried between calls (chunked:C); those
+lines carry the timing only (no roofline, kernels or cpu_baseline).
 """
 
 from __future__ import annotations
@@ -156,6 +161,82 @@ def cpu_baseline(w, repeats: int, budget_s: float):
                       f"run(s), {t:.2f} s each"}, y
 
 
+def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_sets) -> int:
+    """Time one option of s5_forward_ex, or chunked streaming, on the workload."""
+    v = args.variant
+    B, P = w.B, w.P
+    x0 = torch.zeros(B, P, dtype=torch.complex64, device=lam.device)
+    xl = torch.empty_like(x0)
+    if v == "bidir":
+        ct_run = torch.cat([ct, ct.conj()], dim=1).contiguous()
+    else:
+        ct_run = ct
+    opts = {"stateful": {}, "half": {"half_spectrum": True}, "bilinear": {"bilinear": True},
+            "gelu": {"gelu": True}, "bidir": {"bidirectional": True}}
+    chunk = int(v.split(":")[1]) if v.startswith("chunked:") else 0
+    if chunk:
+        if w.L % chunk:
+            print("chunk must divide L", file=sys.stderr)
+            return 2
+        n_ck = w.L // chunk
+        ucs = [[us[k][:, j * chunk:(j + 1) * chunk].contiguous() for j in range(n_ck)] for k in range(n_sets)]
+        ycs = [[torch.empty_like(ucs[0][0]) for _ in range(n_ck)] for _ in range(n_sets)]
+        dcs = ([[deltas[k][:, j * chunk:(j + 1) * chunk].contiguous() for j in range(n_ck)]
+                for k in range(n_sets)] if w.time_varying else None)
+        xs = [x0, xl]
+    elif v not in opts:
+        print(f"unknown variant {v}", file=sys.stderr)
+        return 2
+
+    def step(i):
+        k = i % n_sets
+        if chunk:
+            for j in range(n_ck):
+                kw = {"delta": dcs[k][j]} if w.time_varying else {"log_delta": logd}
+                s5.forward_ex(ucs[k][j], lam, bt, ct, d, x0=xs[j & 1], x_last=xs[(j + 1) & 1],
+                              y=ycs[k][j], **kw)
+            return
+        kw = {"delta": deltas[k]} if w.time_varying else {"log_delta": logd}
+        extra = {"x0": x0, "x_last": xl} if v == "stateful" else {}
+        s5.forward_ex(us[k], lam, bt, ct_run, d, y=ys[k], **kw, **extra, **opts[v])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernels = None
+    if not chunk:
+        # HIP events around the first three launches of each call (packing,
+        # aggregate pass, state and output pass: the forward half for bidir)
+        ev = HipEvents()
+        evs = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            s5.set_profiling_events(evs[i])
+            step(args.warmup + args.steps + i)
+        torch.cuda.synchronize()
+        s5.set_profiling_events(None)
+        ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(3)] for e in evs]).mean(axis=0)
+        for e in evs:
+            for h in e:
+                ev.destroy(h)
+        kernels = {"pack_us": round(float(ms[0]) * 1e3, 2), "reduce_us": round(float(ms[1]) * 1e3, 2),
+                   "scan_us": round(float(ms[2]) * 1e3, 2)}
+    workload = (f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
+                f"{'_timevarying' if w.time_varying else ''}")
+    print(json.dumps({"metric": METRIC, "kernels": kernels, "value": round(w.B * w.L / (ms_per_step * 1e-3), 1),
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+                      "dtype": w.io, "data": "synthetic",
+                      "config": {"workload": workload, "variant": v, "buffer_sets": n_sets}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +246,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--variant", default="plain",
+                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -213,6 +296,9 @@ def main() -> int:
             s5.forward_timevarying(us[k], lam, bt, ct, d, deltas[k], y=ys[k])
         else:
             s5.forward(us[k], lam, bt, ct, d, logd, y=ys[k])
+
+    if args.variant != "plain":
+        return bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_sets)
 
     for i in range(args.warmup):
         step(i)

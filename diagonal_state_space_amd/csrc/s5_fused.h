@@ -37,6 +37,8 @@ struct ModeParams {
   float2 aseg;     // exp(Lseg lambda Delta): one whole stream   (time-invariant)
   float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval
   float pad_;
+  float2 alast;    // abar^m, m = ((L-1) mod Lseg) + 1: the stream holding token
+                   // L-1, from its first token through L-1  (time-invariant)
 };
 
 // One forward call, as the kernels see it.

@@ -184,13 +184,12 @@ __device__ __forceinline__ void record_partial(const FusedParams& q, int b, int 
 
 // pass 2, in the lanes of stream lt.t of range lt.qq right after their start
 // state is known: the state after token L-1 for the lane's modes. The
-// time-invariant transition over the m steps is Lambda_bar^m, in float64.
+// time-invariant transition over the m steps is Lambda_bar^m (packed in float64).
 template <int R, int MPW, bool TV>
 __device__ __forceinline__ void write_final_state(const FusedParams& q, int b, const LastTok& lt, const Lane& ln,
                                                   const cf (&st)[MPW][4]) {
   if (ln.t != lt.t) return;
   const float2* c = q.cap + static_cast<size_t>(b) * 2 * q.Ppad;
-  const double m = static_cast<double>(lt.i * R + lt.n + 1);
 #pragma unroll
   for (int jj = 0; jj < MPW; ++jj)
 #pragma unroll
@@ -202,20 +201,8 @@ __device__ __forceinline__ void write_final_state(const FusedParams& q, int b, c
       if constexpr (TV) {
         A = {c[q.Ppad + pm].x, c[q.Ppad + pm].y};
       } else {
-        // Lambda_bar^m = exp(m log Lambda_bar); log Lambda_bar = lambda Delta
-        // for zero-order hold
-        const double dt = exp(static_cast<double>(q.log_delta[pm]));
-        double zr = static_cast<double>(q.lam[pm].x) * dt, zi = static_cast<double>(q.lam[pm].y) * dt;
-        if (q.bilinear) {
-          const double br = 1.0 - 0.5 * zr, bi = -0.5 * zi, den = br * br + bi * bi;
-          const double ar = 2.0 * br / den - 1.0, ai = 2.0 * -bi / den;
-          zr = 0.5 * log(ar * ar + ai * ai);
-          zi = atan2(ai, ar);
-        }
-        const double mag = exp(zr * m);
-        double sn, cs;
-        sincos(zi * m, &sn, &cs);
-        A = {static_cast<float>(mag * cs), static_cast<float>(mag * sn)};
+        const float2 al = q.modes[pm].alast;   // abar^m, from the float64 packing
+        A = {al.x, al.y};
       }
       const cf x = cfma(A, st[jj][r], X);
       q.xlast[static_cast<size_t>(b) * q.P + pm] = make_float2(x.re, x.im);
@@ -266,8 +253,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, cons
   const int tok0 = qq * kStreams * q.Lseg;
   const int rows = min(q.L - tok0, kStreams * q.Lseg);
   const size_t row0 = rev ? static_cast<size_t>(b) * q.L + (q.L - tok0 - rows) : range_row0(q, b, qq);
-  const char* base = static_cast<const char*>(t) + row0 * q.H * esz;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * q.H * esz, kBufferWord3);
+  // The fields are workgroup-uniform; reading them from the first lane tells
+  // the compiler so (where it cannot prove it, every buffer access would be
+  // wrapped in a loop over the distinct descriptors of the wave's lanes).
+  const uint64_t a = reinterpret_cast<uint64_t>(static_cast<const char*>(t) + row0 * q.H * esz);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int nbytes = __builtin_amdgcn_readfirstlane(rows * q.H * esz);
+  char* base = reinterpret_cast<char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, kBufferWord3);
 }
 
 // Memory row, relative to the range descriptor's base, of relative token row
@@ -283,21 +277,27 @@ struct RowMap {
   }
 };
 
-template <bool EXT>
+template <bool REV>
 __device__ __forceinline__ RowMap row_map(const FusedParams& q, int qq) {
-  if (EXT && q.rev) return {true, min(q.L - qq * kStreams * q.Lseg, kStreams * q.Lseg) - 1};
+  if (REV && q.rev) return {true, min(q.L - qq * kStreams * q.Lseg, kStreams * q.Lseg) - 1};
   return {false, 0};
 }
 
-// epilogue options of the extended instances: add to y, GELU
+// Output epilogue by instance: XM = 2 always GELU; XM = 3 adds to y (the
+// backward scan of the bidirectional form), then GELU if asked. The addition
+// reads y in the store path; a load there behind a runtime test would make
+// the compiler wait for every outstanding load (the prefetched u tiles) at
+// the merge, so it is compiled only where every call adds. Runtime tests in
+// the store path also split the readout loop's scheduling regions, so the
+// plain and state-only instances have none.
 struct Epi {
   bool accum;
   bool gelu;
 };
 
-template <bool EXT>
+template <int XM>
 __device__ __forceinline__ Epi epilogue(const FusedParams& q) {
-  return {EXT && q.accum != 0, EXT && q.gelu != 0};
+  return {XM == 3, XM == 2 || (XM == 3 && q.gelu != 0)};
 }
 
 template <int R, bool BF16, int NB, int NWV, bool VEC>
@@ -552,8 +552,9 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
 // ---- pass 1 --------------------------------------------------------------------------
 
 // MPW: mode tiles per wave (Ppad = 64 MPW); R: tokens per stream per chunk.
-template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool EXT>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, int XM>
 __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
+  constexpr bool EXT = XM != 0;   // options of the extended entry point
   constexpr int NP = BF16 ? 1 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
   if (q.Ppad != 64 * MPW || q.R != R) return;   // dispatch mismatch: do nothing
@@ -693,8 +694,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 // Wave w (0..7) owns mode tiles j = w + 8 jj (j < 4 MPW): half the weights
 // and states of a four-wave split, so two waves fit on each SIMD and one
 // wave's scan overlaps the other's MFMAs. All waves share each u tile.
-template <int MPW, int R, bool TV, bool BF16, bool EXT>
+template <int MPW, int R, bool TV, bool BF16, int XM>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
+  constexpr bool EXT = XM != 0;   // options of the extended entry point
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int NW8 = 2 * kWaves;
   constexpr int NT = 4 * MPW;                 // mode tiles
@@ -799,10 +801,13 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
           }
     }
   };
-  // the stream states through one chunk's drive
-  auto scan = [&](int i, const f32x4 (&acc)[M8][2][R], const float4 (&dl)[TV ? M8 : 1][TV ? R : 1])
-      __attribute__((always_inline)) {
-    const bool rec = cap_chunk == i;   // this chunk holds token L-1 (uniform)
+  // the stream states through one chunk's drive; rec: the chunk holding token
+  // L-1. Time-invariant: a separate copy for that chunk (rec_c), so that the
+  // others test nothing per step; time-varying: a runtime test (rec_rt), which
+  // measured faster there than the second copy.
+  auto scan = [&](auto rec_c, bool rec_rt, const f32x4 (&acc)[M8][2][R],
+                  const float4 (&dl)[TV ? M8 : 1][TV ? R : 1]) __attribute__((always_inline)) {
+    const bool rec = decltype(rec_c)::value || rec_rt;
 #pragma unroll
     for (int m = 0; m < M8; ++m) {
       const int j = ln.w + NW8 * m;
@@ -866,7 +871,13 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         float4 dl[TV ? M8 : 1][TV ? R : 1];
         delta(i0 + c, dl);
         mma(lds + (half * G + c) * ut, acc);
-        scan(i0 + c, acc, dl);
+        if constexpr (TV) {
+          scan(std::false_type{}, EXT && cap_chunk == i0 + c, acc, dl);
+        } else if (EXT && cap_chunk == i0 + c) {
+          scan(std::true_type{}, false, acc, dl);
+        } else {
+          scan(std::false_type{}, false, acc, dl);
+        }
       }
       // the next group's tiles into the other half (read by the previous group
       // before the last barrier)
@@ -951,7 +962,21 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
 // hardware conversion (round to nearest even). Rows past the sequence end
 // fall outside the descriptor and features >= H get an offset beyond it, so
 // the hardware drops those writes. VEC: H % 4 == 0, one vector store.
-__device__ __forceinline__ float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+// GELU(v) = v Phi(v), Phi the standard normal distribution function, with
+// erf from Abramowitz & Stegun's formula 7.1.26 (Handbook of Mathematical
+// Functions): for z >= 0, erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// exp(-z^2), t = 1/(1 + p z), absolute error below 1.5e-7. With z = |v|/sqrt2,
+// Phi(|v|) = 1 - q/2 and Phi(-|v|) = q/2 for q = 1 - erf(z). Branch-free.
+__device__ __forceinline__ float gelu_exact(float v) {
+  const float z = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float half_q = 0.5f * t * poly * __expf(-z * z);
+  return v * (v >= 0.0f ? 1.0f - half_q : half_q);
+}
 
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int h0, int H, const f32x4& acc,
@@ -1161,8 +1186,9 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
   }
 }
 
-template <int MPW, int R, bool TV, bool BF16, bool KEEP, bool EXT>
+template <int MPW, int R, bool TV, bool BF16, bool KEEP, int XM>
 __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
+  constexpr bool EXT = XM != 0;   // options of the extended entry point
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1172,7 +1198,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
   const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
-  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
+  const RowMap rmap = row_map<XM == 3>(q, qq);   // forward or reverse time
   const int KS = q.Hpad >> 5;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   const int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
@@ -1372,7 +1398,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the drive
       stash_u<R, BF16, NB, kWaves>(q, ust, lds + ui2 * ut);
-      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, rmap, epilogue<EXT>(q), ck, mt.d, xb, lds + ui * ut, i, ln);
+      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, rmap, epilogue<XM>(q), ck, mt.d, xb, lds + ui * ut, i, ln);
       ui = ui1;
     }
   }
@@ -1567,8 +1593,9 @@ __device__ __forceinline__ void drive_scan_chunk(bool bil, int KS, const BKeep<M
   for (int j0 = 0; j0 < MPW; j0 += JG) drive_scan_tiles<MPW, JG, R, TV, BF16, kOnce>(bil, j0, KS, bk, ua, ub, mt, ln, dl, st, xb);
 }
 
-template <int MPW, int R, bool TV, bool BF16, bool EXT>
+template <int MPW, int R, bool TV, bool BF16, int XM>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
+  constexpr bool EXT = XM != 0;   // options of the extended entry point
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1579,7 +1606,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   const int b = bq / q.Q;
   const int qq = bq - b * q.Q;
   const bool bil = EXT && q.bilinear;        // bilinear per-step discretisation
-  const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
+  const RowMap rmap = row_map<XM == 3>(q, qq);   // forward or reverse time
   const int KS = q.Hpad >> 5;
   const int HT = q.Hpad >> 4;
   const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
@@ -1702,7 +1729,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // y stores, so that waiting for the loads does not wait for them
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
       stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
-      readout_store<R, BF16, VEC>(q, yrsrc, rmap, epilogue<EXT>(q), dk, yacc, lds + ui * ut, i, ln);
+      readout_store<R, BF16, VEC>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc, lds + ui * ut, i, ln);
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
       ui = ui1;
     }
@@ -1727,32 +1754,38 @@ hipError_t launch_one(int blocks, int threads, size_t lds, hipStream_t s, const 
   return hipGetLastError();
 }
 
-// EXT: instances with the options of the extended entry point (initial and
-// final state, reverse time, accumulate into y, GELU, bilinear steps); the
-// plain calls run kernels with that code compiled out
+// XM (pass 2): 0 plain calls (option code compiled out); 1 initial and final
+// state, bilinear steps; 2 those and GELU; 3 those and reverse time, adding
+// to y and GELU on request (the backward scan of the bidirectional form).
+// Pass 1 writes no y: its instance 1 serves every call with options.
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
-  const bool st = q.x0 != nullptr || q.xlast != nullptr || q.rev || q.accum || q.gelu || (q.bilinear && TV);
+  const bool xm = q.x0 != nullptr || q.xlast != nullptr || q.rev || (q.bilinear && TV);
   if constexpr (KEEP) {
-    return st ? launch_one<k_reduce_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q)
-              : launch_one<k_reduce_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+    if (xm) return launch_one<k_reduce_ws<MPW, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+    return launch_one<k_reduce_ws<MPW, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
   } else {
-    return st ? launch_one<k_reduce<MPW, R, TV, BF16, KEEP, true>>(blocks, kThreads, p.lds_reduce, s, q)
-              : launch_one<k_reduce<MPW, R, TV, BF16, KEEP, false>>(blocks, kThreads, p.lds_reduce, s, q);
+    if (xm) return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_reduce, s, q);
+    return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 0>>(blocks, kThreads, p.lds_reduce, s, q);
   }
 }
 
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
-  const bool st = q.x0 != nullptr || q.xlast != nullptr || q.rev || q.accum || q.gelu || (q.bilinear && TV);
+  if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
+  const int xm = q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
   if constexpr (KEEP) {
-    return st ? launch_one<k_scan_ws<MPW, R, TV, BF16, true>>(blocks, 2 * kThreads, p.lds_scan, s, q)
-              : launch_one<k_scan_ws<MPW, R, TV, BF16, false>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    if (xm == 3) return launch_one<k_scan_ws<MPW, R, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    if (xm == 2) return launch_one<k_scan_ws<MPW, R, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    if (xm == 1) return launch_one<k_scan_ws<MPW, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    return launch_one<k_scan_ws<MPW, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_scan, s, q);
   } else {
-    return st ? launch_one<k_scan<MPW, R, TV, BF16, KEEP, true>>(blocks, kThreads, p.lds_scan, s, q)
-              : launch_one<k_scan<MPW, R, TV, BF16, KEEP, false>>(blocks, kThreads, p.lds_scan, s, q);
+    if (xm == 3) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 3>>(blocks, kThreads, p.lds_scan, s, q);
+    if (xm == 2) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 2>>(blocks, kThreads, p.lds_scan, s, q);
+    if (xm == 1) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_scan, s, q);
+    return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 0>>(blocks, kThreads, p.lds_scan, s, q);
   }
 }
 

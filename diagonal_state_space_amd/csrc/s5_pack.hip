@@ -136,6 +136,9 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
           }
           const zd a = zexp(z);
           const zd as = zexp({z.re * q.Lseg, z.im * q.Lseg});
+          const double m = (q.L - 1) % q.Lseg + 1;
+          const zd al = zexp({z.re * m, z.im * m});
+          mp.alast = make_float2(static_cast<float>(al.re), static_cast<float>(al.im));
           mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));
           mp.aseg = make_float2(static_cast<float>(as.re), static_cast<float>(as.im));
         }

@@ -189,8 +189,9 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *       "Discretization and the step size"; abhik.ai review: the official
  *       code offers it as an alternative). Time-invariant or time-varying.
  *   S5_FLAG_GELU  y is GELU of the pre-activation, y * Phi(y) with the
- *       standard normal distribution function Phi (exact form, float32;
- *       papercache notes App. A `apply_S5_layer`).
+ *       standard normal distribution function Phi (the exact form, not the
+ *       tanh one; papercache notes App. A `apply_S5_layer`), in float32 with
+ *       erf from Abramowitz & Stegun 7.1.26 (absolute error < 1.5e-7).
  *   S5_FLAG_BIDIRECTIONAL  a second, backward scan over the same Lambda_bar
  *       and B_bar, x'_k = Lambda_bar x'_{k+1} + B_bar u_k from x'_L = 0,
  *       read out by the second half of C~, which then has 2P columns:
