@@ -161,6 +161,36 @@ def cpu_baseline(w, repeats: int, budget_s: float):
                       f"run(s), {t:.2f} s each"}, y
 
 
+def bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas) -> int:
+    """Single recurrent steps (s5_step) for the workload's B sequences: one
+    token per sequence per call, the state carried in place."""
+    n = 64
+    u1 = [us[0][:, k].contiguous() for k in range(n)]
+    dl = [deltas[0][:, k].contiguous() for k in range(n)] if w.time_varying else None
+    x = torch.zeros(w.B, w.P, dtype=torch.complex64, device=lam.device)
+    y = torch.empty_like(u1[0])
+
+    def one(i):
+        kw = {"delta": dl[i % n]} if w.time_varying else {"log_delta": logd}
+        s5.step(u1[i % n], lam, bt, ct, d, x, y=y, **kw)
+
+    steps = max(args.steps, 200)
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    print(json.dumps({"metric": "S5 single recurrent step, tokens/s (B per call)", "unit": "tokens/s",
+                      "value": round(w.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 5), "steps": steps,
+                      "dtype": w.io, "data": "synthetic",
+                      "config": {"workload": f"s5_step_B{w.B}_H{w.H}_P{w.P}_{w.io}", "variant": "step"}}),
+          flush=True)
+    return 0
+
+
 def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_sets) -> int:
     """Time one option of s5_forward_ex, or chunked streaming, on the workload."""
     v = args.variant
@@ -174,6 +204,8 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
     opts = {"stateful": {}, "half": {"half_spectrum": True}, "bilinear": {"bilinear": True},
             "gelu": {"gelu": True}, "bidir": {"bidirectional": True}}
     chunk = int(v.split(":")[1]) if v.startswith("chunked:") else 0
+    if v == "step":
+        return bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas)
     if chunk:
         if w.L % chunk:
             print("chunk must divide L", file=sys.stderr)
@@ -247,7 +279,7 @@ def main() -> int:
     ap.add_argument("--cpu-repeats", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--variant", default="plain",
-                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C")
+                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C | step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()

@@ -42,7 +42,7 @@ lib_path = os.path.join(_PKG, "libs5.so")
 _lib = None
 
 EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_forward_stateful",
-           "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_status_string",
+           "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_step", "s5_status_string",
            "s5_set_profiling_events")
 
 # option bits of s5_forward_ex (include/s5.h)
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.s5_forward_timevarying_stateful.restype = st
         L.s5_forward_ex.argtypes = [ctypes.POINTER(ForwardDesc), vp]
         L.s5_forward_ex.restype = st
+        L.s5_step.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_uint32] + [vp] * 10
+        L.s5_step.restype = st
         L.s5_status_string.argtypes = [st]
         L.s5_status_string.restype = ctypes.c_char_p
         L.s5_set_profiling_events.argtypes = [vp, ctypes.c_int]
@@ -282,6 +284,41 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
                        x_last.data_ptr() if x_last is not None else None)
     _check(lib().s5_forward_ex(ctypes.byref(desc), _stream_handle(stream)), "s5_forward_ex")
     return y, x_last
+
+
+def step(u, lam, b_tilde, c_tilde, d, x, log_delta=None, delta=None, *, half_spectrum=False,
+         bilinear=False, gelu=False, y=None, stream=None):
+    """One recurrent step (s5_step): u [B, H]; x [B, P] complex64 updated in
+    place; exactly one of log_delta [P] and delta [B, P]. Returns y [B, H]."""
+    import torch
+    if u.dim() != 2:
+        raise ValueError("u must be [B, H]")
+    B, H = u.shape
+    P = lam.shape[0]
+    io = _io_code(u.dtype)
+    _dev_tensor(u, "u", u.dtype, (B, H))
+    _dev_tensor(lam, "lam", torch.complex64, (P,))
+    _dev_tensor(b_tilde, "b_tilde", torch.complex64, (P, H))
+    _dev_tensor(c_tilde, "c_tilde", torch.complex64, (H, P))
+    _dev_tensor(d, "d", torch.float32, (H,))
+    _dev_tensor(x, "x", torch.complex64, (B, P))
+    if (log_delta is None) == (delta is None):
+        raise ValueError("give exactly one of log_delta and delta")
+    if log_delta is not None:
+        _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    if delta is not None:
+        _dev_tensor(delta, "delta", torch.float32, (B, P))
+    if y is None:
+        y = torch.empty_like(u)
+    _dev_tensor(y, "y", u.dtype, (B, H))
+    flags = ((FLAG_HALF_SPECTRUM if half_spectrum else 0) | (FLAG_BILINEAR if bilinear else 0) |
+             (FLAG_GELU if gelu else 0))
+    _check(lib().s5_step(B, H, P, io, flags, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
+                         c_tilde.data_ptr(), d.data_ptr(),
+                         log_delta.data_ptr() if log_delta is not None else None,
+                         delta.data_ptr() if delta is not None else None, x.data_ptr(), y.data_ptr(),
+                         _stream_handle(stream)), "s5_step")
+    return y
 
 
 def set_profiling_events(events) -> None:

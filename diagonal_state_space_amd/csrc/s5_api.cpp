@@ -310,6 +310,55 @@ s5_status s5_forward_ex(const s5_forward_desc* x, hipStream_t stream) {
                         x->log_delta, x->delta, x->y, x->delta != nullptr, x->x0, x->x_last, o, stream);
 }
 
+s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, const void* u,
+                  const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde, const float* d,
+                  const float* log_delta, const float* delta, s5_c64* x, void* y, hipStream_t stream) {
+  if (B < 0) return S5_ERR_INVALID_ARGUMENT;
+  s5_status st = check_sizes(P, H);
+  if (st != S5_OK) return st;
+  if (io != S5_F32 && io != S5_BF16) return S5_ERR_UNSUPPORTED;
+  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU;
+  if ((flags & ~known) != 0) return S5_ERR_INVALID_ARGUMENT;   // no backward scan in a single step
+  if ((log_delta == nullptr) == (delta == nullptr)) return S5_ERR_INVALID_ARGUMENT;
+  if (!lambda || !b_tilde || !c_tilde || !d) return S5_ERR_INVALID_ARGUMENT;
+  if (B > 0 && (!u || !x || !y)) return S5_ERR_INVALID_ARGUMENT;
+  if (B > INT32_MAX / (H > P ? H : P)) return S5_ERR_UNSUPPORTED;
+  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, x, y};
+  for (const void* p : ptrs) {
+    if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
+  }
+  if (B == 0) return S5_OK;
+  const int64_t es = io == S5_BF16 ? 2 : 4;
+  // x is read and written in place; y and x may overlap no input and not each other
+  const Range rx = range_of(x, B * P * 8), ry = range_of(y, B * H * es);
+  const Range inputs[] = {range_of(u, B * H * es), range_of(lambda, P * 8), range_of(b_tilde, P * H * 8),
+                          range_of(c_tilde, H * P * 8), range_of(d, H * 4),
+                          log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
+                          delta ? range_of(delta, B * P * 4) : Range{0, 0}};
+  if (overlaps(rx, ry)) return S5_ERR_INVALID_ARGUMENT;
+  for (const Range& r : inputs) {
+    if (overlaps(rx, r) || overlaps(ry, r)) return S5_ERR_INVALID_ARGUMENT;
+  }
+  s5::StepArgs a{};
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.P = static_cast<int>(P);
+  a.bf16_io = io == S5_BF16;
+  a.bilinear = (flags & S5_FLAG_BILINEAR) != 0;
+  a.gelu = (flags & S5_FLAG_GELU) != 0;
+  a.c_scale = (flags & S5_FLAG_HALF_SPECTRUM) ? 2.0f : 1.0f;
+  a.u = u;
+  a.lam = reinterpret_cast<const float2*>(lambda);
+  a.b_tilde = reinterpret_cast<const float2*>(b_tilde);
+  a.c_tilde = reinterpret_cast<const float2*>(c_tilde);
+  a.d = d;
+  a.log_delta = log_delta;
+  a.delta = delta;
+  a.x = reinterpret_cast<float2*>(x);
+  a.y = y;
+  return s5::launch_step(a, stream) == hipSuccess ? S5_OK : S5_ERR_HIP;
+}
+
 const char* s5_status_string(s5_status s) {
   switch (s) {
     case S5_OK: return "S5_OK";

@@ -37,6 +37,27 @@ struct ForwardArgs {
   bool gelu = false;            // GELU of the final y
 };
 
+// One recurrent step for B sequences (validated on the host): x [B, P] in
+// place, y [B, H]; exactly one of log_delta [P] and delta [B, P].
+struct StepArgs {
+  int B, H, P;
+  bool bf16_io;
+  bool bilinear;
+  bool gelu;
+  float c_scale;
+  const void* u;
+  const float2* lam;
+  const float2* b_tilde;
+  const float2* c_tilde;
+  const float* d;
+  const float* log_delta;
+  const float* delta;
+  float2* x;
+  void* y;
+};
+
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+
 // Bytes of stream-ordered scratch the forward path needs for these sizes.
 size_t forward_workspace_bytes(const ForwardArgs& a);
 

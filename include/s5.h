@@ -239,6 +239,38 @@ typedef struct {
 
 s5_status s5_forward_ex(const s5_forward_desc* desc, hipStream_t stream);
 
+/*
+ * s5_step - one recurrent step for B sequences: the online form, which keeps
+ * only the current state (abhik.ai review, "Associative scans preserve the
+ * recurrence": streaming keeps one state per layer, paper Sec. 2.2/3.4;
+ * papercache notes Sec. 3.3, online generation):
+ *     x <- Lambda_bar x + B_bar u,    y = Re(C~ x) + D u
+ * with the discretisation of s5_forward (log_delta, per-mode) or of
+ * s5_forward_timevarying (delta, this step's interval per sequence and mode).
+ * Equal, up to rounding, to s5_forward_stateful / s5_forward_ex over L = 1
+ * with x0 = x and x_last written back to x.
+ *
+ *   B, H, P     sequences (>= 0; 0 is a no-op), features, complex modes
+ *   io          element type of u and y
+ *   flags       S5_FLAG_HALF_SPECTRUM, S5_FLAG_BILINEAR, S5_FLAG_GELU (as in
+ *               s5_forward_ex); S5_FLAG_BIDIRECTIONAL is rejected
+ *   u           [B,H]  this step's input
+ *   lambda, b_tilde [P,H], c_tilde [H,P], d [H]   as s5_forward
+ *   log_delta   [P] per-mode log interval, or NULL
+ *   delta       [B,P] this step's interval, or NULL (exactly one is given)
+ *   x           [B,P] complex64 state, read and overwritten in place
+ *   y           [B,H]  out
+ * Precision: float32 state and sums on the vector units (no bf16 operands);
+ * time-invariant discretisation in float64, per-step intervals in float32.
+ * x and y may overlap no input and not each other.
+ * Errors: S5_ERR_INVALID_ARGUMENT (null pointer, B < 0, P or H < 1, unknown
+ * or bidirectional flag, both or neither interval arrays, overlaps),
+ * S5_ERR_UNSUPPORTED (io, size limits, misalignment), S5_ERR_HIP.
+ */
+s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, const void* u,
+                  const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde, const float* d,
+                  const float* log_delta, const float* delta, s5_c64* x, void* y, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* s5_status_string(s5_status s);
 

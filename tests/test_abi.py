@@ -191,3 +191,24 @@ def test_forward_ex_validation():
     assert _fwd_ex(flags=bidir | s5.FLAG_GELU | s5.FLAG_HALF_SPECTRUM, B=0) == OK   # empty: no-op
     assert _fwd_ex(flags=s5.FLAG_BILINEAR, L=0) == OK
     assert _fwd_ex(P=0) == INVALID and _fwd_ex(H=1000) == UNSUPPORTED
+
+
+def _step(B=2, H=4, P=3, io=0, flags=0, logd=FAKE + 0x5000, delta=None, x=FAKE + 0x8000, y=FAKE + 0x9000,
+          u=FAKE):
+    return s5.lib().s5_step(B, H, P, io, flags, u, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                            FAKE + 0x4000, logd, delta, x, y, None)
+
+
+def test_step_validation():
+    assert _step(flags=s5.FLAG_BIDIRECTIONAL) == INVALID      # no backward scan in one step
+    assert _step(flags=1 << 9) == INVALID
+    assert _step(logd=None) == INVALID                        # neither interval array
+    assert _step(delta=FAKE + 0x6000) == INVALID              # both
+    assert _step(x=FAKE + 0x9000) == INVALID                  # x overlaps y
+    assert _step(x=FAKE + 0x2000) == INVALID                  # x overlaps B~
+    assert _step(y=FAKE) == INVALID                           # y overlaps u
+    assert _step(x=None) == INVALID and _step(u=None) == INVALID
+    assert _step(B=-1) == INVALID and _step(P=0) == INVALID
+    assert _step(H=1000) == UNSUPPORTED and _step(io=5) == UNSUPPORTED
+    assert _step(x=FAKE + 0x8008) == UNSUPPORTED              # misaligned
+    assert _step(B=0) == OK                                   # no-op
