@@ -183,11 +183,41 @@ def bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas) -> int:
         one(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    print(json.dumps({"metric": "S5 single recurrent step, tokens/s (B per call)", "unit": "tokens/s",
-                      "value": round(w.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 5), "steps": steps,
-                      "dtype": w.io, "data": "synthetic",
-                      "config": {"workload": f"s5_step_B{w.B}_H{w.H}_P{w.P}_{w.io}", "variant": "step"}}),
-          flush=True)
+    # the kernel alone: events on the stream the binding launches on
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    for i in range(50):
+        e0[i].record()
+        one(i)
+        e1[i].record()
+    torch.cuda.synchronize()
+    k_us = float(np.median([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1e3
+    s_io = 2 if w.io == "bf16" else 4
+    nbytes = (8 * w.P + 16 * w.P * w.H + 4 * w.H + 4 * w.P + 2 * w.B * w.H * s_io + 16 * w.B * w.P
+              + (4 * w.B * w.P if w.time_varying else 0))
+    gbs = nbytes / (k_us * 1e-6) / 1e9
+    out = {"metric": "S5 single recurrent step, tokens/s (B per call)", "unit": "tokens/s",
+           "value": round(w.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 5), "steps": steps,
+           "higher_is_better": True, "dtype": w.io, "data": "synthetic",
+           "config": {"workload": f"s5_step_B{w.B}_H{w.H}_P{w.P}_{w.io}"
+                                  f"{'_timevarying' if w.time_varying else ''}", "variant": "step"},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "k_step",
+                        "kernel_us": round(k_us, 2), "per_launch": {"bytes": nbytes}}}
+    if not args.no_cpu_baseline:
+        import oracle.s5_oracle as orc
+        kw = {"delta": w.delta[:, :1]} if w.time_varying else {"log_delta": w.log_delta}
+        x0 = np.zeros((w.B, w.P), np.complex128)
+        u1 = w.u[:, :1]
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_budget, 5.0):
+            orc.forward_ex(u1, w.lam, w.b_tilde, w.c_tilde, w.d, x0=x0, **kw)
+            reps += 1
+        t = (time.perf_counter() - t0) / reps
+        out["cpu_baseline"] = {"value": w.B / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                               "sample": f"one step of B={w.B} sequences (oracle forward_ex, L = 1), "
+                                         f"{reps} repetitions, {t * 1e3:.2f} ms each"}
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -241,32 +271,78 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernels = None
-    if not chunk:
-        # HIP events around the first three launches of each call (packing,
-        # aggregate pass, state and output pass: the forward half for bidir)
-        ev = HipEvents()
-        evs = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            s5.set_profiling_events(evs[i])
-            step(args.warmup + args.steps + i)
-        torch.cuda.synchronize()
-        s5.set_profiling_events(None)
-        ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(3)] for e in evs]).mean(axis=0)
-        for e in evs:
-            for h in e:
-                ev.destroy(h)
-        kernels = {"pack_us": round(float(ms[0]) * 1e3, 2), "reduce_us": round(float(ms[1]) * 1e3, 2),
-                   "scan_us": round(float(ms[2]) * 1e3, 2)}
+    # HIP events around every launch of one call (chunked: the last call of
+    # the step): packing, aggregate pass, state and output pass, and for the
+    # bidirectional form the same three for the backward scan
+    nl = 6 if v == "bidir" else 3
+    ev = HipEvents()
+    evs = [[ev.create() for _ in range(2 * nl)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        s5.set_profiling_events(evs[i])
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    s5.set_profiling_events(None)
+    ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(nl)] for e in evs]).mean(axis=0)
+    for e in evs:
+        for h in e:
+            ev.destroy(h)
+    names = ["pack_us", "reduce_us", "scan_us", "back_pack_us", "back_reduce_us", "back_scan_us"]
+    kernels = {names[k]: round(float(ms[k]) * 1e3, 2) for k in range(nl)}
+    # dominant kernel: the (slower) state and output pass; its algorithmic
+    # work is 8 P H flops per token of the call
+    k_dom = 5 if v == "bidir" and ms[5] > ms[2] else 2
+    tokens_call = w.B * (chunk if chunk else w.L)
+    flops = 8 * w.P * w.H * tokens_call
+    achieved = flops / (float(ms[k_dom]) * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.io]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "k_scan (backward scan)" if k_dom == 5 else "k_scan",
+            "kernel_us": round(float(ms[k_dom]) * 1e3, 2), "per_launch": {"flops": flops}}
     workload = (f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
                 f"{'_timevarying' if w.time_varying else ''}")
-    print(json.dumps({"metric": METRIC, "kernels": kernels, "value": round(w.B * w.L / (ms_per_step * 1e-3), 1),
-                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-                      "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-                      "dtype": w.io, "data": "synthetic",
-                      "config": {"workload": workload, "variant": v, "buffer_sets": n_sets}}), flush=True)
+    out = {"metric": METRIC, "value": round(w.B * w.L / (ms_per_step * 1e-3), 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.io, "data": "synthetic",
+           "config": {"workload": workload, "variant": v, "buffer_sets": n_sets},
+           "roofline": roof, "kernels": kernels}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_variant(w, v, ct_run, args.cpu_budget)
+    print(json.dumps(out), flush=True)
     return 0
+
+
+def cpu_baseline_variant(w, v, ct_run, budget_s: float):
+    """The oracle's forward_ex with the variant's options on the whole
+    workload (chunked: one call over the whole sequence, as the chunks carry
+    the state exactly), median of runs within the budget."""
+    import oracle.s5_oracle as orc
+    c = ct_run.cpu().numpy() if v == "bidir" else w.c_tilde
+    kw = {"delta": w.delta} if w.time_varying else {"log_delta": w.log_delta}
+    opts = {"half": {"conj_sym": True}, "bilinear": {"method": "bilinear"}, "gelu": {"activation": "gelu"},
+            "bidir": {"bidirectional": True}}.get(v, {})
+    if v == "stateful" or v.startswith("chunked:"):
+        kw["x0"] = np.zeros((w.B, w.P), np.complex128)
+    times = []
+    while not times or (sum(times) < budget_s and len(times) < 25):
+        t0 = time.perf_counter()
+        orc.forward_ex(w.u, w.lam, w.b_tilde, c, w.d, **kw, **opts)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"whole workload (B={w.B}, L={w.L}), oracle forward_ex with the variant's options, "
+                      f"float64 NumPy, median of {len(times)} run(s), {t:.2f} s each"}
+
+
+def _blas_threads() -> int:
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return int(max([i.get("num_threads", 1) for i in info] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
 
 def main() -> int:

@@ -322,10 +322,11 @@ def step(u, lam, b_tilde, c_tilde, d, x, log_delta=None, delta=None, *, half_spe
 
 
 def set_profiling_events(events) -> None:
-    """Raw hipEvent_t handles (ints), an even number up to 6: events[2k] and
+    """Raw hipEvent_t handles (ints), an even number up to 12: events[2k] and
     events[2k+1] are recorded around the k-th kernel launch (0 packing, 1
-    aggregate pass, 2 state and output pass) of later forward calls from this
-    thread. An empty sequence (or None) turns the hook off."""
+    aggregate pass, 2 state and output pass; 3-5 the same for the backward
+    scan of the bidirectional form) of later forward calls from this thread.
+    An empty sequence (or None) turns the hook off."""
     events = list(events or [])
     arr = (ctypes.c_void_p * max(1, len(events)))(*events) if events else None
     _check(lib().s5_set_profiling_events(arr, len(events)), "s5_set_profiling_events")

@@ -283,13 +283,16 @@ const char* s5_status_string(s5_status s);
  * hipEventElapsedTime gives that kernel's duration alone. The launches of one
  * forward call are, in order: k = 0 parameter packing (discretisation and
  * operand layouts), k = 1 the aggregate pass (state of every token range from
- * a zero start), k = 2 the state and output pass. count 0 turns the hook off.
+ * a zero start), k = 2 the state and output pass; the bidirectional form of
+ * s5_forward_ex adds k = 3..5, the same three for the backward scan. count 0
+ * turns the hook off. (Also recorded by s5_forward_stateful,
+ * s5_forward_timevarying_stateful and s5_forward_ex.)
  * The handles are copied; the events stay owned by the caller and must
  * outlive the calls that record them. The setting is per host thread.
  * Errors: S5_ERR_INVALID_ARGUMENT for an odd or out-of-range count, a NULL
  * array with count > 0, or a NULL handle among the first count.
  */
-#define S5_PROFILING_MAX_EVENTS 6
+#define S5_PROFILING_MAX_EVENTS 12
 s5_status s5_set_profiling_events(const hipEvent_t* events, int count);
 
 #ifdef __cplusplus

@@ -109,13 +109,14 @@ def test_discretize_validation():
 
 def test_profiling_events_validation():
     L = s5.lib()
-    arr = (ctypes.c_void_p * 6)(*([FAKE] * 6))
+    arr = (ctypes.c_void_p * 14)(*([FAKE] * 14))
     assert L.s5_set_profiling_events(arr, 3) == INVALID           # odd count
-    assert L.s5_set_profiling_events(arr, 8) == INVALID           # beyond the maximum
+    assert L.s5_set_profiling_events(arr, 14) == INVALID          # beyond the maximum (12)
     assert L.s5_set_profiling_events(None, 2) == INVALID          # no array
     holes = (ctypes.c_void_p * 2)(FAKE, None)
     assert L.s5_set_profiling_events(holes, 2) == INVALID         # NULL handle
     assert L.s5_set_profiling_events(arr, 6) == OK
+    assert L.s5_set_profiling_events(arr, 12) == OK
     assert L.s5_set_profiling_events(None, 0) == OK
 
 
