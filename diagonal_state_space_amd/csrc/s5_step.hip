@@ -12,7 +12,7 @@ namespace s5 {
 
 namespace {
 
-constexpr int kStepThreads = 512;   // >= S5_MAX_H outputs, 2 threads per mode
+constexpr int kStepThreads = 512;   // >= S5_MAX_H outputs, >= 2 S5_MAX_P
 
 struct zd {
   double re, im;
@@ -55,9 +55,23 @@ __device__ void disc_mode64(zd lam, double dt, bool bilinear, zd& abar, zd& gain
 
 __device__ __forceinline__ float gelu_step(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
+// lanes per row of a sum: the 512 threads spread over `rows` rows, a power
+// of two from 1 to 8, the lanes of a row adjacent
+__device__ __forceinline__ int lanes_per_row(int rows) {
+  int k = 1;
+  while (k < 8 && rows * (2 * k) <= kStepThreads) k *= 2;
+  return k;
+}
+
+// sum over the k adjacent lanes of a row (k a power of two <= 8)
+__device__ __forceinline__ float row_sum(float v, int k) {
+  for (int o = 1; o < k; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
   __shared__ float s_u[kStepThreads];
-  __shared__ float2 s_bu[2][kStepThreads / 2];
+  __shared__ float2 s_bu[kStepThreads / 2];
   __shared__ float2 s_x[kStepThreads / 2];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -66,33 +80,35 @@ __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
     s_u[h] = q.bf16_io ? bf16_to_f32(static_cast<const uint16_t*>(q.u)[ub + h]) : static_cast<const float*>(q.u)[ub + h];
   __syncthreads();
 
-  // drive: thread (p, half) sums B~[p, h] u[h] over its half of the features
-  const int p = t & (kStepThreads / 2 - 1);
-  const int half = t / (kStepThreads / 2);
-  if (p < q.P) {
-    const int hh = (q.H + 1) / 2;
-    const int h0 = half * hh;
-    const int h1 = min(q.H, h0 + hh);
-    const float2* row = q.b_tilde + static_cast<size_t>(p) * q.H;
+  // drive: the k lanes of mode p sum B~[p, h] u[h] over h = part, part + k, ...
+  const int kd = lanes_per_row(q.P);
+  const int p = t / kd;
+  const int part = t - p * kd;
+  {
     float re = 0.0f, im = 0.0f;
-#pragma unroll 8
-    for (int h = h0; h < h1; ++h) {
-      const float2 bt = row[h];
-      re = fmaf(bt.x, s_u[h], re);
-      im = fmaf(bt.y, s_u[h], im);
+    if (p < q.P) {
+      const float2* row = q.b_tilde + static_cast<size_t>(p) * q.H;
+#pragma unroll 16
+      for (int h = part; h < q.H; h += kd) {
+        const float2 bt = row[h];
+        re = fmaf(bt.x, s_u[h], re);
+        im = fmaf(bt.y, s_u[h], im);
+      }
     }
-    s_bu[half][p] = make_float2(re, im);
+    re = row_sum(re, kd);   // every lane takes part (the shuffles span the wave)
+    im = row_sum(im, kd);
+    if (p < q.P && part == 0) s_bu[p] = make_float2(re, im);
   }
   __syncthreads();
 
-  // state update of mode p (first half of the threads), in place
-  if (half == 0 && p < q.P) {
-    const cf bu = {s_bu[0][p].x + s_bu[1][p].x, s_bu[0][p].y + s_bu[1][p].y};
-    const size_t xi = static_cast<size_t>(b) * q.P + p;
+  // state update of mode t, in place
+  if (t < q.P) {
+    const cf bu = {s_bu[t].x, s_bu[t].y};
+    const size_t xi = static_cast<size_t>(b) * q.P + t;
     cf a, g;
     if (q.delta != nullptr) {
       // per-step interval: float32, as the time-varying forward pass
-      const cf lam = {q.lam[p].x, q.lam[p].y};
+      const cf lam = {q.lam[t].x, q.lam[t].y};
       const float dt = q.delta[xi];
       if (q.bilinear) {
         bilinear_step(lam, dt, a, g);
@@ -103,33 +119,39 @@ __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
       }
     } else {
       zd a64, g64;
-      disc_mode64({q.lam[p].x, q.lam[p].y}, exp(static_cast<double>(q.log_delta[p])), q.bilinear, a64, g64);
+      disc_mode64({q.lam[t].x, q.lam[t].y}, exp(static_cast<double>(q.log_delta[t])), q.bilinear, a64, g64);
       a = {static_cast<float>(a64.re), static_cast<float>(a64.im)};
       g = {static_cast<float>(g64.re), static_cast<float>(g64.im)};
     }
     const float2 x0 = q.x[xi];
     const cf xn = cfma(a, {x0.x, x0.y}, cmul(g, bu));
     q.x[xi] = make_float2(xn.re, xn.im);
-    s_x[p] = make_float2(xn.re, xn.im);
+    s_x[t] = make_float2(xn.re, xn.im);
   }
   __syncthreads();
 
-  // readout of feature h = t
-  if (t < q.H) {
-    const float2* row = q.c_tilde + static_cast<size_t>(t) * q.P;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int m = 0; m < q.P; ++m) {
+  // readout: the k lanes of feature h sum Re(C~[h, m] x[m]) over m = part, part + k, ...
+  const int kr = lanes_per_row(q.H);
+  const int h = t / kr;
+  const int rp = t - h * kr;
+  float acc = 0.0f;
+  if (h < q.H) {
+    const float2* row = q.c_tilde + static_cast<size_t>(h) * q.P;
+#pragma unroll 16
+    for (int m = rp; m < q.P; m += kr) {
       const float2 c = row[m];
       const float2 xv = s_x[m];
       acc = fmaf(c.x, xv.x, fmaf(-c.y, xv.y, acc));
     }
-    float yv = fmaf(q.d[t], s_u[t], q.c_scale * acc);
+  }
+  acc = row_sum(acc, kr);
+  if (h < q.H && rp == 0) {
+    float yv = fmaf(q.d[h], s_u[h], q.c_scale * acc);
     if (q.gelu) yv = gelu_step(yv);
     if (q.bf16_io) {
-      static_cast<uint16_t*>(q.y)[ub + t] = f32_to_bf16(yv);
+      static_cast<uint16_t*>(q.y)[ub + h] = f32_to_bf16(yv);
     } else {
-      static_cast<float*>(q.y)[ub + t] = yv;
+      static_cast<float*>(q.y)[ub + h] = yv;
     }
   }
 }
