@@ -1167,11 +1167,69 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
 // y of chunk i from the register-weight readout's accumulators: feedthrough
 // from u tile i in LDS and D from the LDS table (h-tiles past H: the stores
 // fall outside the descriptor and are dropped)
+// y values already in memory for the readout lane's outputs of chunk i (the
+// backward scan adds to them), raw: 4 bf16 or 4 floats per (h-tile, step),
+// zeros outside the range or past H. Loaded a chunk ahead of their use.
+template <bool BF16>
+struct YOld {
+  std::conditional_t<BF16, uint2, uint4> v[kKeepHT][2];
+};
+
 template <int R, bool BF16, bool VEC>
+__device__ __forceinline__ void load_y_old(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm, int i,
+                                           const Lane& ln, YOld<BF16>& o) {
+  static_assert(R <= 2, "two steps per chunk at most");
+  constexpr int esz = BF16 ? 2 : 4;
+#pragma unroll
+  for (int e = 0; e < kKeepHT; ++e) {
+    const int h0 = 16 * (ln.w + kWaves * e) + 4 * ln.g;
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      const int roff = rm(rel_row<R>(q, ln.t, i, n)) * q.H;
+      if constexpr (VEC) {
+        const int off = h0 < q.H ? (roff + h0) * esz : kBufferOOB;
+        if constexpr (BF16) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0);
+          o.v[e][n] = make_uint2(v[0], v[1]);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0);
+          o.v[e][n] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int off = h0 + m < q.H ? (roff + h0 + m) * esz : kBufferOOB;
+          w[m] = BF16 ? static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(yr, off, 0, 0))
+                      : __builtin_amdgcn_raw_buffer_load_b32(yr, off, 0, 0);
+        }
+        if constexpr (BF16) {
+          o.v[e][n] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+        } else {
+          o.v[e][n] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 y_old_f32(const std::conditional_t<BF16, uint2, uint4>& v) {
+  if constexpr (BF16) {
+    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                 __uint_as_float(v.y & 0xffff0000u)};
+  } else {
+    return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+  }
+}
+
+// ACC: add `old` (the y already in memory, loaded a chunk ahead) to the sums
+template <int R, bool BF16, bool VEC, bool ACC = false>
 __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm,
                                               const Epi& ep,
                                               const float4 (&dk)[kKeepHT], const f32x4 (&yacc)[kKeepHT][R],
-                                              const lds_byte* ub, int i, const Lane& ln) {
+                                              const lds_byte* ub, int i, const Lane& ln,
+                                              const YOld<BF16>* old = nullptr) {
   float uv[kKeepHT][R][4];
 #pragma unroll
   for (int e = 0; e < kKeepHT; ++e)
@@ -1181,8 +1239,12 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
   for (int e = 0; e < kKeepHT; ++e) {
     const int h0 = 16 * (ln.w + kWaves * e) + 4 * ln.g;
 #pragma unroll
-    for (int n = 0; n < R; ++n)
-      store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], dk[e], uv[e][n], ep);
+    for (int n = 0; n < R; ++n) {
+      f32x4 a = yacc[e][n];
+      if constexpr (ACC) a += y_old_f32<BF16>(old->v[e][n]);
+      store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, a, dk[e], uv[e][n],
+                         Epi{ACC ? false : ep.accum, ep.gelu});
+    }
   }
 }
 
@@ -1693,6 +1755,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       ui = ui1;
     }
   } else {
+    // backward scan (XM = 3): the y being added to, a chunk ahead in registers
+    constexpr bool kAcc = XM == 3;
+    YOld<BF16> yold;
+    if constexpr (kAcc) load_y_old<R, BF16, VEC>(q, yrsrc, rmap, 0, ln, yold);
     int ui = 0;   // i % 3
     for (int i = 0; i < q.nck; ++i) {
       const int ui1 = ui == 2 ? 0 : ui + 1;
@@ -1701,6 +1767,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // (not carried across iterations: no register shuffles, no early wait)
       UStage<NB> ust2;
       fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 2, ust2);
+      YOld<BF16> ynext;
+      if constexpr (kAcc) load_y_old<R, BF16, VEC>(q, yrsrc, rmap, i + 1, ln, ynext);
       const lds_byte* xr = xlds + (i & 1) * xt;
       f32x4 yacc[kKeepHT][R];
 #pragma unroll
@@ -1714,7 +1782,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
       // the u loads first, then the x reads kAhead K-steps ahead of their
       // MFMAs (left alone, the scheduler puts each load next to its use)
-      __builtin_amdgcn_sched_group_barrier(0x020, VEC ? NB : NB * (BF16 ? 8 : 4), 0);
+      __builtin_amdgcn_sched_group_barrier(
+          0x020, (VEC ? NB : NB * (BF16 ? 8 : 4)) + (kAcc ? kKeepHT * R * (VEC ? 1 : 4) : 0), 0);
       __builtin_amdgcn_sched_group_barrier(0x100, (kAhead < K2 ? kAhead : K2) * NP * R, 0);
 #pragma unroll
       for (int s = 0; s < K2; ++s) {
@@ -1729,8 +1798,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // y stores, so that waiting for the loads does not wait for them
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
       stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
-      readout_store<R, BF16, VEC>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc, lds + ui * ut, i, ln);
+      readout_store<R, BF16, VEC, kAcc>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc, lds + ui * ut, i, ln, &yold);
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
+      if constexpr (kAcc) yold = ynext;
       ui = ui1;
     }
   }
