@@ -119,6 +119,11 @@ CASES = [
     ((1, 5001, 128, 256, "bf16", False), {"bidir": True}),          # many ranges, ragged end
     ((2, 3000, 128, 128, "bf16", False), {"bidir": True, "half": True, "gelu": True, "bilinear": True}),
     ((2, 2000, 96, 128, "f32", False), {"bidir": True, "gelu": True}),
+    # four-wave kernels (weights streamed from L2) with each option instance
+    ((2, 1000, 256, 192, "bf16", False), {"gelu": True}),
+    ((1, 700, 512, 256, "bf16", False), {"bidir": True, "half": True}),
+    ((2, 600, 200, 256, "f32", False), {"bilinear": True, "state": True}),
+    ((2, 513, 160, 96, "f32", True), {"bilinear": True, "gelu": True, "state": True}),
 ]
 
 
