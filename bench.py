@@ -78,11 +78,18 @@ class HipEvents:
         self.h.hipEventDestroy(ctypes.c_void_p(e))
 
 
+# sources that do not build or launch the forward passes' kernels (the
+# single-step kernel, the host-side discretisation entry point, the C ABI
+# layer's validation): edits there leave the traffic record valid
+DIGEST_EXCLUDE = {"s5_step.hip", "s5_discretize.hip", "s5_api.cpp"}
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP/C++ sources of the library (sorted by name)."""
+    """sha256 over the HIP/C++ sources that build and launch the forward
+    passes' kernels (sorted by name)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name not in DIGEST_EXCLUDE:
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
