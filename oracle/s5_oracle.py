@@ -56,6 +56,12 @@ O10 bidirectional form: a second, backward scan over the same
     (factor 2 on both terms under O7). Time-invariant only; no state in or
     out. [wikillm notes, "Paper vs code", bidirectional scans; abhik.ai
     review, offline bidirectional use]
+O11 gated activation after the layer, with a dense H x H matrix W and an
+    optional bias b: g = GELU(y); variant 1 returns g * sigma(g W^T + b)
+    (the paper's gate), variant 2 returns y * sigma(g W^T + b) (the un-
+    activated y gated, GELU only inside the gate); sigma is the logistic
+    function. [wikillm notes, "Paper vs code": GLU variant and dense gate
+    bias; the pseudocode's half_glu1 step]
 
 Every function is pinned by the checks in tests/test_oracle_pins.py against
 closed forms, an ODE solve, the convolution-kernel form, impulse responses,
@@ -87,6 +93,8 @@ __all__ = [
     "gelu",
     "scan_reverse",
     "forward_ex",
+    "sigmoid",
+    "glu",
 ]
 
 # |z| below which the gain uses the Taylor series of phi1 (abhik.ai review, row 2)
@@ -313,3 +321,25 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
     if activation == "gelu":
         y = gelu(y)                                                   # O9
     return y, x_last
+
+
+def sigmoid(x):
+    """The logistic function 1 / (1 + exp(-x)), float64."""
+    return scipy.special.expit(np.asarray(x, dtype=np.float64))
+
+
+def glu(y, w, bias=None, variant=1):
+    """O11: y [..., H] real; w [H, H] (output j reads w[j, :]); bias [H] or
+    None. Variant 1: g * sigmoid(g w^T + b), variant 2: y * sigmoid(g w^T + b),
+    with g = GELU(y)."""
+    y = np.asarray(y, dtype=np.float64)
+    g = gelu(y)
+    pre = g @ np.asarray(w, dtype=np.float64).T
+    if bias is not None:
+        pre = pre + np.asarray(bias, dtype=np.float64)
+    gate = sigmoid(pre)
+    if variant == 1:
+        return g * gate
+    if variant == 2:
+        return y * gate
+    raise ValueError("variant must be 1 or 2")

@@ -494,6 +494,49 @@ def pin_bidirectional_reversal():
     return _rel(y, yr[:, ::-1])
 
 
+def pin_sigmoid_tanh_identity():
+    """sigma(x) = (1 + tanh(x / 2)) / 2, and sigma(x) + sigma(-x) = 1."""
+    x = np.linspace(-30.0, 30.0, 601)
+    err = float(np.max(np.abs(orc.sigmoid(x) - 0.5 * (1.0 + np.tanh(0.5 * x)))))
+    return max(err, float(np.max(np.abs(orc.sigmoid(x) + orc.sigmoid(-x) - 1.0))))
+
+
+def pin_glu_brute_force():
+    """O11 against explicit loops over tokens, outputs and inputs on a tiny
+    case with a non-symmetric W, for both variants, with and without bias."""
+    rng = _rng(47)
+    T, H = 3, 5
+    y = rng.normal(size=(T, H)) * 2.0
+    w = rng.normal(size=(H, H))
+    b = rng.normal(size=H)
+    err = 0.0
+    for variant in (1, 2):
+        for bias in (None, b):
+            got = orc.glu(y, w, bias, variant)
+            for t in range(T):
+                g = [y[t, i] * 0.5 * (1.0 + math.erf(y[t, i] / math.sqrt(2.0))) for i in range(H)]
+                for j in range(H):
+                    pre = sum(w[j, i] * g[i] for i in range(H)) + (0.0 if bias is None else bias[j])
+                    gate = 1.0 / (1.0 + math.exp(-pre))
+                    want = (g[j] if variant == 1 else y[t, j]) * gate
+                    err = max(err, abs(got[t, j] - want))
+    return err
+
+
+def pin_glu_limits():
+    """W = 0, b = 0 halves the gated value; a large positive bias opens the
+    gate fully (variant 1 gives GELU(y), variant 2 gives y)."""
+    rng = _rng(48)
+    y = rng.normal(size=(4, 6))
+    z = np.zeros((6, 6))
+    err = max(float(np.max(np.abs(orc.glu(y, z, None, 1) - 0.5 * orc.gelu(y)))),
+              float(np.max(np.abs(orc.glu(y, z, None, 2) - 0.5 * y))))
+    big = np.full(6, 60.0)
+    err = max(err, float(np.max(np.abs(orc.glu(y, z, big, 1) - orc.gelu(y)))),
+              float(np.max(np.abs(orc.glu(y, z, big, 2) - y))))
+    return err
+
+
 ALL_PINS = {
     "zoh_expm": (pin_zoh_expm, 1e-12),
     "constant_input": (pin_constant_input_closed_form, 1e-12),
@@ -516,6 +559,9 @@ ALL_PINS = {
     "gelu_values": (pin_gelu_values, 1e-13),
     "bidirectional_convolution": (pin_bidirectional_convolution, 1e-10),
     "bidirectional_reversal": (pin_bidirectional_reversal, 1e-12),
+    "sigmoid_tanh_identity": (pin_sigmoid_tanh_identity, 1e-15),
+    "glu_brute_force": (pin_glu_brute_force, 1e-13),
+    "glu_limits": (pin_glu_limits, 1e-15),
 }
 
 
@@ -860,3 +906,25 @@ def test_forward_ex_reduces_to_the_plain_forms():
         orc.forward_ex(u, lam, bt, ct2, d, delta=dt, bidirectional=True)
     with pytest.raises(ValueError):
         orc.forward_ex(u, lam, bt, ct2, d, log_delta=logd, x0=x0, bidirectional=True)
+
+
+def test_planted_glu_transposed_weight(monkeypatch):
+    good = orc.glu
+    monkeypatch.setattr(orc, "glu", lambda y, w, bias=None, variant=1: good(y, np.asarray(w).T, bias, variant))
+    assert _fails("glu_brute_force")
+
+
+def test_planted_glu_variant_two_gates_gelu(monkeypatch):
+    good = orc.glu
+    monkeypatch.setattr(orc, "glu", lambda y, w, bias=None, variant=1: good(y, w, bias, 1))
+    assert _fails("glu_brute_force") and _fails("glu_limits")
+
+
+def test_planted_glu_gate_without_gelu(monkeypatch):
+    def raw_gate(y, w, bias=None, variant=1):
+        y = np.asarray(y, np.float64)
+        pre = y @ np.asarray(w).T + (0.0 if bias is None else bias)
+        g = orc.gelu(y)
+        return (g if variant == 1 else y) * orc.sigmoid(pre)
+    monkeypatch.setattr(orc, "glu", raw_gate)
+    assert _fails("glu_brute_force")
