@@ -228,6 +228,66 @@ def bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas) -> int:
     return 0
 
 
+def bench_glu(args, w, s5, torch, us, ys, n_sets) -> int:
+    """The gated activation (s5_glu, variant 1 or 2 from "glu" / "glu2") over
+    the workload's B*L tokens of H features (the layer output's shape), with
+    a dense W ~ N(0, 1/H) and a bias; HBM-bound: y in, out written."""
+    variant = 2 if args.variant == "glu2" else 1
+    rng = np.random.default_rng(7)
+    wmat = (rng.normal(size=(w.H, w.H)) / math.sqrt(w.H)).astype(np.float32)
+    bias = (rng.normal(size=w.H) * 0.5).astype(np.float32)
+    wd = torch.from_numpy(wmat).cuda()
+    bd = torch.from_numpy(bias).cuda()
+    yin = [u.view(-1, w.H) for u in us]
+    outs = [y.view(-1, w.H) for y in ys]
+
+    def one(i):
+        k = i % n_sets
+        s5.glu(yin[k], wd, bd, variant, out=outs[k])
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(args.warmup + i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        e0[i].record()
+        one(i)
+        e1[i].record()
+    torch.cuda.synchronize()
+    k_us = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1e3
+    T = w.B * w.L
+    s_io = 2 if w.io == "bf16" else 4
+    nbytes = 2 * T * w.H * s_io + 4 * w.H * w.H + 4 * w.H
+    gbs = nbytes / (k_us * 1e-6) / 1e9
+    out = {"metric": "S5 gated activation tokens/s (B*L tokens of H features)", "unit": "tokens/s",
+           "value": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5), "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "dtype": w.io, "data": "synthetic",
+           "config": {"workload": f"s5_glu{variant}_T{T}_H{w.H}_{w.io}", "variant": args.variant},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_glu",
+                        "kernel_us": round(k_us, 2), "per_launch": {"bytes": nbytes, "flops": 2 * T * w.H * w.H}}}
+    if not args.no_cpu_baseline:
+        import oracle.s5_oracle as orc
+        yv = w.u.reshape(-1, w.H)
+        times = []
+        while not times or (sum(times) < args.cpu_budget and len(times) < 10):
+            t1 = time.perf_counter()
+            orc.glu(yv, wmat, bias, variant)
+            times.append(time.perf_counter() - t1)
+        t = float(np.median(times))
+        out["cpu_baseline"] = {"value": T / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                               "sample": f"whole workload ({T} tokens), oracle glu, float64 NumPy, median of "
+                                         f"{len(times)} run(s), {t:.2f} s each"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_sets) -> int:
     """Time one option of s5_forward_ex, or chunked streaming, on the workload."""
     v = args.variant
@@ -243,6 +303,8 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
     chunk = int(v.split(":")[1]) if v.startswith("chunked:") else 0
     if v == "step":
         return bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas)
+    if v.startswith("glu"):
+        return bench_glu(args, w, s5, torch, us, ys, n_sets)
     if chunk:
         if w.L % chunk:
             print("chunk must divide L", file=sys.stderr)
@@ -362,7 +424,7 @@ def main() -> int:
     ap.add_argument("--cpu-repeats", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--variant", default="plain",
-                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C | step")
+                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C | step | glu | glu2")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()

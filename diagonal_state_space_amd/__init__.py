@@ -42,7 +42,7 @@ lib_path = os.path.join(_PKG, "libs5.so")
 _lib = None
 
 EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_forward_stateful",
-           "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_step", "s5_status_string",
+           "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_step", "s5_glu", "s5_status_string",
            "s5_set_profiling_events")
 
 # option bits of s5_forward_ex (include/s5.h)
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.s5_forward_ex.restype = st
         L.s5_step.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_uint32] + [vp] * 10
         L.s5_step.restype = st
+        L.s5_glu.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+        L.s5_glu.restype = st
         L.s5_status_string.argtypes = [st]
         L.s5_status_string.restype = ctypes.c_char_p
         L.s5_set_profiling_events.argtypes = [vp, ctypes.c_int]
@@ -319,6 +321,28 @@ def step(u, lam, b_tilde, c_tilde, d, x, log_delta=None, delta=None, *, half_spe
                          delta.data_ptr() if delta is not None else None, x.data_ptr(), y.data_ptr(),
                          _stream_handle(stream)), "s5_step")
     return y
+
+
+def glu(y, w, bias=None, variant=1, out=None, stream=None):
+    """Gated activation (s5_glu): y [..., H] float32 or bfloat16 (any leading
+    shape, contiguous); w [H, H] float32; bias [H] float32 or None. Returns
+    (variant 1) GELU(y) * sigmoid(GELU(y) w^T + b) or (variant 2)
+    y * sigmoid(GELU(y) w^T + b); out may be y (in place)."""
+    import torch
+    H = y.shape[-1]
+    T = y.numel() // H if H else 0
+    io = _io_code(y.dtype)
+    _dev_tensor(y, "y", y.dtype, tuple(y.shape))
+    _dev_tensor(w, "w", torch.float32, (H, H))
+    if bias is not None:
+        _dev_tensor(bias, "bias", torch.float32, (H,))
+    if out is None:
+        out = torch.empty_like(y)
+    _dev_tensor(out, "out", y.dtype, tuple(y.shape))
+    _check(lib().s5_glu(T, H, io, int(variant), y.data_ptr(), w.data_ptr(),
+                        bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                        _stream_handle(stream)), "s5_glu")
+    return out
 
 
 def set_profiling_events(events) -> None:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libs5.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["s5_api.cpp", "s5_discretize.hip", "s5_forward.hip", "s5_pack.hip", "s5_step.hip",
+SOURCES = ["s5_api.cpp", "s5_discretize.hip", "s5_forward.hip", "s5_pack.hip", "s5_step.hip", "s5_glu.hip",
            "s5_fused_bf16_ti.hip", "s5_fused_bf16_tv.hip", "s5_fused_f32_ti.hip", "s5_fused_f32_tv.hip"]
 
 # Packed-FP32 instructions are disabled for all device code.

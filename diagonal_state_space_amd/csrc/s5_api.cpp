@@ -359,6 +359,36 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
   return s5::launch_step(a, stream) == hipSuccess ? S5_OK : S5_ERR_HIP;
 }
 
+s5_status s5_glu(int64_t T, int64_t H, s5_dtype io, int variant, const void* y, const float* w,
+                 const float* bias, void* out, hipStream_t stream) {
+  if (T < 0 || H < 1) return S5_ERR_INVALID_ARGUMENT;
+  if (H > S5_GLU_MAX_H || T > INT32_MAX / H) return S5_ERR_UNSUPPORTED;
+  if (io != S5_F32 && io != S5_BF16) return S5_ERR_UNSUPPORTED;
+  if (variant != 1 && variant != 2) return S5_ERR_INVALID_ARGUMENT;
+  if (!w || (T > 0 && (!y || !out))) return S5_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {y, w, bias, out};
+  for (const void* p : ptrs) {
+    if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return S5_OK;
+  const int64_t es = io == S5_BF16 ? 2 : 4;
+  const Range ro = range_of(out, T * H * es), ry = range_of(y, T * H * es);
+  // out may be y itself (in place); otherwise it overlaps no input
+  if (out != y && overlaps(ro, ry)) return S5_ERR_INVALID_ARGUMENT;
+  if (overlaps(ro, range_of(w, H * H * 4))) return S5_ERR_INVALID_ARGUMENT;
+  if (bias && overlaps(ro, range_of(bias, H * 4))) return S5_ERR_INVALID_ARGUMENT;
+  s5::GluArgs a{};
+  a.T = static_cast<int>(T);
+  a.H = static_cast<int>(H);
+  a.bf16_io = io == S5_BF16;
+  a.variant = variant;
+  a.y = y;
+  a.w = w;
+  a.bias = bias;
+  a.out = out;
+  return s5::launch_glu(a, stream) == hipSuccess ? S5_OK : S5_ERR_HIP;
+}
+
 const char* s5_status_string(s5_status s) {
   switch (s) {
     case S5_OK: return "S5_OK";

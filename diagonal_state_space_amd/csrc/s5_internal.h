@@ -58,6 +58,20 @@ struct StepArgs {
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
+// Gated activation over T tokens of H features (validated on the host):
+// out = (variant 1: GELU(y); 2: y) * sigma(W GELU(y) + bias); H <= 256.
+struct GluArgs {
+  int T, H;
+  bool bf16_io;
+  int variant;
+  const void* y;
+  const float* w;      // [H, H] row-major: output j reads w[j, :]
+  const float* bias;   // [H] or null
+  void* out;
+};
+
+hipError_t launch_glu(const GluArgs& a, hipStream_t stream);
+
 // Bytes of stream-ordered scratch the forward path needs for these sizes.
 size_t forward_workspace_bytes(const ForwardArgs& a);
 

@@ -271,6 +271,32 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
                   const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde, const float* d,
                   const float* log_delta, const float* delta, s5_c64* x, void* y, hipStream_t stream);
 
+/*
+ * s5_glu - the gated activation that follows the layer in the S5 network
+ * (wikillm notes, "Paper vs code": GLU variant and dense gate bias; the
+ * pseudocode's half_glu1 step), for T tokens of H features:
+ *     g = GELU(y),  gate = sigma(W g + bias)      (sigma: logistic function)
+ *     variant 1: out = g * gate     (the paper's gate)
+ *     variant 2: out = y * gate     (the un-activated y gated)
+ *
+ *   T, H        tokens (>= 0; 0 is a no-op) and features (1..S5_GLU_MAX_H)
+ *   io          element type of y and out
+ *   variant     1 or 2
+ *   y           [T,H]  input (e.g. the y of s5_forward with B*L tokens)
+ *   w           [H,H]  float32, row-major: output j reads w[j, :]
+ *   bias        [H]    float32, or NULL for none
+ *   out         [T,H]  out; may be y itself (in place), else overlaps no input
+ * Precision: W g on the matrix cores with bf16 operands (bf16 io) or the
+ * bf16 hi/lo split of each float32 operand with three products (float32
+ * io); float32 sums, GELU and gate.
+ * Errors: S5_ERR_INVALID_ARGUMENT (null pointer, T < 0, H < 1, variant not
+ * 1 or 2, overlaps), S5_ERR_UNSUPPORTED (io, H > S5_GLU_MAX_H,
+ * misalignment), S5_ERR_HIP.
+ */
+#define S5_GLU_MAX_H 256
+s5_status s5_glu(int64_t T, int64_t H, s5_dtype io, int variant, const void* y, const float* w,
+                 const float* bias, void* out, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* s5_status_string(s5_status s);
 

@@ -213,3 +213,19 @@ def test_step_validation():
     assert _step(H=1000) == UNSUPPORTED and _step(io=5) == UNSUPPORTED
     assert _step(x=FAKE + 0x8008) == UNSUPPORTED              # misaligned
     assert _step(B=0) == OK                                   # no-op
+
+
+def _glu(T=4, H=8, io=0, variant=1, y=FAKE, w=FAKE + 0x1000, bias=FAKE + 0x2000, out=FAKE + 0x3000):
+    return s5.lib().s5_glu(T, H, io, variant, y, w, bias, out, None)
+
+
+def test_glu_validation():
+    assert _glu(variant=3) == INVALID
+    assert _glu(H=0) == INVALID and _glu(T=-1) == INVALID
+    assert _glu(H=300) == UNSUPPORTED and _glu(io=7) == UNSUPPORTED
+    assert _glu(w=None) == INVALID and _glu(y=None) == INVALID and _glu(out=None) == INVALID
+    assert _glu(out=FAKE + 16) == INVALID          # partial overlap with y
+    assert _glu(out=FAKE + 0x1000) == INVALID      # out overlaps W
+    assert _glu(out=FAKE + 0x2000) == INVALID      # out overlaps the bias
+    assert _glu(y=FAKE + 8) == UNSUPPORTED         # misaligned
+    assert _glu(T=0) == OK                         # no-op
