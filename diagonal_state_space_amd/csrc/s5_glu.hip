@@ -10,6 +10,8 @@
 // three products), with the epilogue's multiplier (GELU(y) or y, float32)
 // beside them. The epilogue adds the bias, applies the logistic gate and the
 // multiplier and stores the result, all in the same pass.
+#include <algorithm>
+
 #include "s5_common.h"
 #include "s5_internal.h"
 
@@ -252,9 +254,12 @@ hipError_t launch_glu(const GluArgs& a, hipStream_t stream) {
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   const int ntiles = (a.T + kGluTokens - 1) / kGluTokens;
-  const int grid = ntiles < 4 * ncu ? ntiles : 4 * ncu;
-  const size_t lds = glu_lds_bytes(a.H, a.bf16_io);
   const bool small = a.H <= 128;
+  // every workgroup reads and converts W once: the large instance (W of up
+  // to 256 KB) takes at least four tiles per workgroup where the tiles allow
+  int grid = ntiles < 4 * ncu ? ntiles : 4 * ncu;
+  if (!small) grid = std::max(std::min(ntiles, ncu), std::min(grid, (ntiles + 3) / 4));
+  const size_t lds = glu_lds_bytes(a.H, a.bf16_io);
   if (a.bf16_io) return small ? glu_go<k_glu<true, true>>(a, grid, lds, stream) : glu_go<k_glu<true, false>>(a, grid, lds, stream);
   return small ? glu_go<k_glu<false, true>>(a, grid, lds, stream) : glu_go<k_glu<false, false>>(a, grid, lds, stream);
 }
