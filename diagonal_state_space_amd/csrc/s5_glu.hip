@@ -100,10 +100,18 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
 #pragma unroll
     for (int s = 0; s < kGluMaxKS; ++s) {
       f32x8 f;
+      const int k0 = 32 * s + 8 * (l >> 4);
+      if (m < HM && s < KS && j < q.H && k0 + 8 <= q.H && q.H % 4 == 0) {
+        // whole row segment, 16-byte aligned: two vector loads
+        const float4* p = reinterpret_cast<const float4*>(q.w + static_cast<size_t>(j) * q.H + k0);
+        const float4 a = p[0], b = p[1];
+        f = f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = 32 * s + 8 * (l >> 4) + i;
-        f[i] = (m < HM && s < KS && j < q.H && k < q.H) ? q.w[static_cast<size_t>(j) * q.H + k] : 0.0f;
+        for (int i = 0; i < 8; ++i) {
+          const int k = k0 + i;
+          f[i] = (m < HM && s < KS && j < q.H && k < q.H) ? q.w[static_cast<size_t>(j) * q.H + k] : 0.0f;
+        }
       }
       const bf16x8 hi = __builtin_convertvector(f, bf16x8);
       wf[mt][s][0] = hi;
@@ -255,9 +263,10 @@ hipError_t launch_glu(const GluArgs& a, hipStream_t stream) {
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   const int ntiles = (a.T + kGluTokens - 1) / kGluTokens;
   const bool small = a.H <= 128;
-  // every workgroup reads and converts W once: the large instance (W of up
-  // to 256 KB) takes at least four tiles per workgroup where the tiles allow
-  int grid = ntiles < 4 * ncu ? ntiles : 4 * ncu;
+  // every workgroup reads and converts W once, so the grid stays at two
+  // workgroups per CU (measured: 4 and 8 per CU were slower); the large
+  // instance (W of up to 256 KB) takes at least four tiles per workgroup
+  int grid = ntiles < 2 * ncu ? ntiles : 2 * ncu;
   if (!small) grid = std::max(std::min(ntiles, ncu), std::min(grid, (ntiles + 3) / 4));
   const size_t lds = glu_lds_bytes(a.H, a.bf16_io);
   if (a.bf16_io) return small ? glu_go<k_glu<true, true>>(a, grid, lds, stream) : glu_go<k_glu<true, false>>(a, grid, lds, stream);
