@@ -229,3 +229,18 @@ def test_glu_validation():
     assert _glu(out=FAKE + 0x2000) == INVALID      # out overlaps the bias
     assert _glu(y=FAKE + 8) == UNSUPPORTED         # misaligned
     assert _glu(T=0) == OK                         # no-op
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_compiles_standalone(tmp_path, lang, std):
+    """include/s5.h needs no HIP headers: plain C and C++ callers can include it."""
+    import shutil
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / "use.c"
+    src.write_text('#include "s5.h"\nint s5_probe(void) { s5_forward_desc d; d.size = sizeof d; '
+                   'return (int)d.size + S5_FLAG_BIDIRECTIONAL + S5_GLU_MAX_H; }\n')
+    r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.dirname(HEADER)}",
+                        "-c", str(src), "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
