@@ -244,3 +244,21 @@ def test_header_compiles_standalone(tmp_path, lang, std):
     r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.dirname(HEADER)}",
                         "-c", str(src), "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # a copy of the package with no libs5.so: the first call raises, there is
+    # no other code path to fall back on
+    import shutil
+    pkg = os.path.join(ROOT, "diagonal_state_space_amd")
+    shutil.copytree(pkg, tmp_path / "diagonal_state_space_amd",
+                    ignore=shutil.ignore_patterns("*.so", "csrc", "__pycache__", "_build"))
+    code = ("import diagonal_state_space_amd as s5, torch\n"
+            "try:\n"
+            "    s5.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                         env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert "raised" in out.stdout and "libs5.so not found" in out.stdout
