@@ -17,9 +17,11 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
   // 16 MPW NP fragments of 16 bytes per lane. Pass 1 (eight waves, each with
   // half the mode tiles) keeps them up to MPW NP = 4; pass 2 (two waves per
-  // SIMD, 256 registers each) up to MPW NP = 4, or 2 with the time-varying step
+  // SIMD, 256 registers each) up to MPW NP = 4, and with the time-varying step
+  // (its interval registers and discretisation beside the weights) up to two
+  // mode tiles per wave
   bool keep = KS <= 4 && MPW * NP <= 4;
-  bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW * NP > 2);
+  bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
   // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
   if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
     if (env[0] == '0') keep = keep_scan = false;

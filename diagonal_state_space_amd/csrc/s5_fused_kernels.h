@@ -1635,13 +1635,15 @@ __device__ __forceinline__ void drive_scan_tiles(bool bil, int j0, int KS, const
   }
 }
 
-// one chunk of a drive wave, JG mode tiles at a time
+// one chunk of a drive wave, JG mode tiles at a time (one with float32 I/O
+// and the time-varying step, whose hi/lo weights and per-step registers
+// leave no room for a second tile's accumulators)
 template <int MPW, int R, bool TV, bool BF16>
 __device__ __forceinline__ void drive_scan_chunk(bool bil, int KS, const BKeep<MPW, BF16 ? 1 : 2>& bk, const lds_byte* ub,
                                                  const ModeTable& mt, const Lane& ln,
                                                  const float4 (&dl)[TV ? MPW : 1][TV ? R : 1],
                                                  cf (&st)[MPW][4], lds_byte* xb) {
-  constexpr int JG = MPW >= 4 ? 1 : (MPW < 2 ? MPW : 2);
+  constexpr int JG = (MPW >= 4 || (TV && !BF16)) ? 1 : (MPW < 2 ? MPW : 2);
   // the chunk's u fragments (K-steps past KS repeat the last real one against
   // zero weights): read from LDS once for all tile groups where registers
   // allow, else again for each group
