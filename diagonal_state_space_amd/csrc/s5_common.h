@@ -49,24 +49,29 @@ __device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
   cp = fmaf(x2, cp, 4.16666667e-2f);
   cp = fmaf(x2, cp, -0.5f);
   const float cx = fmaf(x2, cp, 1.0f);
-  const int q = static_cast<int>(qf) & 3;
-  s = (q == 0) ? sx : (q == 1) ? cx : (q == 2) ? -sx : -cx;
-  c = (q == 0) ? cx : (q == 1) ? -sx : (q == 2) ? -cx : sx;
+  // quadrant q (mod 4): odd q swaps the pair; bit 1 of q flips the sine's
+  // sign, bit 1 of q + 1 the cosine's (exact, and without branches)
+  const int q = static_cast<int>(qf);
+  const bool swap = (q & 1) != 0;
+  const float s0 = swap ? cx : sx;
+  const float c0 = swap ? sx : cx;
+  s = __uint_as_float(__float_as_uint(s0) ^ (static_cast<uint32_t>(q & 2) << 30));
+  c = __uint_as_float(__float_as_uint(c0) ^ (static_cast<uint32_t>((q + 1) & 2) << 30));
 }
 
 // e^r - 1: degree-8 Taylor polynomial for |r| < 1/2 (truncation < 3e-9
 // relative), exp(r) - 1 otherwise (no cancellation there).
 __device__ __forceinline__ float expm1_small(float r) {
-  if (fabsf(r) < 0.5f) {
-    float p = fmaf(r, 2.48015873e-5f, 1.98412698e-4f);
-    p = fmaf(r, p, 1.38888889e-3f);
-    p = fmaf(r, p, 8.33333333e-3f);
-    p = fmaf(r, p, 4.16666667e-2f);
-    p = fmaf(r, p, 1.66666667e-1f);
-    p = fmaf(r, p, 0.5f);
-    return fmaf(r * r, p, r);
-  }
-  return __expf(r) - 1.0f;
+  // both forms, then a select: a branch would split the wave's scan loop
+  float p = fmaf(r, 2.48015873e-5f, 1.98412698e-4f);
+  p = fmaf(r, p, 1.38888889e-3f);
+  p = fmaf(r, p, 8.33333333e-3f);
+  p = fmaf(r, p, 4.16666667e-2f);
+  p = fmaf(r, p, 1.66666667e-1f);
+  p = fmaf(r, p, 0.5f);
+  const float series = fmaf(r * r, p, r);
+  const float direct = __expf(r) - 1.0f;
+  return fabsf(r) < 0.5f ? series : direct;
 }
 
 // Zero-order hold of one mode for a per-step interval dt >= 0 (the
@@ -75,6 +80,10 @@ __device__ __forceinline__ float expm1_small(float r) {
 // The integer part of th is removed exactly (rint), so the angle's only error
 // is the rounding of th itself, the same as rounding w. Then as zoh_f32:
 //   abar - 1 = (expm1(r)(1 - 2 s^2) - 2 s^2,  e^r 2 s c),  gain = (abar - 1)/lam.
+// SEL computes the small-|z| form on every lane and selects it (no branch in
+// the caller's loop); otherwise it sits behind a branch that waves skip when
+// no lane needs it. Both give the same values.
+template <bool SEL = false>
 __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
   const float r = lam.re * dt;
   const float th = hrev * dt;
@@ -90,10 +99,11 @@ __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float d
   gain = cmul(am1, inv_lam);
   // |z| < 1e-4 (also covers lam = 0): dt * (1 + z/2 + z^2/6)
   const float w = lam.im * dt;
-  if (fabsf(r) + fabsf(w) < 1e-4f) {
+  const bool tiny = fabsf(r) + fabsf(w) < 1e-4f;
+  if (SEL || tiny) {
     const float hr = 0.5f * r + (r * r - w * w) * (1.0f / 6.0f);
     const float hi = 0.5f * w + (2.0f * r * w) * (1.0f / 6.0f);
-    gain = {dt * (1.0f + hr), dt * hi};
+    gain = {tiny ? dt * (1.0f + hr) : gain.re, tiny ? dt * hi : gain.im};
   }
 }
 
@@ -110,11 +120,12 @@ __device__ __forceinline__ void bilinear_step(cf lam, float dt, cf& abar, cf& ga
 }
 
 // one per-step discretisation: bilinear when `bil`, else zero-order hold
+template <bool SEL = false>
 __device__ __forceinline__ void disc_step(bool bil, cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
   if (bil) {
     bilinear_step(lam, dt, abar, gain);
   } else {
-    zoh_step(lam, inv_lam, hrev, dt, abar, gain);
+    zoh_step<SEL>(lam, inv_lam, hrev, dt, abar, gain);
   }
 }
 

@@ -1602,7 +1602,7 @@ __device__ __forceinline__ void drive_scan_tiles(bool bil, int j0, int KS, const
 #pragma unroll
         for (int n = 0; n < R; ++n) {
           cf a, gn;
-          disc_step(bil, lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
+          disc_step<true>(bil, lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
           x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
           acc[jj][0][n][r] = x.re;
           acc[jj][1][n][r] = x.im;
