@@ -131,6 +131,7 @@ __device__ __forceinline__ void disc_step(bool bil, cf lam, cf inv_lam, float hr
 
 // ---- MFMA operand types and helpers ----------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 

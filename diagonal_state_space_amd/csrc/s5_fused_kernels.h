@@ -214,6 +214,10 @@ __device__ __forceinline__ void write_final_state(const FusedParams& q, int b, c
 // 8 bf16, or 4 floats per half (halves 0 and 1 = elements 0-3 and 4-7). Wave w
 // moves blocks w, w + 4, ...: fetch_u loads them into registers a chunk ahead,
 // stash_u writes them to LDS before the barrier that publishes the tile.
+// SPLIT (float32 u, pass 1): the same bytes hold instead the two bf16 planes
+// of the drive's operands, hi and lo (u = hi + lo to 2^-17), split once when
+// the tile is staged rather than by each of the eight waves that read it.
+// Pass 2 keeps the floats: its D u feedthrough reads u itself.
 // (Copies straight from global memory to LDS were measured slower here: every
 // LDS access after one waits for it.)
 //
@@ -348,7 +352,7 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rs
   }
 }
 
-template <int R, bool BF16, int NB, int NWV>
+template <int R, bool BF16, int NB, int NWV, bool SPLIT = false>
 __device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& st, lds_byte* ub) {
   Lane ln = lane_ids();
   if constexpr (NWV != kWaves) ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NWV - 1);
@@ -364,17 +368,34 @@ __device__ __forceinline__ void stash_u(const FusedParams& q, const UStage<NB>& 
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       continue;
     }
-    lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
+    if constexpr (BF16 || !SPLIT) {
+      lds_st<uint4>(ub + blk * kBlock + ln.l * 16, st.v[e]);
+    } else {
+      // the bf16 hi and lo operand planes of the fragment (blocks 2f and
+      // 2f + 1), this half's four elements at bytes 8 half .. 8 half + 7 of
+      // the lane's slot
+      const int half = blk & 1;
+      const int f = blk >> 1;
+      const f32x4 v = {__uint_as_float(st.v[e].x), __uint_as_float(st.v[e].y), __uint_as_float(st.v[e].z),
+                       __uint_as_float(st.v[e].w)};
+      const bf16x4 hi = __builtin_convertvector(v, bf16x4);
+      const bf16x4 lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
+      lds_st<uint2>(ub + (2 * f) * kBlock + ln.l * 16 + 8 * half, __builtin_bit_cast(uint2, hi));
+      lds_st<uint2>(ub + (2 * f + 1) * kBlock + ln.l * 16 + 8 * half, __builtin_bit_cast(uint2, lo));
+    }
   }
 }
 
 // drive operand fragments of K-step s from the u tile: [plane][n]
-template <int R, bool BF16>
+template <int R, bool BF16, bool SPLIT = false>
 __device__ __forceinline__ void get_u(const lds_byte* ub, int s, int l, bf16x8 (&uf)[BF16 ? 1 : 2][R]) {
 #pragma unroll
   for (int n = 0; n < R; ++n) {
     if constexpr (BF16) {
       uf[0][n] = as_bf16x8(lds_ld<uint4>(ub + (s * R + n) * kBlock + l * 16));
+    } else if constexpr (SPLIT) {
+      uf[0][n] = as_bf16x8(lds_ld<uint4>(ub + ((s * R + n) * 2) * kBlock + l * 16));
+      uf[1][n] = as_bf16x8(lds_ld<uint4>(ub + ((s * R + n) * 2 + 1) * kBlock + l * 16));
     } else {
       const float4 a = lds_ld<float4>(ub + ((s * R + n) * 2) * kBlock + l * 16);
       const float4 c = lds_ld<float4>(ub + ((s * R + n) * 2 + 1) * kBlock + l * 16);
@@ -442,7 +463,7 @@ __device__ __forceinline__ void load_b_keep(const FusedParams& q, int w, int l, 
   }
 }
 
-template <int MPW, int R, bool BF16, bool KEEP>
+template <int MPW, int R, bool BF16, bool KEEP, bool SPLIT = false>
 __device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF16 ? 1 : 2>& bk,
                                       const lds_byte* ub, int w, int l, f32x4 (&acc)[MPW][2][R]) {
   constexpr int NP = BF16 ? 1 : 2;
@@ -459,7 +480,7 @@ __device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF1
 #pragma unroll
     for (int s = 0; s < kKeepKS; ++s) {
       bf16x8 uf[NP][R];
-      get_u<R, BF16>(ub, s < KS ? s : KS - 1, l, uf);
+      get_u<R, BF16, SPLIT>(ub, s < KS ? s : KS - 1, l, uf);
       mfma_drive<MPW, R, NP>(bk.f[s], uf, acc);
     }
   } else {
@@ -469,7 +490,7 @@ __device__ __forceinline__ void drive(const FusedParams& q, const BKeep<MPW, BF1
       bf16x8 an[MPW][2][NP];
       if (s + 1 < KS) load_b_step<MPW, NP>(q, w, l, s + 1, an);
       bf16x8 uf[NP][R];
-      get_u<R, BF16>(ub, s, l, uf);
+      get_u<R, BF16, SPLIT>(ub, s, l, uf);
       mfma_drive<MPW, R, NP>(a, uf, acc);
       if (s + 1 < KS) {
 #pragma unroll
@@ -598,7 +619,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
   {
     UStage<NB> ust;
     fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, 0, ust);
-    stash_u<R, BF16, NB, kWaves>(q, ust, lds);
+    stash_u<R, BF16, NB, kWaves, !BF16>(q, ust, lds);
   }
   lds_barrier();
   for (int i = 0; i < q.nck; ++i) {
@@ -612,7 +633,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     UStage<NB> ust;
     fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 1, ust);
     f32x4 acc[MPW][2][R];
-    drive<MPW, R, BF16, KEEP>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
+    drive<MPW, R, BF16, KEEP, !BF16>(q, bk, lds + (i & 1) * ut, ln.w, ln.l, acc);
     const bool rec = cap_chunk == i;   // this chunk holds token L-1 (uniform)
 #pragma unroll
     for (int jj = 0; jj < MPW; ++jj) {
@@ -647,7 +668,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
     }
     // u tile i+1 into the buffer that drive(i-1) read before the last barrier
     __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after this chunk's work
-    stash_u<R, BF16, NB, kWaves>(q, ust, lds + ((i + 1) & 1) * ut);
+    stash_u<R, BF16, NB, kWaves, !BF16>(q, ust, lds + ((i + 1) & 1) * ut);
     lds_barrier();
     if constexpr (TV) {
 #pragma unroll
@@ -786,7 +807,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll
     for (int s = 0; s < kKeepKS; ++s) {
       bf16x8 uf[NP][R];
-      get_u<R, BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
+      get_u<R, BF16, !BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
 #pragma unroll
       for (int m = 0; m < M8; ++m)
 #pragma unroll
@@ -855,7 +876,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll
       for (int c = 0; c < G; ++c) fetch_u<R, BF16, NB, NW8, VEC>(q, ursrc, rmap, qq, c, ust[c]);
 #pragma unroll
-      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8>(q, ust[c], lds + c * ut);
+      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8, !BF16>(q, ust[c], lds + c * ut);
     }
     lds_barrier();   // mode table, u tiles of group 0
     for (int i0 = 0; i0 < q.nck; i0 += G) {
@@ -883,7 +904,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       // before the last barrier)
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the group's work
 #pragma unroll
-      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8>(q, ust[c], lds + ((1 - half) * G + c) * ut);
+      for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8, !BF16>(q, ust[c], lds + ((1 - half) * G + c) * ut);
       lds_barrier();
     }
   };
