@@ -33,9 +33,11 @@ __device__ __forceinline__ cf cfma(cf a, cf x, cf b) {
   return {fmaf(a.re, x.re, fmaf(-a.im, x.im, b.re)), fmaf(a.re, x.im, fmaf(a.im, x.re, b.im))};
 }
 
-// sin and cos of 2*pi*t for |t| <= 1/2 revolution (t exact): octant
-// reduction to |x| <= pi/4, then Taylor polynomials (truncation below 3e-8
-// absolute; relative accuracy is kept for small t).
+// sin and cos of 2*pi*t for t in revolutions (t exact, |4 t| < 2^31):
+// quarter-turn reduction to |x| <= pi/4 (f = t - q/4 is exact: for
+// |t| > 1/8, q/4 is a multiple of ulp(t) and |f| <= 1/8 < |t|; otherwise
+// q = 0), then Taylor polynomials
+// (truncation below 3e-8 absolute; relative accuracy is kept for small t).
 __device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
   const float qf = rintf(4.0f * t);               // quadrant, -2..2
   const float f = fmaf(-0.25f, qf, t);            // exact: |f| <= 1/8
@@ -51,7 +53,7 @@ __device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
   const float cx = fmaf(x2, cp, 1.0f);
   // quadrant q (mod 4): odd q swaps the pair; bit 1 of q flips the sine's
   // sign, bit 1 of q + 1 the cosine's (exact, and without branches)
-  const int q = static_cast<int>(qf);
+  const int q = __float2int_rz(qf);   // saturating hardware conversion
   const bool swap = (q & 1) != 0;
   const float s0 = swap ? cx : sx;
   const float c0 = swap ? sx : cx;
@@ -77,8 +79,9 @@ __device__ __forceinline__ float expm1_small(float r) {
 // Zero-order hold of one mode for a per-step interval dt >= 0 (the
 // time-varying path), with the half-angle taken in revolutions:
 //   w/2 = Im(lam) dt / 2 = 2 pi th,  th = dt * Im(lam)/(4 pi) = dt * hrev.
-// The integer part of th is removed exactly (rint), so the angle's only error
-// is the rounding of th itself, the same as rounding w. Then as zoh_f32:
+// Whole turns of th drop out exactly in the quarter-turn reduction, so the
+// angle's only error is the rounding of th itself, the same as rounding w.
+// Then as zoh_f32:
 //   abar - 1 = (expm1(r)(1 - 2 s^2) - 2 s^2,  e^r 2 s c),  gain = (abar - 1)/lam.
 // SEL computes the small-|z| form on every lane and selects it (no branch in
 // the caller's loop); otherwise it sits behind a branch that waves skip when
@@ -88,7 +91,7 @@ __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float d
   const float r = lam.re * dt;
   const float th = hrev * dt;
   float s, c;
-  sincos_rev(th - rintf(th), s, c);
+  sincos_rev(th, s, c);
   const float em1 = expm1_small(r);
   const float er = em1 + 1.0f;
   const float two_s2 = 2.0f * s * s;
