@@ -208,8 +208,8 @@ def pin_half_spectrum():
 
 def pin_scan_bracketings():
     """Every bracketing of the operator over L <= 7 elements gives the state of
-    the sequential loop, and a recursive pairwise prefix scan (all prefixes,
-    odd lengths included) matches every step of the loop."""
+    the sequential loop, and two log-depth prefix scans (all prefixes, lengths
+    that are not powers of two included) match every step of the loop."""
     rng = _rng(7)
     P = 3
     err = 0.0
@@ -230,23 +230,38 @@ def pin_scan_bracketings():
         for tree in all_trees(0, L):
             err = max(err, _rel(tree[1], xs[-1]))
 
-        def prefix(items):
-            if len(items) <= 1:
-                return list(items)
-            paired = [orc.compose(items[i], items[i + 1]) for i in range(0, len(items) - 1, 2)]
-            pre = prefix(paired)
-            out = []
-            for i, it in enumerate(items):
-                if i % 2 == 1:
-                    out.append(pre[i // 2])
-                elif i == 0:
-                    out.append(it)
-                else:
-                    out.append(orc.compose(pre[i // 2 - 1], it))
-            return out
-
-        pre = prefix([(a[i], b[i]) for i in range(L)])
-        err = max(err, _rel(np.array([p[1] for p in pre]), xs))
+        # Two log-depth scans of the pairs, each a different bracketing of
+        # the same products. Work-efficient form: an up-sweep that combines
+        # neighbouring subtrees at strides 1, 2, 4, ..., then a down-sweep
+        # that hands every subtree the combination of all pairs before it
+        # (the input padded with the identity map (1, 0) to a power of two).
+        # Step-doubling form: at each stride d every prefix absorbs the
+        # prefix d places before it.
+        one = (np.ones(P, np.complex128), np.zeros(P, np.complex128))
+        items = [(a[i], b[i]) for i in range(L)]
+        n = 1 << (L - 1).bit_length()
+        tree = items + [one] * (n - L)
+        stride = 1
+        while stride < n:
+            for right in range(2 * stride - 1, n, 2 * stride):
+                tree[right] = orc.compose(tree[right - stride], tree[right])
+            stride *= 2
+        tree[n - 1] = one
+        while stride > 1:
+            stride //= 2
+            for right in range(2 * stride - 1, n, 2 * stride):
+                before, left_total = tree[right], tree[right - stride]
+                tree[right - stride] = before
+                tree[right] = orc.compose(before, left_total)
+        up_down = [orc.compose(tree[i], items[i]) for i in range(L)]
+        doubling = list(items)
+        stride = 1
+        while stride < L:
+            doubling = [doubling[i] if i < stride else orc.compose(doubling[i - stride], doubling[i])
+                        for i in range(L)]
+            stride *= 2
+        for pre in (up_down, doubling):
+            err = max(err, _rel(np.array([p[1] for p in pre]), xs))
     return err
 
 
@@ -593,6 +608,42 @@ def test_golden_bilinear_scalar():
         assert abs(lb.real - expect) <= 0.5 * 10.0 ** (-dec) and abs(lb.imag) < 1e-15
 
 
+def _s4_two_state_system():
+    """The S4 page's two-state example in the form the S5 oracle takes: the
+    HiPPO-LegS matrix of size 2 (eigenvalues -1, -2) and its input vector
+    B_n = (2n+1)^(1/2), diagonalised numerically (A = V diag(lam) V^-1), so
+    that B~ = V^-1 B and C~ = C V with C = [1 0]. The bilinear map is a
+    rational function of A, so it commutes with the change of basis."""
+    a = wl.hippo_legs(2)
+    bvec = np.sqrt(2.0 * np.arange(2) + 1.0)
+    lam, v = np.linalg.eig(a)
+    bt = np.linalg.solve(v, bvec)[:, None].astype(np.complex128)
+    ct = (np.array([[1.0, 0.0]]) @ v).astype(np.complex128)
+    return lam.astype(np.complex128), bt, ct
+
+
+def pin_s4_two_state_pulse():
+    """S4 page, section "An LTI system computes a convolution": the bilinear
+    two-state system at step size 1 gives the printed kernel (2/3)(1/3)^i as
+    its impulse response and the pulse outputs 2/3, 8/9, 26/27, 80/81, then a
+    decay by 3 per step (tests/golden/s4_bilinear_n2_pulse.txt)."""
+    ref = _load_golden("s4_bilinear_n2_pulse.txt")
+    lam, bt, ct = _s4_two_state_system()
+    logd = np.zeros(2)                       # Delta = 1
+    n = ref.shape[0]
+    u = ref[:, 1].reshape(1, n, 1)
+    y, _ = orc.forward_ex(u, lam, bt, ct, np.zeros(1), log_delta=logd, method="bilinear")
+    imp = np.zeros((1, n, 1))
+    imp[0, 0, 0] = 1.0
+    k, _ = orc.forward_ex(imp, lam, bt, ct, np.zeros(1), log_delta=logd, method="bilinear")
+    return max(float(np.max(np.abs(y[0, :, 0] - ref[:, 2] / ref[:, 3]))),
+               float(np.max(np.abs(k[0, :, 0] - ref[:, 4] / ref[:, 5]))))
+
+
+def test_golden_s4_two_state_pulse():
+    assert pin_s4_two_state_pulse() <= 1e-13
+
+
 def test_golden_zoh_scalar():
     for lre, lim, dt, expect in _load_golden("zoh_scalar.txt"):
         lb, _ = orc.zoh(lre + 1j * lim, dt)
@@ -858,6 +909,32 @@ def test_planted_bilinear_gain_without_backward_step(monkeypatch):
     monkeypatch.setattr(orc, "bilinear", lambda lam, delta: (good(lam, delta)[0],
                                                              np.broadcast_to(orc.check_intervals(delta), np.shape(good(lam, delta)[1])).astype(np.complex128)))
     assert _fails("bilinear_trapezoid") and _fails("bilinear_equilibrium")
+
+
+def test_planted_bilinear_gain_without_backward_step_trips_s4_example(monkeypatch):
+    good = orc.bilinear
+    monkeypatch.setattr(orc, "bilinear", lambda lam, delta: (good(lam, delta)[0],
+                                                             np.broadcast_to(orc.check_intervals(delta), np.shape(good(lam, delta)[1])).astype(np.complex128)))
+    assert pin_s4_two_state_pulse() > 1e-3
+
+
+def test_planted_bilinear_replaced_by_zoh_trips_s4_example(monkeypatch):
+    monkeypatch.setattr(orc, "bilinear", orc.zoh)
+    assert pin_s4_two_state_pulse() > 1e-3
+
+
+def test_planted_bilinear_forward_step_only_trips_s4_example(monkeypatch):
+    # Lambda_bar = 1 + z/2 without the backward half-step
+    good = orc.bilinear
+    monkeypatch.setattr(orc, "bilinear", lambda lam, delta: (1.0 + 0.5 * np.asarray(lam) * orc.check_intervals(delta),
+                                                             good(lam, delta)[1]))
+    assert pin_s4_two_state_pulse() > 1e-3
+
+
+def test_planted_compose_order_swapped(monkeypatch):
+    monkeypatch.setattr(orc, "compose", lambda earlier, later: (earlier[0] * later[0],
+                                                               earlier[0] * later[1] + earlier[1]))
+    assert _fails("bracketings")
 
 
 def test_planted_backward_scan_exclusive(monkeypatch):
