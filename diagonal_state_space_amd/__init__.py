@@ -50,6 +50,7 @@ FLAG_HALF_SPECTRUM = 1 << 0
 FLAG_BILINEAR = 1 << 1
 FLAG_GELU = 1 << 2
 FLAG_BIDIRECTIONAL = 1 << 3
+FLAG_GELU_TANH = 1 << 4
 
 
 class ForwardDesc(ctypes.Structure):
@@ -245,7 +246,7 @@ def forward_timevarying_stateful(u, lam, b_tilde, c_tilde, d, delta, x0=None, y=
 
 def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None, *,
                half_spectrum=False, bilinear=False, gelu=False, bidirectional=False,
-               final_state=False, y=None, x_last=None, stream=None):
+               final_state=False, gelu_tanh=False, y=None, x_last=None, stream=None):
     """The forward pass with its options (s5_forward_ex): exactly one of
     log_delta [P] (time-invariant) and delta [B, L, P] (time-varying);
     c_tilde [H, 2P] when bidirectional. Returns (y, x_last), x_last None
@@ -278,7 +279,8 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
     if x_last is not None:
         _dev_tensor(x_last, "x_last", torch.complex64, (B, P))
     flags = ((FLAG_HALF_SPECTRUM if half_spectrum else 0) | (FLAG_BILINEAR if bilinear else 0) |
-             (FLAG_GELU if gelu else 0) | (FLAG_BIDIRECTIONAL if bidirectional else 0))
+             (FLAG_GELU if gelu else 0) | (FLAG_BIDIRECTIONAL if bidirectional else 0) |
+             (FLAG_GELU_TANH if gelu_tanh else 0))
     desc = ForwardDesc(ctypes.sizeof(ForwardDesc), flags, io, B, L, H, P, u.data_ptr(), lam.data_ptr(),
                        b_tilde.data_ptr(), c_tilde.data_ptr(), d.data_ptr(),
                        log_delta.data_ptr() if log_delta is not None else None,
@@ -289,7 +291,7 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
 
 
 def step(u, lam, b_tilde, c_tilde, d, x, log_delta=None, delta=None, *, half_spectrum=False,
-         bilinear=False, gelu=False, y=None, stream=None):
+         bilinear=False, gelu=False, gelu_tanh=False, y=None, stream=None):
     """One recurrent step (s5_step): u [B, H]; x [B, P] complex64 updated in
     place; exactly one of log_delta [P] and delta [B, P]. Returns y [B, H]."""
     import torch
@@ -314,7 +316,7 @@ def step(u, lam, b_tilde, c_tilde, d, x, log_delta=None, delta=None, *, half_spe
         y = torch.empty_like(u)
     _dev_tensor(y, "y", u.dtype, (B, H))
     flags = ((FLAG_HALF_SPECTRUM if half_spectrum else 0) | (FLAG_BILINEAR if bilinear else 0) |
-             (FLAG_GELU if gelu else 0))
+             (FLAG_GELU if gelu else 0) | (FLAG_GELU_TANH if gelu_tanh else 0))
     _check(lib().s5_step(B, H, P, io, flags, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
                          c_tilde.data_ptr(), d.data_ptr(),
                          log_delta.data_ptr() if log_delta is not None else None,

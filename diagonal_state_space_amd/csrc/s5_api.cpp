@@ -121,7 +121,7 @@ s5_status check_sizes(int64_t P, int64_t H) {
 struct Options {
   float c_scale = 1.0f;    // readout factor: 2 for half-spectrum storage
   bool bilinear = false;   // bilinear discretisation
-  bool gelu = false;       // GELU epilogue
+  int gelu = 0;            // GELU epilogue: 0 no, 1 exact form, 2 tanh form
   bool bidir = false;      // forward and backward scans, C~ with 2P columns
 };
 
@@ -206,17 +206,17 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.xlast = reinterpret_cast<float2*>(x_last);
   a.c_scale = opt.c_scale;
   a.bilinear = opt.bilinear;
-  a.gelu = opt.gelu && !opt.bidir;
+  a.gelu = opt.bidir ? 0 : opt.gelu;
   a.c_ld = static_cast<int>(c_cols);
 
-  if (!s5::forward_supported(a)) return S5_ERR_UNSUPPORTED;
+  s5::ForwardLayout lay;
+  if (!s5::forward_layout(a, lay)) return S5_ERR_UNSUPPORTED;
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
-  const size_t bytes = s5::forward_workspace_bytes(a);
   Scratch* ws = nullptr;
-  hipError_t e = scratch_acquire(bytes, stream, &ws);
+  hipError_t e = scratch_acquire(lay.total, stream, &ws);
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
-  e = s5::launch_forward(a, ws->ptr, stream, tl_events, tl_nevents);
+  e = s5::launch_forward(a, lay, ws->ptr, stream, tl_events, tl_nevents);
   if (e == hipSuccess && opt.bidir) {
     // backward scan: reverse time, second half of C~, no feedthrough (the
     // forward pass added it), added to the forward pass's y; then GELU
@@ -227,7 +227,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
     r.accum = true;
     r.gelu = opt.gelu;
     const int skip = 6;   // events of the forward pass's three launches
-    e = s5::launch_forward(r, ws->ptr, stream, tl_nevents > skip ? tl_events + skip : nullptr,
+    e = s5::launch_forward(r, lay, ws->ptr, stream, tl_nevents > skip ? tl_events + skip : nullptr,
                            tl_nevents > skip ? tl_nevents - skip : 0);
   }
   const hipError_t ef = scratch_release(ws, stream);
@@ -261,7 +261,7 @@ s5_status s5_discretize(int64_t P, int64_t H, const s5_c64* lambda, const s5_c64
   const hipError_t e = s5::launch_discretize(
       static_cast<int>(P), static_cast<int>(H), reinterpret_cast<const float2*>(lambda),
       reinterpret_cast<const float2*>(b_tilde), log_delta, reinterpret_cast<float2*>(lambda_bar),
-      reinterpret_cast<float2*>(b_bar), nullptr, 0, nullptr, stream);
+      reinterpret_cast<float2*>(b_bar), stream);
   return e == hipSuccess ? S5_OK : S5_ERR_HIP;
 }
 
@@ -298,13 +298,15 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
 
 s5_status s5_forward_ex(const s5_forward_desc* x, hipStream_t stream) {
   if (x == nullptr || x->size != sizeof(s5_forward_desc)) return S5_ERR_INVALID_ARGUMENT;
-  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_BIDIRECTIONAL;
+  const uint32_t known =
+      S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_BIDIRECTIONAL | S5_FLAG_GELU_TANH;
   if ((x->flags & ~known) != 0) return S5_ERR_INVALID_ARGUMENT;
+  if ((x->flags & S5_FLAG_GELU) && (x->flags & S5_FLAG_GELU_TANH)) return S5_ERR_INVALID_ARGUMENT;
   if ((x->log_delta == nullptr) == (x->delta == nullptr)) return S5_ERR_INVALID_ARGUMENT;
   Options o;
   o.c_scale = (x->flags & S5_FLAG_HALF_SPECTRUM) ? 2.0f : 1.0f;
   o.bilinear = (x->flags & S5_FLAG_BILINEAR) != 0;
-  o.gelu = (x->flags & S5_FLAG_GELU) != 0;
+  o.gelu = (x->flags & S5_FLAG_GELU) ? 1 : (x->flags & S5_FLAG_GELU_TANH) ? 2 : 0;
   o.bidir = (x->flags & S5_FLAG_BIDIRECTIONAL) != 0;
   return forward_common(x->B, x->L, x->H, x->P, x->io, x->u, x->lambda, x->b_tilde, x->c_tilde, x->d,
                         x->log_delta, x->delta, x->y, x->delta != nullptr, x->x0, x->x_last, o, stream);
@@ -317,8 +319,9 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
   s5_status st = check_sizes(P, H);
   if (st != S5_OK) return st;
   if (io != S5_F32 && io != S5_BF16) return S5_ERR_UNSUPPORTED;
-  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU;
+  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_GELU_TANH;
   if ((flags & ~known) != 0) return S5_ERR_INVALID_ARGUMENT;   // no backward scan in a single step
+  if ((flags & S5_FLAG_GELU) && (flags & S5_FLAG_GELU_TANH)) return S5_ERR_INVALID_ARGUMENT;
   if ((log_delta == nullptr) == (delta == nullptr)) return S5_ERR_INVALID_ARGUMENT;
   if (!lambda || !b_tilde || !c_tilde || !d) return S5_ERR_INVALID_ARGUMENT;
   if (B > 0 && (!u || !x || !y)) return S5_ERR_INVALID_ARGUMENT;
@@ -345,7 +348,7 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
   a.P = static_cast<int>(P);
   a.bf16_io = io == S5_BF16;
   a.bilinear = (flags & S5_FLAG_BILINEAR) != 0;
-  a.gelu = (flags & S5_FLAG_GELU) != 0;
+  a.gelu = (flags & S5_FLAG_GELU) ? 1 : (flags & S5_FLAG_GELU_TANH) ? 2 : 0;
   a.c_scale = (flags & S5_FLAG_HALF_SPECTRUM) ? 2.0f : 1.0f;
   a.u = u;
   a.lam = reinterpret_cast<const float2*>(lambda);

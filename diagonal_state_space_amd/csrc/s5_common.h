@@ -33,13 +33,15 @@ __device__ __forceinline__ cf cfma(cf a, cf x, cf b) {
   return {fmaf(a.re, x.re, fmaf(-a.im, x.im, b.re)), fmaf(a.re, x.im, fmaf(a.im, x.re, b.im))};
 }
 
-// sin and cos of 2*pi*t for t in revolutions (t exact, |4 t| < 2^31):
-// quarter-turn reduction to |x| <= pi/4 (f = t - q/4 is exact: for
-// |t| > 1/8, q/4 is a multiple of ulp(t) and |f| <= 1/8 < |t|; otherwise
-// q = 0), then Taylor polynomials
-// (truncation below 3e-8 absolute; relative accuracy is kept for small t).
+// sin and cos of 2*pi*t for t in revolutions, any finite t: quarter-turn
+// reduction to |x| <= pi/4 (f = t - q/4 is exact: for |t| > 1/8, q/4 is a
+// multiple of ulp(t) and |f| <= 1/8 < |t|; otherwise q = 0), then Taylor
+// polynomials (truncation below 3e-8 absolute; relative accuracy is kept for
+// small t). The quadrant count q = rint(4t) is reduced modulo 4 while still a
+// float (exactly: both terms are integers and their difference is in
+// [-2, 2]), so that its conversion to an integer cannot saturate.
 __device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
-  const float qf = rintf(4.0f * t);               // quadrant, -2..2
+  const float qf = rintf(4.0f * t);               // quadrant count
   const float f = fmaf(-0.25f, qf, t);            // exact: |f| <= 1/8
   const float x = 6.28318530717958647692f * f;
   const float x2 = x * x;
@@ -53,7 +55,7 @@ __device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
   const float cx = fmaf(x2, cp, 1.0f);
   // quadrant q (mod 4): odd q swaps the pair; bit 1 of q flips the sine's
   // sign, bit 1 of q + 1 the cosine's (exact, and without branches)
-  const int q = __float2int_rz(qf);   // saturating hardware conversion
+  const int q = __float2int_rz(fmaf(-4.0f, rintf(0.25f * qf), qf));   // -2..2
   const bool swap = (q & 1) != 0;
   const float s0 = swap ? cx : sx;
   const float c0 = swap ? sx : cx;
@@ -132,6 +134,36 @@ __device__ __forceinline__ void disc_step(bool bil, cf lam, cf inv_lam, float hr
   }
 }
 
+// ---- GELU epilogue forms -------------------------------------------------------
+// Exact form: GELU(v) = v Phi(v), Phi the standard normal distribution
+// function, with erf from Abramowitz & Stegun's formula 7.1.26 (Handbook of
+// Mathematical Functions; absolute error below 1.5e-7): for z >= 0,
+// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) with
+// t = 1/(1 + p z). With z = |v|/sqrt2, Phi(|v|) = 1 - q/2 and Phi(-|v|) = q/2
+// for q = 1 - erf(z). Branch-free.
+__device__ __forceinline__ float gelu_erf(float v) {
+  const float z = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float half_q = 0.5f * t * poly * __expf(-z * z);
+  return v * (v >= 0.0f ? 1.0f - half_q : half_q);
+}
+
+// Tanh form: v/2 (1 + tanh(k)), k = sqrt(2/pi) (v + 0.044715 v^3), the
+// approximation that the App. A listing's library GELU applies by default.
+// Since (1 + tanh k)/2 = 1/(1 + e^-2k), it is v / (1 + e^-2k); for v -> -inf
+// the exponential overflows to inf and the result is -0.
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float k2 = v * fmaf(0.0713548162726f, v * v, 1.5957691216057f);   // 2k
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-k2));
+}
+
+// GELU form code: 0 none, 1 exact (erf), 2 tanh
+__device__ __forceinline__ float gelu_form(float v, int form) { return form == 2 ? gelu_tanh(v) : gelu_erf(v); }
+
 // ---- MFMA operand types and helpers ----------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -146,27 +178,6 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint4* p) { return *p; }
-
-// relaxed agent-scope accesses: not cached in the (per-XCD) L2
-__device__ __forceinline__ void st_agent(float2* p, cf v) {
-  const uint64_t bits = (static_cast<uint64_t>(__float_as_uint(v.im)) << 32) | __float_as_uint(v.re);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ cf ld_agent(const float2* p) {
-  const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-  return {__uint_as_float(static_cast<uint32_t>(bits)), __uint_as_float(static_cast<uint32_t>(bits >> 32))};
-}
-
-template <bool BF16>
-__device__ __forceinline__ float load_io(const void* p, size_t i) {
-  if constexpr (BF16) {
-    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  } else {
-    return static_cast<const float*>(p)[i];
-  }
-}
-
 
 // Write 8 float values as bf16 hi (and lo if `lo` is non-null) fragments.
 __device__ __forceinline__ void put_frag(const float (&v)[8], uint4* hi, uint4* lo) {

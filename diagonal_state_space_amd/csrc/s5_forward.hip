@@ -2,7 +2,6 @@
 // three launches (parameter packing, aggregate pass, state and output pass),
 // all on the caller's stream.
 #include <algorithm>
-#include <cstdlib>
 
 #include "s5_fused.h"
 #include "s5_internal.h"
@@ -20,12 +19,8 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   // SIMD, 256 registers each) up to MPW NP = 4, and with the time-varying step
   // (its interval registers and discretisation beside the weights) up to two
   // mode tiles per wave
-  bool keep = KS <= 4 && MPW * NP <= 4;
-  bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
-  // S5_KEEP_WEIGHTS=0 streams the weights from L2 instead (tuning)
-  if (const char* env = std::getenv("S5_KEEP_WEIGHTS")) {
-    if (env[0] == '0') keep = keep_scan = false;
-  }
+  const bool keep = KS <= 4 && MPW * NP <= 4;
+  const bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
   p.R = 0;
   // bf16 instances are compiled for R = 2 (which always fits); float32 ones
   // also for R = 1, taken where three u tiles and two x tiles of R = 2
@@ -79,12 +74,6 @@ namespace {
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-struct Layout {
-  FusedPlan plan;
-  int Ppad, Hpad;
-  size_t bpack, cpack, modes, sagg, sagg_a, tot, tot_a, cap, total;
-};
-
 int device_cus() {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -92,12 +81,14 @@ int device_cus() {
   return ncu;
 }
 
-Layout layout(const ForwardArgs& a) {
-  Layout l{};
+}  // namespace
+
+bool forward_layout(const ForwardArgs& a, ForwardLayout& l) {
+  l = ForwardLayout{};
   l.Ppad = ((a.P + 63) / 64) * 64;
   l.Hpad = ((a.H + 31) / 32) * 32;
   fused_shape(a.bf16_io, a.time_varying, l.Ppad, l.Hpad, l.plan);
-  if (l.plan.R == 0) return l;
+  if (l.plan.R == 0) return false;
   const int ncu = device_cus();
   fused_split(a.B, a.L, a.H, a.P, ncu > 0 ? ncu : 256, l.plan);
   const size_t planes = a.bf16_io ? 1 : 2;
@@ -114,8 +105,10 @@ Layout layout(const ForwardArgs& a) {
   l.tot_a = off;  off += align_up(nranges * l.Ppad * sizeof(float2));
   l.cap = off;    off += align_up(static_cast<size_t>(a.B) * 2 * l.Ppad * sizeof(float2));
   l.total = off;
-  return l;
+  return true;
 }
+
+namespace {
 
 using Launcher = hipError_t (*)(const FusedParams&, const FusedPlan&, hipStream_t);
 
@@ -142,17 +135,6 @@ hipError_t launch_scan(const FusedParams& q, const FusedPlan& p, hipStream_t s) 
   return q.time_varying ? launch_scan_f32_tv(q, p, s) : launch_scan_f32_ti(q, p, s);
 }
 
-size_t forward_workspace_bytes(const ForwardArgs& a) {
-  const Layout l = layout(a);
-  return l.plan.R == 0 ? 0 : l.total;
-}
-
-bool forward_supported(const ForwardArgs& a) {
-  FusedPlan p;
-  fused_shape(a.bf16_io, a.time_varying, ((a.P + 63) / 64) * 64, ((a.H + 31) / 32) * 32, p);
-  return p.R != 0;
-}
-
 namespace {
 __global__ void __launch_bounds__(256) k_state_passthrough(const float2* x0, float2* xlast, int64_t n) {
   for (int64_t k = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; k < n;
@@ -168,8 +150,8 @@ hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, 
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, const hipEvent_t* ev, int nev) {
-  const Layout l = layout(a);
+hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws, hipStream_t stream,
+                          const hipEvent_t* ev, int nev) {
   if (l.plan.R == 0) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   FusedParams q{};

@@ -71,7 +71,7 @@ struct FusedParams {
   int bilinear;       // bilinear instead of zero-order hold discretisation
   int rev;            // reverse time: token k is row L-1-k of u and y
   int accum;          // y += the readout (D u included when d is given)
-  int gelu;           // y = GELU(y) after the sum
+  int gelu;           // y = GELU(y) after the sum: 0 no, 1 exact form, 2 tanh form
   // workspace
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O)
   uint4* cpack;       // readout operand fragments (hi, then lo)
@@ -91,6 +91,14 @@ struct FusedPlan {
   bool keep_scan = false;   // pass 2 holds B_bar and C' in registers (wave-specialized kernel)
   int group = 1;            // nck is a multiple of this (reduce_group with `keep`)
   size_t lds_reduce = 0, lds_scan = 0, lds_reduce_ws = 0;
+};
+
+// Plan and workspace layout of one forward call (byte offsets into the
+// 256-byte aligned workspace; total = bytes needed).
+struct ForwardLayout {
+  FusedPlan plan;
+  int Ppad = 0, Hpad = 0;
+  size_t bpack = 0, cpack = 0, modes = 0, sagg = 0, sagg_a = 0, tot = 0, tot_a = 0, cap = 0, total = 0;
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).

@@ -287,7 +287,8 @@ __device__ __forceinline__ RowMap row_map(const FusedParams& q, int qq) {
   return {false, 0};
 }
 
-// Output epilogue by instance: XM = 2 always GELU; XM = 3 adds to y (the
+// Output epilogue by instance: XM = 2 always GELU (the form from q.gelu:
+// 1 exact, 2 tanh); XM = 3 adds to y (the
 // backward scan of the bidirectional form), then GELU if asked. The addition
 // reads y in the store path; a load there behind a runtime test would make
 // the compiler wait for every outstanding load (the prefetched u tiles) at
@@ -297,11 +298,12 @@ __device__ __forceinline__ RowMap row_map(const FusedParams& q, int qq) {
 struct Epi {
   bool accum;
   bool gelu;
+  bool tanh_form;   // GELU in its tanh form (else the exact form)
 };
 
 template <int XM>
 __device__ __forceinline__ Epi epilogue(const FusedParams& q) {
-  return {XM == 3, XM == 2 || (XM == 3 && q.gelu != 0)};
+  return {XM == 3, XM == 2 || (XM == 3 && q.gelu != 0), (XM == 2 || XM == 3) && q.gelu == 2};
 }
 
 template <int R, bool BF16, int NB, int NWV, bool VEC>
@@ -979,26 +981,11 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
 }
 
 // y = acc + D u for 4 consecutive features h0..h0+3 of one row (row offset
-// roff, in elements, inside the range descriptor yr); bf16 rounding by the
-// hardware conversion (round to nearest even). Rows past the sequence end
-// fall outside the descriptor and features >= H get an offset beyond it, so
-// the hardware drops those writes. VEC: H % 4 == 0, one vector store.
-// GELU(v) = v Phi(v), Phi the standard normal distribution function, with
-// erf from Abramowitz & Stegun's formula 7.1.26 (Handbook of Mathematical
-// Functions): for z >= 0, erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
-// exp(-z^2), t = 1/(1 + p z), absolute error below 1.5e-7. With z = |v|/sqrt2,
-// Phi(|v|) = 1 - q/2 and Phi(-|v|) = q/2 for q = 1 - erf(z). Branch-free.
-__device__ __forceinline__ float gelu_exact(float v) {
-  const float z = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float poly = fmaf(t, 1.061405429f, -1.453152027f);
-  poly = fmaf(t, poly, 1.421413741f);
-  poly = fmaf(t, poly, -0.284496736f);
-  poly = fmaf(t, poly, 0.254829592f);
-  const float half_q = 0.5f * t * poly * __expf(-z * z);
-  return v * (v >= 0.0f ? 1.0f - half_q : half_q);
-}
-
+// roff, in elements, inside the range descriptor yr), then the GELU form the
+// epilogue asks for; bf16 rounding by the hardware conversion (round to
+// nearest even). Rows past the sequence end fall outside the descriptor and
+// features >= H get an offset beyond it, so the hardware drops those writes.
+// VEC: H % 4 == 0, one vector store.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int h0, int H, const f32x4& acc,
                                         const float4& d4, const float (&uv)[4], const Epi& ep) {
@@ -1017,8 +1004,13 @@ __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int
       }
     }
     if (ep.gelu) {
+      if (ep.tanh_form) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) yv[m] = gelu_exact(yv[m]);
+        for (int m = 0; m < 4; ++m) yv[m] = gelu_tanh(yv[m]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) yv[m] = gelu_erf(yv[m]);
+      }
     }
     if constexpr (BF16) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -1040,7 +1032,7 @@ __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int
           yv[m] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(yr, off, 0, 0));
         }
       }
-      if (ep.gelu) yv[m] = gelu_exact(yv[m]);
+      if (ep.gelu) yv[m] = ep.tanh_form ? gelu_tanh(yv[m]) : gelu_erf(yv[m]);
       if constexpr (BF16) {
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(yv[m])), yr, off,
                                               0, 0);
@@ -1264,7 +1256,7 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
       f32x4 a = yacc[e][n];
       if constexpr (ACC) a += y_old_f32<BF16>(old->v[e][n]);
       store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, a, dk[e], uv[e][n],
-                         Epi{ACC ? false : ep.accum, ep.gelu});
+                         Epi{ACC ? false : ep.accum, ep.gelu, ep.tanh_form});
     }
   }
 }

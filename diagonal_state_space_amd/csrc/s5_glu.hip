@@ -30,19 +30,6 @@ constexpr int glu_ks() { return SMALL ? 4 : 8; }
 template <bool SMALL>
 constexpr int glu_mt() { return SMALL ? 1 : 2; }
 
-// GELU(v) = v Phi(v) with erf from Abramowitz & Stegun's formula 7.1.26
-// (|error| < 1.5e-7), branch-free: for z = |v|/sqrt2, t = 1/(1 + p z),
-// Phi(|v|) = 1 - q/2 and Phi(-|v|) = q/2, q = t (a1 + t (a2 + ...)) exp(-z^2)
-__device__ __forceinline__ float gelu_f(float v) {
-  const float z = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float poly = fmaf(t, 1.061405429f, -1.453152027f);
-  poly = fmaf(t, poly, 1.421413741f);
-  poly = fmaf(t, poly, -0.284496736f);
-  poly = fmaf(t, poly, 0.254829592f);
-  const float half_q = 0.5f * t * poly * __expf(-z * z);
-  return v * (v >= 0.0f ? 1.0f - half_q : half_q);
-}
 
 // 8 consecutive elements of y from element index idx (zeros past `count`);
 // vec: one 16-byte (bf16) or two 16-byte (float32) loads
@@ -155,7 +142,7 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
       for (int i = 0; i < 8; ++i) yv[i] = ynext[c][i];
       f32x8 f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = gelu_f(yv[i]);
+      for (int i = 0; i < 8; ++i) f[i] = gelu_erf(yv[i]);
       const bf16x8 hi = __builtin_convertvector(f, bf16x8);
       *reinterpret_cast<uint4*>(gblk(s, nt, 0) + l * 16) = as_u4(hi);
       if constexpr (NP == 2)

@@ -4,14 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "s5_fused.h"
+
 namespace s5 {
 
-// Discretisation (float64 inside). Any output pointer may be null.
+// Zero-order-hold discretisation (float64 inside): lam_bar [P], b_bar [P, H].
 hipError_t launch_discretize(int P, int H, const float2* lam, const float2* b_tilde,
-                             const float* log_delta, float2* lam_bar, float2* b_bar,
-                             float2* pow_out, int pow_n, float2* inv_lam, hipStream_t stream);
-
-hipError_t launch_inv_lambda(int P, const float2* lam, float2* out, hipStream_t stream);
+                             const float* log_delta, float2* lam_bar, float2* b_bar, hipStream_t stream);
 
 // Arguments of one forward call after validation on the host.
 struct ForwardArgs {
@@ -34,7 +33,7 @@ struct ForwardArgs {
   bool bilinear = false;        // bilinear discretisation
   bool rev = false;             // reverse time (the backward scan)
   bool accum = false;           // add the result to y
-  bool gelu = false;            // GELU of the final y
+  int gelu = 0;                 // GELU of the final y: 0 no, 1 exact form, 2 tanh form
 };
 
 // One recurrent step for B sequences (validated on the host): x [B, P] in
@@ -43,7 +42,7 @@ struct StepArgs {
   int B, H, P;
   bool bf16_io;
   bool bilinear;
-  bool gelu;
+  int gelu;   // 0 no GELU, 1 exact form, 2 tanh form
   float c_scale;
   const void* u;
   const float2* lam;
@@ -72,20 +71,18 @@ struct GluArgs {
 
 hipError_t launch_glu(const GluArgs& a, hipStream_t stream);
 
-// Bytes of stream-ordered scratch the forward path needs for these sizes.
-size_t forward_workspace_bytes(const ForwardArgs& a);
-
-// Whether a compiled kernel instance covers these sizes.
-bool forward_supported(const ForwardArgs& a);
+// Launch plan and workspace layout for these sizes, computed once per call;
+// false when no compiled kernel instance covers them.
+bool forward_layout(const ForwardArgs& a, ForwardLayout& l);
 
 // Zero-length sequences: the final state is the initial one (x0, or zero when
 // x0 is null); n = B*P complex values.
 hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, hipStream_t stream);
 
-// Enqueue the whole forward path on `stream` using `ws` (forward_workspace_bytes
-// bytes, 256-byte aligned). ev[2k] / ev[2k+1] are recorded around the k-th
-// kernel launch for k < nev/2.
-hipError_t launch_forward(const ForwardArgs& a, void* ws, hipStream_t stream, const hipEvent_t* ev,
-                          int nev);
+// Enqueue the whole forward path on `stream` using `ws` (l.total bytes,
+// 256-byte aligned), with the layout forward_layout gave for `a`. ev[2k] /
+// ev[2k+1] are recorded around the k-th kernel launch for k < nev/2.
+hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws, hipStream_t stream,
+                          const hipEvent_t* ev, int nev);
 
 }  // namespace s5

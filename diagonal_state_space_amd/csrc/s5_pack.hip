@@ -4,52 +4,14 @@
 // size"), the MFMA operand layouts of B_bar and C', and the per-mode
 // constants.
 #include "s5_common.h"
+#include "s5_f64.h"
 #include "s5_fused.h"
 
 namespace s5 {
 
 namespace {
 
-struct zd {
-  double re, im;
-};
-__device__ __forceinline__ zd zmul(zd a, zd b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
-__device__ __forceinline__ zd zdiv(zd a, zd b) {
-  const double den = b.re * b.re + b.im * b.im;
-  return {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
-}
-__device__ __forceinline__ zd zexp(zd z) {
-  const double e = exp(z.re);
-  double s, c;
-  sincos(z.im, &s, &c);
-  return {e * c, e * s};
-}
-
-// gain (exp(z)-1)/lambda, z = lambda*delta; 9-term phi1 series for |z| < 1e-4
-__device__ zd gain64(zd lam, double delta) {
-  const zd z = {lam.re * delta, lam.im * delta};
-  if (sqrt(z.re * z.re + z.im * z.im) < 1e-4) {
-    zd term = {1.0, 0.0}, phi = {1.0, 0.0};
-    for (int n = 1; n <= 8; ++n) {
-      term = zmul(term, z);
-      term.re /= (n + 1);
-      term.im /= (n + 1);
-      phi.re += term.re;
-      phi.im += term.im;
-    }
-    return {delta * phi.re, delta * phi.im};
-  }
-  const zd e = zexp(z);
-  return zdiv({e.re - 1.0, e.im}, lam);
-}
-
-__device__ __forceinline__ zd zlog(zd z) { return {log(sqrt(z.re * z.re + z.im * z.im)), atan2(z.im, z.re)}; }
-
-// bilinear map of one mode: z = lambda*delta, Lambda_bar = (1 + z/2)/(1 - z/2)
-// = 2 w - 1 and gain = delta w, with w = 1/(1 - z/2)
-__device__ zd bilinear_w64(zd lam, double delta) {
-  return zdiv({1.0, 0.0}, {1.0 - 0.5 * lam.re * delta, -0.5 * lam.im * delta});
-}
+using f64::zd;
 
 __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int KS = q.Hpad / 32;
@@ -72,13 +34,8 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
         if (!q.time_varying) {
-          const double dt = exp(static_cast<double>(q.log_delta[p]));
-          if (q.bilinear) {
-            const zd w = bilinear_w64(lam, dt);
-            g = {dt * w.re, dt * w.im};
-          } else {
-            g = gain64(lam, dt);
-          }
+          zd abar;
+          f64::discretize(lam, exp(static_cast<double>(q.log_delta[p])), q.bilinear, abar, g);
         } else {
           g = {1.0, 0.0};
         }
@@ -89,7 +46,7 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         double val = 0.0;
         if (p < q.P && h < q.H) {
           const float2 bt = q.b_tilde[static_cast<size_t>(p) * q.H + h];
-          const zd b = zmul(g, {bt.x, bt.y});
+          const zd b = f64::zmul(g, {bt.x, bt.y});
           val = c == 0 ? b.re : b.im;
         }
         v[i] = static_cast<float>(val);
@@ -123,7 +80,7 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
         mp.lam = make_float2(q.lam[p].x, q.lam[p].y);
-        const zd il = zdiv({1.0, 0.0}, lam);
+        const zd il = f64::zdiv({1.0, 0.0}, lam);
         mp.inv_lam = make_float2(static_cast<float>(il.re), static_cast<float>(il.im));
         mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
         if (!q.time_varying) {
@@ -131,13 +88,14 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
           // log of Lambda_bar: z itself for zero-order hold
           zd z = {lam.re * dt, lam.im * dt};
           if (q.bilinear) {
-            const zd w = bilinear_w64(lam, dt);
-            z = zlog({2.0 * w.re - 1.0, 2.0 * w.im});
+            zd ab, g;
+            f64::bilinear(lam, dt, ab, g);
+            z = f64::zlog(ab);
           }
-          const zd a = zexp(z);
-          const zd as = zexp({z.re * q.Lseg, z.im * q.Lseg});
+          const zd a = f64::zexp(z);
+          const zd as = f64::zexp({z.re * q.Lseg, z.im * q.Lseg});
           const double m = (q.L - 1) % q.Lseg + 1;
-          const zd al = zexp({z.re * m, z.im * m});
+          const zd al = f64::zexp({z.re * m, z.im * m});
           mp.alast = make_float2(static_cast<float>(al.re), static_cast<float>(al.im));
           mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));
           mp.aseg = make_float2(static_cast<float>(as.re), static_cast<float>(as.im));

@@ -6,6 +6,7 @@
 // One workgroup per sequence; the whole step is a few hundred kilobytes of
 // parameter reads, so it is latency-bound and runs on the vector units.
 #include "s5_common.h"
+#include "s5_f64.h"
 #include "s5_internal.h"
 
 namespace s5 {
@@ -14,46 +15,8 @@ namespace {
 
 constexpr int kStepThreads = 512;   // >= S5_MAX_H outputs, >= 2 S5_MAX_P
 
-struct zd {
-  double re, im;
-};
-__device__ __forceinline__ zd zmul(zd a, zd b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
-__device__ __forceinline__ zd zdiv(zd a, zd b) {
-  const double den = b.re * b.re + b.im * b.im;
-  return {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
-}
+using f64::zd;
 
-// float64 discretisation of one mode for interval dt: zero-order hold
-// (Lambda_bar = e^z, gain = (e^z - 1)/lambda, 9-term phi1 series for
-// |z| < 1e-4) or bilinear (w = 1/(1 - z/2), Lambda_bar = 2w - 1, gain = dt w)
-__device__ void disc_mode64(zd lam, double dt, bool bilinear, zd& abar, zd& gain) {
-  const zd z = {lam.re * dt, lam.im * dt};
-  if (bilinear) {
-    const zd w = zdiv({1.0, 0.0}, {1.0 - 0.5 * z.re, -0.5 * z.im});
-    abar = {2.0 * w.re - 1.0, 2.0 * w.im};
-    gain = {dt * w.re, dt * w.im};
-    return;
-  }
-  const double e = exp(z.re);
-  double sn, cs;
-  sincos(z.im, &sn, &cs);
-  abar = {e * cs, e * sn};
-  if (sqrt(z.re * z.re + z.im * z.im) < 1e-4) {
-    zd term = {1.0, 0.0}, phi = {1.0, 0.0};
-    for (int n = 1; n <= 8; ++n) {
-      term = zmul(term, z);
-      term.re /= (n + 1);
-      term.im /= (n + 1);
-      phi.re += term.re;
-      phi.im += term.im;
-    }
-    gain = {dt * phi.re, dt * phi.im};
-  } else {
-    gain = zdiv({abar.re - 1.0, abar.im}, lam);
-  }
-}
-
-__device__ __forceinline__ float gelu_step(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
 // lanes per row of a sum: the 512 threads spread over `rows` rows, a power
 // of two from 1 to 8, the lanes of a row adjacent
@@ -113,13 +76,13 @@ __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
       if (q.bilinear) {
         bilinear_step(lam, dt, a, g);
       } else {
-        const zd il = zdiv({1.0, 0.0}, {lam.re, lam.im});
+        const zd il = f64::zdiv({1.0, 0.0}, {lam.re, lam.im});
         const float hrev = static_cast<float>(static_cast<double>(lam.im) / (4.0 * 3.14159265358979323846));
         zoh_step(lam, {static_cast<float>(il.re), static_cast<float>(il.im)}, hrev, dt, a, g);
       }
     } else {
       zd a64, g64;
-      disc_mode64({q.lam[t].x, q.lam[t].y}, exp(static_cast<double>(q.log_delta[t])), q.bilinear, a64, g64);
+      f64::discretize({q.lam[t].x, q.lam[t].y}, exp(static_cast<double>(q.log_delta[t])), q.bilinear, a64, g64);
       a = {static_cast<float>(a64.re), static_cast<float>(a64.im)};
       g = {static_cast<float>(g64.re), static_cast<float>(g64.im)};
     }
@@ -147,7 +110,7 @@ __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
   acc = row_sum(acc, kr);
   if (h < q.H && rp == 0) {
     float yv = fmaf(q.d[h], s_u[h], q.c_scale * acc);
-    if (q.gelu) yv = gelu_step(yv);
+    if (q.gelu != 0) yv = gelu_form(yv, q.gelu);
     if (q.bf16_io) {
       static_cast<uint16_t*>(q.y)[ub + h] = f32_to_bf16(yv);
     } else {

@@ -189,9 +189,14 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *       "Discretization and the step size"; abhik.ai review: the official
  *       code offers it as an alternative). Time-invariant or time-varying.
  *   S5_FLAG_GELU  y is GELU of the pre-activation, y * Phi(y) with the
- *       standard normal distribution function Phi (the exact form, not the
- *       tanh one; papercache notes App. A `apply_S5_layer`), in float32 with
- *       erf from Abramowitz & Stegun 7.1.26 (absolute error < 1.5e-7).
+ *       standard normal distribution function Phi (the function's definition;
+ *       papercache notes App. A `apply_S5_layer` applies a GELU to the
+ *       pre-activations), in float32 with erf from Abramowitz & Stegun
+ *       7.1.26 (absolute error < 1.5e-7).
+ *   S5_FLAG_GELU_TANH  y is the tanh approximation of GELU,
+ *       y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))), the form the App. A
+ *       listing's library call computes by default; within 5e-4 of the exact
+ *       form. Exclusive with S5_FLAG_GELU.
  *   S5_FLAG_BIDIRECTIONAL  a second, backward scan over the same Lambda_bar
  *       and B_bar, x'_k = Lambda_bar x'_{k+1} + B_bar u_k from x'_L = 0,
  *       read out by the second half of C~, which then has 2P columns:
@@ -210,14 +215,15 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *               exactly one of log_delta and delta is given
  *   x0, x_last  as s5_forward_stateful (NULL: zero / not written)
  * Errors: as s5_forward_stateful; S5_ERR_INVALID_ARGUMENT for a wrong size
- * field, unknown flags, both or neither interval arrays, or
+ * field, unknown flags, both GELU forms, both or neither interval arrays, or
  * S5_FLAG_BIDIRECTIONAL with delta, x0 or x_last.
  */
 enum {
   S5_FLAG_HALF_SPECTRUM = 1u << 0,
   S5_FLAG_BILINEAR = 1u << 1,
   S5_FLAG_GELU = 1u << 2,
-  S5_FLAG_BIDIRECTIONAL = 1u << 3
+  S5_FLAG_BIDIRECTIONAL = 1u << 3,
+  S5_FLAG_GELU_TANH = 1u << 4
 };
 
 typedef struct {
@@ -252,8 +258,9 @@ s5_status s5_forward_ex(const s5_forward_desc* desc, hipStream_t stream);
  *
  *   B, H, P     sequences (>= 0; 0 is a no-op), features, complex modes
  *   io          element type of u and y
- *   flags       S5_FLAG_HALF_SPECTRUM, S5_FLAG_BILINEAR, S5_FLAG_GELU (as in
- *               s5_forward_ex); S5_FLAG_BIDIRECTIONAL is rejected
+ *   flags       S5_FLAG_HALF_SPECTRUM, S5_FLAG_BILINEAR, S5_FLAG_GELU or
+ *               S5_FLAG_GELU_TANH (as in s5_forward_ex);
+ *               S5_FLAG_BIDIRECTIONAL is rejected
  *   u           [B,H]  this step's input
  *   lambda, b_tilde [P,H], c_tilde [H,P], d [H]   as s5_forward
  *   log_delta   [P] per-mode log interval, or NULL

@@ -49,6 +49,10 @@ O9  GELU epilogue: y -> y * Phi(y), Phi the standard normal distribution
     function (written with erf), applied to the pre-activation output.
     [papercache notes, App. A `apply_S5_layer`; wikillm notes, gated
     activation step; the plain reading of "GELU" is the exact form]
+O9t the tanh form of the GELU epilogue, y/2 (1 + tanh(sqrt(2/pi)(y +
+    0.044715 y^3))): the App. A listing ends in the JAX library's gelu, whose
+    default is this approximation. [papercache notes, App. A
+    `apply_S5_layer`]
 O10 bidirectional form: a second, backward scan over the same
     Lambda_bar and B_bar, x'_k = Lambda_bar * x'_{k+1} + B_bar u_k from
     x'_L = 0 (inclusive of step k), read out by the second half of a
@@ -91,6 +95,7 @@ __all__ = [
     "bilinear",
     "readout_half",
     "gelu",
+    "gelu_tanh",
     "scan_reverse",
     "forward_ex",
     "sigmoid",
@@ -261,6 +266,12 @@ def gelu(y):
     return y * 0.5 * (1.0 + scipy.special.erf(y / math.sqrt(2.0)))
 
 
+def gelu_tanh(y):
+    """O9t: the tanh approximation y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))."""
+    y = np.asarray(y, dtype=np.float64)
+    return 0.5 * y * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (y + 0.044715 * y ** 3)))
+
+
 def scan_reverse(lam_bar, bu):
     """O10: x'_k = a * x'_{k+1} + b_k from x'_L = 0, explicit loop from
     k = L-1 down to 0. ``bu`` [B, L, P]; ``lam_bar`` [P]."""
@@ -281,7 +292,7 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
     or time-varying (``delta`` [B, L, P]) intervals, ZOH (O2) or bilinear
     (O8) discretisation, optional initial state (O6), half-spectrum readout
     (O7), bidirectional scans (O10, ``c_tilde`` [H, 2P]) and a GELU epilogue
-    (O9, ``activation="gelu"``).
+    (O9, ``activation="gelu"``, or its tanh form O9t, ``"gelu_tanh"``).
 
     Returns (y [B, L, H] float64, x_last [B, P] complex128, or None for the
     bidirectional form)."""
@@ -295,8 +306,8 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
         raise ValueError("give exactly one of log_delta and delta")
     if bidirectional and (tv or x0 is not None):
         raise ValueError("the bidirectional form is time-invariant and stateless")
-    if activation not in (None, "gelu"):
-        raise ValueError("activation must be None or 'gelu'")
+    if activation not in (None, "gelu", "gelu_tanh"):
+        raise ValueError("activation must be None, 'gelu' or 'gelu_tanh'")
     if tv:
         lam_bar, gain = disc(lam[None, None, :], delta)               # O1, O2/O8
         bu = gain * drive(u, b_tilde)                                 # O3
@@ -320,6 +331,8 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
             x_last = np.asarray(x0, dtype=np.complex128).reshape(Bn, P)
     if activation == "gelu":
         y = gelu(y)                                                   # O9
+    elif activation == "gelu_tanh":
+        y = gelu_tanh(y)                                              # O9t
     return y, x_last
 
 

@@ -85,7 +85,7 @@ def _run(w, opts, c2=None, x0=None):
     y, xl = s5.forward_ex(u, dev["lam"], dev["b_tilde"], ct, dev["d"], x0=x0d,
                           final_state=opts.get("state", False), half_spectrum=opts.get("half", False),
                           bilinear=opts.get("bilinear", False), gelu=opts.get("gelu", False),
-                          bidirectional=opts.get("bidir", False), **kw)
+                          gelu_tanh=opts.get("gelu_tanh", False), bidirectional=opts.get("bidir", False), **kw)
     torch.cuda.synchronize()
     return y, xl
 
@@ -94,7 +94,7 @@ def _oracle(w, opts, c2=None, x0=None):
     kw = {"delta": w.delta} if w.time_varying else {"log_delta": w.log_delta}
     return orc.forward_ex(w.u, w.lam, w.b_tilde, c2 if c2 is not None else w.c_tilde, w.d, x0=x0,
                           conj_sym=opts.get("half", False), method="bilinear" if opts.get("bilinear") else "zoh",
-                          activation="gelu" if opts.get("gelu") else None,
+                          activation="gelu" if opts.get("gelu") else "gelu_tanh" if opts.get("gelu_tanh") else None,
                           bidirectional=opts.get("bidir", False), **kw)
 
 
@@ -112,6 +112,10 @@ CASES = [
     ((2, 300, 24, 40, "f32", False), {"gelu": True}),
     ((2, 1000, 128, 256, "bf16", False), {"gelu": True}),
     ((2, 513, 96, 128, "f32", True), {"gelu": True, "state": True}),
+    ((2, 300, 24, 40, "f32", False), {"gelu_tanh": True}),
+    ((2, 1000, 128, 256, "bf16", False), {"gelu_tanh": True}),
+    ((2, 513, 96, 128, "f32", True), {"gelu_tanh": True, "state": True}),
+    ((2, 600, 64, 64, "f32", False), {"bidir": True, "gelu_tanh": True}),
     ((1, 1, 5, 3, "f32", False), {"bidir": True}),
     ((2, 97, 24, 40, "f32", False), {"bidir": True}),
     ((2, 97, 24, 40, "bf16", False), {"bidir": True}),
@@ -148,7 +152,7 @@ def test_option_parity(case):
     if opts.get("bidir") and io == "bf16":
         first = dict(opts, bidir=False, gelu=False)
         y_first, _ = _oracle(w, first, np.ascontiguousarray(c2[:, :P]), None)
-    ey = _y_err(io, y, yo, y_first, opts.get("gelu", False))
+    ey = _y_err(io, y, yo, y_first, opts.get("gelu", False) or opts.get("gelu_tanh", False))
     msg = f"[options]   y {ey:.3e} (tol {w.tol:.0e})"
     if opts.get("state"):
         ex = _x_err(xl, xo)

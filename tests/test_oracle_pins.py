@@ -467,6 +467,27 @@ def pin_gelu_values():
     return err
 
 
+def pin_gelu_tanh():
+    """O9t, the tanh form: (1 + tanh k)/2 is the logistic function of 2k, so
+    the form equals x * expit(2k) evaluated through the exponential; it is odd
+    up to the identity f(x) - f(-x) = x; its x^2 Taylor coefficient is
+    GELU's, 1/sqrt(2 pi) (from Phi'(0)); and it stays within 5e-4 of
+    x Phi(x) with Phi integrated numerically (it approximates GELU)."""
+    xs = np.linspace(-6.0, 6.0, 97)
+    k = math.sqrt(2.0 / math.pi) * (xs + 0.044715 * xs ** 3)
+    f = orc.gelu_tanh(xs)
+    err = float(np.max(np.abs(f - xs * scipy.special.expit(2.0 * k))))
+    err = max(err, float(np.max(np.abs(f - orc.gelu_tanh(-xs) - xs))))
+    h = 1e-4
+    c2 = (float(orc.gelu_tanh(h)) + float(orc.gelu_tanh(-h))) / (2.0 * h * h)
+    err = max(err, abs(c2 - 1.0 / math.sqrt(2.0 * math.pi)) * 1e-6)
+    phi = np.array([0.5 + scipy.integrate.quad(lambda t: math.exp(-0.5 * t * t), 0.0, x,
+                                               epsabs=1e-14, epsrel=1e-13)[0] / math.sqrt(2 * math.pi)
+                    for x in xs])
+    dist = float(np.max(np.abs(f - xs * phi)))
+    return err if dist <= 5e-4 else max(err, dist)
+
+
 def _conv_bidirectional(u, lam, bt, ct2, d, logd):
     """Two-sided convolution: y_k = sum_{j<=k} Kf_{k-j} u_j + sum_{j>=k} Kb_{j-k} u_j
     + D u_k, Kf_i = Re(C_f Lb^i B_bar), Kb_i = Re(C_b Lb^i B_bar), with the
@@ -572,6 +593,7 @@ ALL_PINS = {
     "bilinear_map": (pin_bilinear_map, 1e-4),
     "half_spectrum_ex": (pin_half_spectrum_ex, 1e-12),
     "gelu_values": (pin_gelu_values, 1e-13),
+    "gelu_tanh": (pin_gelu_tanh, 1e-12),
     "bidirectional_convolution": (pin_bidirectional_convolution, 1e-10),
     "bidirectional_reversal": (pin_bidirectional_reversal, 1e-12),
     "sigmoid_tanh_identity": (pin_sigmoid_tanh_identity, 1e-15),
@@ -961,6 +983,35 @@ def test_planted_gelu_tanh_form(monkeypatch):
         return 0.5 * y * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (y + 0.044715 * y ** 3)))
     monkeypatch.setattr(orc, "gelu", tanh_gelu)
     assert _fails("gelu_values")
+
+
+def test_planted_gelu_tanh_without_sqrt_two_over_pi(monkeypatch):
+    monkeypatch.setattr(orc, "gelu_tanh", lambda y: 0.5 * np.asarray(y, np.float64)
+                        * (1.0 + np.tanh(np.asarray(y, np.float64) + 0.044715 * np.asarray(y, np.float64) ** 3)))
+    assert _fails("gelu_tanh")
+
+
+def test_planted_gelu_tanh_cubic_coefficient(monkeypatch):
+    monkeypatch.setattr(orc, "gelu_tanh", lambda y: 0.5 * np.asarray(y, np.float64)
+                        * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (np.asarray(y, np.float64)
+                                                                  + 0.44715 * np.asarray(y, np.float64) ** 3))))
+    assert _fails("gelu_tanh")
+
+
+def test_planted_gelu_tanh_replaced_by_exact_form(monkeypatch):
+    monkeypatch.setattr(orc, "gelu_tanh", orc.gelu)
+    assert _fails("gelu_tanh")
+
+
+def test_gelu_forms_differ_through_forward_ex():
+    rng = _rng(47)
+    lam, bt, ct, d, logd = _rand_params(rng, 4, 6)
+    u = 3.0 * rng.normal(size=(1, 40, 4))
+    y0 = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd)[0]
+    ye = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd, activation="gelu")[0]
+    yt = orc.forward_ex(u, lam, bt, ct, d, log_delta=logd, activation="gelu_tanh")[0]
+    assert np.array_equal(ye, orc.gelu(y0)) and np.array_equal(yt, orc.gelu_tanh(y0))
+    assert 1e-6 < float(np.max(np.abs(ye - yt))) <= 5e-4
 
 
 def test_forward_ex_reduces_to_the_plain_forms():

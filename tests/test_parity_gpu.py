@@ -144,6 +144,34 @@ def test_zero_intervals_are_identity_steps():
     check(w, "zero intervals")
 
 
+@pytest.mark.parametrize("tv,io", [(False, "f32"), (False, "bf16"), (True, "f32")])
+def test_zero_and_near_threshold_lambda_delta(tv, io):
+    """Modes at the discretisation's special points: lambda = 0 (the gain's
+    removable singularity, gain = Delta) and |lambda Delta| on both sides of
+    1e-4, where the gain switches between the quotient and the series. Time-
+    invariant: |z| = 0.5e-4, 0.99e-4, 1.01e-4, 2e-4 exactly at the mode's
+    interval; time-varying: the per-step intervals spread |z| over several
+    decades around 1e-4."""
+    H, P = (96, 128) if tv else (64, 64)
+    w = wl.make_random(2, 700, H, P, io=io, tv=tv, seed=21, kind="random_walk" if tv else "normal")
+    lam = w.lam.astype(np.complex128)
+    lam[0] = 0.0
+    lam[5] = 0.0
+    if tv:
+        med = np.median(w.delta[:, :, 1:5].astype(np.float64), axis=(0, 1))
+        for j, target in zip(range(1, 5), (0.3e-4, 1e-4, 3e-4, 1e-3)):
+            lam[j] = (target / med[j - 1]) * np.exp(1j * (0.3 + j))
+    else:
+        dl = np.exp(w.log_delta.astype(np.float64))
+        for j, target in zip(range(1, 5), (0.5e-4, 0.99e-4, 1.01e-4, 2e-4)):
+            lam[j] = (target / dl[j]) * np.exp(1j * (0.3 + j))
+    w.lam = lam.astype(np.complex64)
+    if not tv:
+        z = np.abs(w.lam[1:5].astype(np.complex128) * np.exp(w.log_delta[1:5].astype(np.float64)))
+        assert z[1] < 1e-4 < z[2]
+    check(w, "lambda = 0 and |lambda Delta| near 1e-4")
+
+
 def test_causality_and_batch_independence():
     w = wl.make_random(3, 400, 64, 64, io="f32", seed=5)
     t = dev(w)
@@ -168,8 +196,8 @@ def test_output_fully_written_nan_poison():
 
 @pytest.mark.parametrize("cfg,B,reps", [(1, 8, 20), (3, 2, 10), (4, 1, 5)])
 def test_run_to_run_bitwise_determinism(cfg, B, reps):
-    # long sequences keep hundreds of chunks of one sequence in flight, so the
-    # look-back takes different paths from run to run; the output must not change
+    # many workgroups of one sequence run in an order that changes from run to
+    # run; every sum has a fixed order, so the output must not change
     w = wl.make_config(cfg, B=B)
     t = dev(w)
     ref = run_gpu(w, t).clone()

@@ -66,6 +66,8 @@ CASES = [
     (7, 96, 128, "f32", True, {"bilinear": True}),
     (33, 512, 200, "bf16", False, {"bilinear": True, "gelu": True}),
     (4, 24, 40, "f32", False, {"gelu": True}),
+    (4, 24, 40, "f32", False, {"gelu_tanh": True}),
+    (7, 96, 128, "f32", True, {"gelu_tanh": True}),
 ]
 
 
@@ -87,7 +89,8 @@ def test_step_parity(case):
     yo, xo = orc.forward_ex(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, x0=x0.astype(np.complex64),
                             conj_sym=opts.get("half_spectrum", False),
                             method="bilinear" if opts.get("bilinear") else "zoh",
-                            activation="gelu" if opts.get("gelu") else None, **okw)
+                            activation="gelu" if opts.get("gelu") else "gelu_tanh" if opts.get("gelu_tanh") else None,
+                            **okw)
     ey, ex = _y_err(io, y, yo[:, 0]), _x_err(x, xo)
     print(f"[step]   y {ey:.3e}  x {ex:.3e}  (tol {w.tol:.0e})", flush=True)
     assert ey <= w.tol and ex <= w.tol
@@ -116,3 +119,35 @@ def test_steps_equal_one_stateful_call(io, tv):
     ey, ex = _y_err(io, y, yo), _x_err(x, xo)
     print(f"[step] {T} steps {io} tv={tv}: y {ey:.3e}  x {ex:.3e}", flush=True)
     assert ey <= w.tol and ex <= w.tol
+
+
+def test_per_step_interval_with_a_huge_angle():
+    """A per-step interval whose half-angle Im(lambda) dt / 2 is about 2^30
+    turns: the float32 product of the interval and Im(lambda)/(4 pi) is then a
+    whole number of turns, so the float32 path sees the angle 0 and gives
+    Lambda_bar = e^(Re(lambda) dt) (the quadrant count, 2^32, must be reduced
+    exactly, not converted with saturation). One step from x0 = 1 with zero
+    input leaves x = Lambda_bar x0; checked through s5_step and through the
+    time-varying stateful forward pass."""
+    import diagonal_state_space_amd as s5
+    cuda = torch.device("cuda:0")
+    omega = 4.0 * math.pi * 2.0 ** 20
+    lam = torch.tensor([complex(-1e-9, omega)], dtype=torch.complex64, device=cuda)
+    hrev = np.float32(np.float64(np.complex64(complex(-1e-9, omega)).imag) / (4.0 * math.pi))
+    dt = np.float32(1024.0)
+    th = np.float32(hrev * dt)
+    assert th == np.floor(th) and th >= 2.0 ** 29          # whole turns, beyond 2^29
+    expect = math.exp(float(np.float32(-1e-9)) * 1024.0)
+    H, P = 4, 1
+    bt = torch.zeros(P, H, dtype=torch.complex64, device=cuda)
+    ct = torch.ones(H, P, dtype=torch.complex64, device=cuda)
+    d = torch.zeros(H, dtype=torch.float32, device=cuda)
+    x = torch.ones(1, P, dtype=torch.complex64, device=cuda)
+    u = torch.zeros(1, H, dtype=torch.float32, device=cuda)
+    delta = torch.full((1, P), float(dt), dtype=torch.float32, device=cuda)
+    s5.step(u, lam, bt, ct, d, x, delta=delta)
+    x0 = torch.ones(1, P, dtype=torch.complex64, device=cuda)
+    _, xl = s5.forward_timevarying_stateful(u.view(1, 1, H), lam, bt, ct, d, delta.view(1, 1, P), x0=x0)
+    torch.cuda.synchronize()
+    for got in (x.cpu().numpy()[0, 0], xl.cpu().numpy()[0, 0]):
+        assert abs(got.real - expect) < 1e-6 and abs(got.imag) < 1e-6, got

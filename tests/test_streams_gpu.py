@@ -1,0 +1,83 @@
+"""Forward calls from several host threads on several streams at once give
+the bits of the same calls run one after another: the library's reusable
+scratch buffers (each taken by one call at a time, reused in stream order or
+after the last user's work has finished) keep concurrent calls apart."""
+
+import threading
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diagonal_state_space_amd  # noqa: F401  (fails loudly if libs5.so is missing)
+
+
+def _inputs(w, cuda):
+    t = {k: torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(cuda)
+         for k in ("lam", "b_tilde", "c_tilde", "d", "log_delta")}
+    if w.io == "bf16":
+        t["u"] = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(cuda)
+    else:
+        t["u"] = torch.from_numpy(w.u).to(cuda)
+    if w.delta is not None:
+        t["delta"] = torch.from_numpy(w.delta).to(cuda)
+    return t
+
+
+def _call(s5, w, t, y):
+    if w.time_varying:
+        s5.forward_timevarying(t["u"], t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["delta"], y=y)
+    else:
+        s5.forward(t["u"], t["lam"], t["b_tilde"], t["c_tilde"], t["d"], t["log_delta"], y=y)
+
+
+def test_concurrent_streams_match_serial():
+    import diagonal_state_space_amd as s5
+    cuda = torch.device("cuda:0")
+    # different shapes, so the calls ask for scratch of different sizes
+    ws = [wl.make_random(4, 3000, 128, 256, io="bf16", seed=31),
+          wl.make_random(2, 5000, 96, 128, io="f32", tv=True, seed=32, kind="random_walk"),
+          wl.make_random(8, 1000, 64, 64, io="f32", seed=33),
+          wl.make_random(3, 2500, 256, 192, io="bf16", seed=34)]
+    ts = [_inputs(w, cuda) for w in ws]
+    refs = []
+    for w, t in zip(ws, ts):
+        y = torch.empty_like(t["u"])
+        _call(s5, w, t, y)
+        refs.append(y)
+    torch.cuda.synchronize()
+    reps = 6
+    outs = [[torch.full_like(t["u"], float("nan")) for _ in range(reps)] for t in ts]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in ws]
+    errors = []
+
+    def worker(k):
+        try:
+            with torch.cuda.stream(streams[k]):
+                for r in range(reps):
+                    _call(s5, ws[k], ts[k], outs[k][r])
+        except Exception as e:   # reported after the join
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(ws))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(len(ws)):
+        for r in range(reps):
+            assert torch.equal(outs[k][r], refs[k]), f"workload {k}, repetition {r}"
+    print(f"[streams] {len(ws)} threads x {reps} calls on separate streams: bitwise equal", flush=True)
