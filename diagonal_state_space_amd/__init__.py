@@ -41,7 +41,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libs5.so")
 _lib = None
 
-EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_timevarying", "s5_forward_stateful",
+EXPORTS = ("s5_discretize", "s5_forward", "s5_forward_noalloc", "s5_forward_timevarying", "s5_forward_stateful",
            "s5_forward_timevarying_stateful", "s5_forward_ex", "s5_step", "s5_glu", "s5_status_string",
            "s5_set_profiling_events")
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.s5_discretize.restype = st
         L.s5_forward.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
         L.s5_forward.restype = st
+        L.s5_forward_noalloc.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.s5_forward_noalloc.restype = st
         L.s5_forward_timevarying.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
                                              vp, vp, vp, vp]
         L.s5_forward_timevarying.restype = st
@@ -189,6 +191,18 @@ def forward(u, lam, b_tilde, c_tilde, d, log_delta, y=None, stream=None):
     _check(lib().s5_forward(B, L, H, P, io, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
                             c_tilde.data_ptr(), d.data_ptr(), log_delta.data_ptr(), y.data_ptr(),
                             _stream_handle(stream)), "s5_forward")
+    return y
+
+
+def forward_noalloc(u, lam, b_tilde, c_tilde, d, log_delta, y=None, stream=None):
+    """As forward, through s5_forward_noalloc: the library's scratch is its
+    fixed per-device array (nothing is allocated by the library)."""
+    import torch
+    B, L, H, P, io, y = _forward_args(u, lam, b_tilde, c_tilde, d, y)
+    _dev_tensor(log_delta, "log_delta", torch.float32, (P,))
+    _check(lib().s5_forward_noalloc(B, L, H, P, io, u.data_ptr(), lam.data_ptr(), b_tilde.data_ptr(),
+                                    c_tilde.data_ptr(), d.data_ptr(), log_delta.data_ptr(), y.data_ptr(),
+                                    _stream_handle(stream)), "s5_forward_noalloc")
     return y
 
 

@@ -10,6 +10,13 @@
 
 #include "s5_internal.h"
 
+// Scratch of the allocation-free entry point: one fixed array per device,
+// held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is resolved once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[S5_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local hipEvent_t tl_events[S5_PROFILING_MAX_EVENTS] = {};
@@ -111,6 +118,28 @@ hipError_t scratch_release(Scratch* s, hipStream_t stream) {
   return e;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return hipSuccess;
+}
+
 s5_status check_sizes(int64_t P, int64_t H) {
   if (P < 1 || H < 1) return S5_ERR_INVALID_ARGUMENT;
   if (P > S5_MAX_P || H > S5_MAX_H) return S5_ERR_UNSUPPORTED;
@@ -129,7 +158,7 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
                          const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
                          const float* d, const float* log_delta, const float* delta, void* y,
                          bool time_varying, const s5_c64* x0, s5_c64* x_last, const Options& opt,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool noalloc = false) {
   if (B < 0 || L < 0) return S5_ERR_INVALID_ARGUMENT;
   s5_status st = check_sizes(P, H);
   if (st != S5_OK) return st;
@@ -211,6 +240,13 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
 
   s5::ForwardLayout lay;
   if (!s5::forward_layout(a, lay)) return S5_ERR_UNSUPPORTED;
+  if (noalloc) {
+    // the fixed per-device array; the options path (backward scan) never comes here
+    if (lay.total > S5_NOALLOC_SCRATCH_BYTES || opt.bidir) return S5_ERR_UNSUPPORTED;
+    void* fixed = nullptr;
+    if (noalloc_scratch(&fixed) != hipSuccess) return S5_ERR_HIP;
+    return s5::launch_forward(a, lay, fixed, stream, tl_events, tl_nevents) == hipSuccess ? S5_OK : S5_ERR_HIP;
+  }
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
   Scratch* ws = nullptr;
   hipError_t e = scratch_acquire(lay.total, stream, &ws);
@@ -270,6 +306,13 @@ s5_status s5_forward(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, co
                      const float* d, const float* log_delta, void* y, hipStream_t stream) {
   return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
                         false, nullptr, nullptr, Options{}, stream);
+}
+
+s5_status s5_forward_noalloc(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                             const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                             const float* d, const float* log_delta, void* y, hipStream_t stream) {
+  return forward_common(B, L, H, P, io, u, lambda, b_tilde, c_tilde, d, log_delta, nullptr, y,
+                        false, nullptr, nullptr, Options{}, stream, true);
 }
 
 s5_status s5_forward_stateful(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,

@@ -304,6 +304,32 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
 s5_status s5_glu(int64_t T, int64_t H, s5_dtype io, int variant, const void* y, const float* w,
                  const float* bias, void* out, hipStream_t stream);
 
+/*
+ * s5_forward_noalloc - s5_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. Same arguments, same kernels, same results (bit for
+ * bit) as s5_forward; the scratch memory (packed operands and the per-range
+ * aggregates) comes from a fixed array of S5_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends, instead
+ * of from the library's hipMalloc'd buffers. Nothing is allocated, by this
+ * call or by anything it calls.
+ *
+ * Every call on one device uses that device's one array: calls that overlap
+ * on a device (on different streams, or from different host threads without
+ * ordering) race and must be serialised by the caller; calls in order on one
+ * stream are safe. No part of the array needs to start at zero.
+ * The scratch a call needs grows with the number of sequence ranges the
+ * kernels split the work into (about max(B, 256) ranges of 16 token streams)
+ * times the padded mode count: about 9.6 MB at B = 16, P = 256. Larger needs
+ * return S5_ERR_UNSUPPORTED before anything is enqueued.
+ * Errors: as s5_forward, plus S5_ERR_UNSUPPORTED when the call needs more
+ * than S5_NOALLOC_SCRATCH_BYTES of scratch.
+ */
+#define S5_NOALLOC_SCRATCH_BYTES (32u << 20)
+s5_status s5_forward_noalloc(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
+                             const s5_c64* lambda, const s5_c64* b_tilde, const s5_c64* c_tilde,
+                             const float* d, const float* log_delta, void* y, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* s5_status_string(s5_status s);
 
