@@ -18,6 +18,17 @@ Prints one JSON line with the contract fields plus
                 summed duration of the three launches
   cpu_baseline  the float64 oracle timed on this host's cores
   parity        max |y - y_oracle| / rms(y_oracle) of the benchmark's output
+  step_events   the same call timed by a HIP event pair on its stream: median
+                and mean of --event-steps calls after 10 warm-ups
+  peaks_measured  the chip's rates measured in this run (libs5_peak.so): a
+                streaming copy for HBM GB/s and a register-only MFMA loop for
+                dense bf16 TF/s, beside the vendor figures; every fraction
+                below is also given against them (frac_measured)
+  configs       the four other workloads (tiny, medium, long, irregular),
+                each measured in this run: wall time per call over rotating
+                buffer sets, tokens/s, per-launch kernel times, the dominant
+                kernel's roofline fraction, the layer's HBM fraction and the
+                parity of its output against the oracle
 
 --variant times the same workload through s5_forward_ex with one option
 (initial/final state, half spectrum, bilinear, GELU, bidirectional) or as a
@@ -142,6 +153,196 @@ def algorithmic_flops(w) -> int:
     """Dense real-equivalent work of the two complex projections: 8*P*H per token
     (4PH for B_bar u, 4PH for Re(C~ x))."""
     return 8 * w.P * w.H * w.B * w.L
+
+
+class PeakProbes:
+    """The chip's rates measured in this run with libs5_peak.so: HBM GB/s of
+    a streaming copy, dense bf16 TF/s of a register-only MFMA loop."""
+
+    def __init__(self):
+        from diagonal_state_space_amd import build_lib
+        self.lib = ctypes.CDLL(build_lib.PEAK_LIB_PATH)
+        self.lib.s5_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_void_p]
+        self.lib.s5_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+
+    def measure(self, torch, copy_mib: int = 2048, reps: int = 10) -> dict:
+        stream = torch.cuda.current_stream()
+        nbytes = copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+
+        def timed(fn):
+            for r in range(-2, reps):
+                if r >= 0:
+                    ev[2 * r].record()
+                fn()
+                if r >= 0:
+                    ev[2 * r + 1].record()
+            torch.cuda.synchronize()
+            return float(np.median([ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)]))
+
+        def probe(nt):
+            rc = self.lib.s5_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, nt, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"s5_peak_copy failed ({rc})")
+
+        copies = {"plain": timed(lambda: probe(0)), "nontemporal": timed(lambda: probe(1)),
+                  "torch": timed(lambda: dst.copy_(src))}
+        if not torch.equal(dst[:4096], src[:4096]):
+            raise RuntimeError("s5_peak_copy: copy mismatch")
+        del src, dst
+        copy_gbs = {k: round(2 * nbytes / (v * 1e-3) / 1e9, 1) for k, v in copies.items()}
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        blocks, iters = 4 * ncu, 4000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+        def mfma():
+            rc = self.lib.s5_peak_mfma_bf16(blocks, iters, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"s5_peak_mfma_bf16 failed ({rc})")
+
+        mfma_ms = timed(mfma)
+        flops = blocks * 4 * 8 * iters * 16384
+        return {"hbm_copy_GBs": max(copy_gbs.values()), "copies_GBs": copy_gbs,
+                "mfma_bf16_TFLOPs": round(flops / (mfma_ms * 1e-3) / 1e12, 1),
+                "vendor": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_PEAK_TFLOPS["bf16"]},
+                "method": f"best of three copies of {copy_mib} MiB (16-byte vector loads/stores, plain and "
+                          f"nontemporal, and torch's copy; median of {reps} each); {blocks} workgroups x 4 "
+                          f"waves x 8 independent v_mfma_f32_16x16x32_bf16 chains x {iters} iterations "
+                          f"(median of {reps})"}
+
+
+def forward_timed(w, s5, torch, warmup: int, steps: int, event_steps: int = 0):
+    """Time s5_forward / s5_forward_timevarying on workload w: rotating input
+    and output sets (> 512 MB in total, so that the 256 MB Infinity Cache
+    cannot serve repeats), `warmup` untimed calls, `steps` calls between two
+    synchronisations (wall clock), then per-launch HIP events on `steps` more
+    calls, and (event_steps > 0) event pairs around whole calls. Returns a
+    dict of timings and the output of the last call."""
+    dev = torch.device("cuda:0")
+    lam = torch.from_numpy(w.lam).to(dev)
+    bt = torch.from_numpy(w.b_tilde).to(dev)
+    ct = torch.from_numpy(w.c_tilde).to(dev)
+    d = torch.from_numpy(w.d).to(dev)
+    logd = torch.from_numpy(w.log_delta).to(dev)
+    if w.io == "bf16":
+        u0 = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        u0 = torch.from_numpy(w.u).to(dev)
+    delta0 = torch.from_numpy(w.delta).to(dev) if w.time_varying else None
+    set_bytes = u0.numel() * u0.element_size() * 2 + (delta0.numel() * 4 if delta0 is not None else 0)
+    n_sets = min(64, max(2, math.ceil(512e6 / set_bytes)))
+    us = [u0] + [u0.clone() for _ in range(n_sets - 1)]
+    ys = [torch.empty_like(u0) for _ in range(n_sets)]
+    deltas = ([delta0] + [delta0.clone() for _ in range(n_sets - 1)]) if delta0 is not None else None
+
+    def step(i):
+        k = i % n_sets
+        if w.time_varying:
+            s5.forward_timevarying(us[k], lam, bt, ct, d, deltas[k], y=ys[k])
+        else:
+            s5.forward(us[k], lam, bt, ct, d, logd, y=ys[k])
+        return k
+
+    i = 0
+    for _ in range(warmup):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = HipEvents()
+    evs = [[ev.create() for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        s5.set_profiling_events(e)
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    s5.set_profiling_events(None)
+    launch_ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(3)] for e in evs])
+    for e in evs:
+        for h in e:
+            ev.destroy(h)
+    res = {"wall_ms": wall_ms, "launch_ms": launch_ms, "n_sets": n_sets,
+           "set_last": (i - 1) % n_sets, "ys": ys, "step": step, "next": i,
+           "params": (lam, bt, ct, d, logd), "us": us, "deltas": deltas}
+    if event_steps > 0:
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(event_steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(event_steps)]
+        for _ in range(10):
+            step(i)
+            i += 1
+        for k in range(event_steps):
+            e0[k].record()
+            step(i)
+            i += 1
+            e1[k].record()
+        torch.cuda.synchronize()
+        call_ms = np.array([a.elapsed_time(b) for a, b in zip(e0, e1)])
+        res["call_ms"] = call_ms
+        res["set_last"] = (i - 1) % n_sets
+    return res
+
+
+def roofline_fracs(w, k_ms: float, layer_ms: float, peaks: dict):
+    """Roofline of the state and output pass (k_scan, time k_ms) and of the
+    whole layer (layer_ms): the bound the algorithmic work sets (MFMA: 8*P*H
+    flops per token; HBM: u, y, Delta and the parameters once), against the
+    vendor peaks and, when given, the rates measured in this run."""
+    flops = algorithmic_flops(w)
+    nbytes = algorithmic_bytes(w)
+    mfma_peak = MFMA_PEAK_TFLOPS[w.io]
+    bound = "mfma" if flops / (mfma_peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+    tf = flops / (k_ms * 1e-3) / 1e12
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    lgbs = nbytes / (layer_ms * 1e-3) / 1e9
+    ltf = flops / (layer_ms * 1e-3) / 1e12
+    out = {"bound": bound, "k_scan_us": round(k_ms * 1e3, 2),
+           "k_scan_mfma_frac": round(tf / mfma_peak, 4), "k_scan_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "layer_us": round(layer_ms * 1e3, 2),
+           "layer_hbm_frac": round(lgbs / HBM_PEAK_GBS, 4), "layer_mfma_frac": round(ltf / mfma_peak, 4)}
+    if peaks:
+        mp, hp = peaks["mfma_bf16_TFLOPs"], peaks["hbm_copy_GBs"]
+        out["frac_measured"] = {"k_scan_mfma": round(tf / mp, 4), "k_scan_hbm": round(gbs / hp, 4),
+                                "layer_hbm": round(lgbs / hp, 4), "layer_mfma": round(ltf / mp, 4)}
+    return out
+
+
+def measure_config(i: int, s5, torch, wl, peaks: dict, warmup: int, steps: int) -> dict:
+    """One of the other workloads, measured in this run (see the module
+    docstring, `configs`)."""
+    import oracle.s5_oracle as orc
+    w = wl.make_config(i)
+    r = forward_timed(w, s5, torch, warmup, steps)
+    mean = r["launch_ms"].mean(axis=0)
+    wall = r["wall_ms"]
+    yg = r["ys"][r["set_last"]].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    if w.time_varying:
+        yo = orc.forward_timevarying(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.delta)
+    else:
+        yo = orc.forward(w.u, w.lam, w.b_tilde, w.c_tilde, w.d, w.log_delta)
+    t_orc = time.perf_counter() - t0
+    rms = math.sqrt(float(np.mean(yo ** 2)))
+    out = {"workload": (f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
+                        f"{'_timevarying' if w.time_varying else ''}"),
+           "ms_per_step": round(wall, 5), "tokens_per_s": round(w.B * w.L / (wall * 1e-3), 1),
+           "steps": steps, "buffer_sets": r["n_sets"],
+           "kernels": {"pack_us": round(float(mean[0]) * 1e3, 2), "reduce_us": round(float(mean[1]) * 1e3, 2),
+                       "scan_us": round(float(mean[2]) * 1e3, 2)},
+           "roofline": roofline_fracs(w, float(mean[2]), float(mean.sum()), peaks),
+           "parity": {"max_err_over_rms": float(np.max(np.abs(yg - yo)) / rms), "tol": w.tol},
+           "oracle_tokens_per_s": round(w.B * w.L / t_orc, 1)}
+    del r
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, repeats: int, budget_s: float):
@@ -428,6 +629,11 @@ def main() -> int:
                     help="plain | stateful | half | bilinear | gelu | bidir | chunked:C | step | glu | glu2")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--other-configs", default="0,1,2,4",
+                    help="workloads measured beside the main one (comma list; empty for none)")
+    ap.add_argument("--event-steps", type=int, default=100,
+                    help="calls timed one by one with a HIP event pair (median reported)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the in-run peak-rate probes")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, 5)
@@ -451,62 +657,38 @@ def main() -> int:
     print(f"[bench] workload {w.name}: B={w.B} L={w.L} H={w.H} P={w.P} io={w.io} "
           f"tv={w.time_varying}", file=sys.stderr, flush=True)
 
-    # parameters (shared) and rotating input/output sets (> 512 MB in total)
-    lam = torch.from_numpy(w.lam).to(dev)
-    bt = torch.from_numpy(w.b_tilde).to(dev)
-    ct = torch.from_numpy(w.c_tilde).to(dev)
-    d = torch.from_numpy(w.d).to(dev)
-    logd = torch.from_numpy(w.log_delta).to(dev)
-    if w.io == "bf16":
-        u0 = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
-    else:
-        u0 = torch.from_numpy(w.u).to(dev)
-    delta0 = torch.from_numpy(w.delta).to(dev) if w.time_varying else None
-    set_bytes = u0.numel() * u0.element_size() * 2 + (delta0.numel() * 4 if delta0 is not None else 0)
-    n_sets = max(4, math.ceil(512e6 / set_bytes))
-    us = [u0] + [u0.clone() for _ in range(n_sets - 1)]
-    ys = [torch.empty_like(u0) for _ in range(n_sets)]
-    deltas = ([delta0] + [delta0.clone() for _ in range(n_sets - 1)]) if delta0 is not None else None
-
-    def step(i):
-        k = i % n_sets
-        if w.time_varying:
-            s5.forward_timevarying(us[k], lam, bt, ct, d, deltas[k], y=ys[k])
-        else:
-            s5.forward(us[k], lam, bt, ct, d, logd, y=ys[k])
-
     if args.variant != "plain":
+        # parameters (shared) and rotating input/output sets (> 512 MB in total)
+        lam = torch.from_numpy(w.lam).to(dev)
+        bt = torch.from_numpy(w.b_tilde).to(dev)
+        ct = torch.from_numpy(w.c_tilde).to(dev)
+        d = torch.from_numpy(w.d).to(dev)
+        logd = torch.from_numpy(w.log_delta).to(dev)
+        if w.io == "bf16":
+            u0 = torch.from_numpy(w.u_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            u0 = torch.from_numpy(w.u).to(dev)
+        delta0 = torch.from_numpy(w.delta).to(dev) if w.time_varying else None
+        set_bytes = u0.numel() * u0.element_size() * 2 + (delta0.numel() * 4 if delta0 is not None else 0)
+        n_sets = max(4, math.ceil(512e6 / set_bytes))
+        us = [u0] + [u0.clone() for _ in range(n_sets - 1)]
+        ys = [torch.empty_like(u0) for _ in range(n_sets)]
+        deltas = ([delta0] + [delta0.clone() for _ in range(n_sets - 1)]) if delta0 is not None else None
         return bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_sets)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    peaks = {}
+    if not args.no_peaks:
+        print("[bench] measuring the chip's peak rates (copy, MFMA loop)", file=sys.stderr, flush=True)
+        peaks = PeakProbes().measure(torch)
 
-    # timed steps: plain forward calls
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # the same steps again with HIP events around each of the three launches
-    # (the events add their own gaps, so they stay out of the timed region)
-    ev = HipEvents()
-    evs = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        s5.set_profiling_events(evs[i])
-        step(args.warmup + args.steps + i)
-    torch.cuda.synchronize()
-    s5.set_profiling_events(None)
-    launch_ms = np.array([[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(3)] for e in evs])
-    for e in evs:
-        for h in e:
-            ev.destroy(h)
+    # warm-up, K timed calls (wall clock), K calls with per-launch events,
+    # then calls timed one by one with event pairs
+    r = forward_timed(w, s5, torch, args.warmup, args.steps, args.event_steps)
+    launch_ms = r["launch_ms"]
     kernel_ms = launch_ms[:, 2]
-
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = r["wall_ms"]
+    n_sets = r["n_sets"]
+    ys = r["ys"]
     tokens = w.B * w.L
     value = tokens / (ms_per_step * 1e-3)
     k_ms = float(np.mean(kernel_ms))
@@ -521,10 +703,14 @@ def main() -> int:
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4), "traffic": None}
+        if peaks:
+            roof["frac_measured"] = round(achieved_tf / peaks["mfma_bf16_TFLOPs"], 4)
     else:
         a_gbs = nbytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        if peaks:
+            roof["frac_measured"] = round(a_gbs / peaks["hbm_copy_GBs"], 4)
     workload = (f"s5_fwd_{w.name}_B{w.B}_L{w.L}_H{w.H}_P{w.P}_{w.io}"
                 f"{'_timevarying' if w.time_varying else ''}")
     roof["traffic"] = measured_traffic(workload)
@@ -539,6 +725,9 @@ def main() -> int:
     achieved_gbs = nbytes / (fwd_ms * 1e-3) / 1e9
     hbm = {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "over": "pack + reduce + scan"}
+    if peaks:
+        hbm["frac_measured"] = round(achieved_gbs / peaks["hbm_copy_GBs"], 4)
+    call_ms = r.get("call_ms")
 
     out = {
         "metric": METRIC,
@@ -560,14 +749,30 @@ def main() -> int:
         "kernels": kernels,
         "hbm": hbm,
     }
+    if call_ms is not None:
+        out["step_events"] = {"median_us": round(float(np.median(call_ms)) * 1e3, 2),
+                              "mean_us": round(float(np.mean(call_ms)) * 1e3, 2),
+                              "calls": int(call_ms.size), "warmup": 10}
+    if peaks:
+        out["peaks_measured"] = peaks
+    yg_main = ys[r["set_last"]].float().cpu().numpy().astype(np.float64)
+    del r, ys
+    torch.cuda.empty_cache()
+    others = [int(c) for c in args.other_configs.split(",") if c.strip() != ""]
+    if others:
+        out["configs"] = {}
+        for c in others:
+            if c == args.config:
+                continue
+            print(f"[bench] workload {c} (in-run measurement)", file=sys.stderr, flush=True)
+            out["configs"][str(c)] = measure_config(c, s5, torch, wl, peaks, 5, max(args.steps, 20))
 
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
         cb, yo = cpu_baseline(w, args.cpu_repeats, args.cpu_budget)
         out["cpu_baseline"] = cb
-        yg = ys[(args.warmup + 2 * args.steps - 1) % n_sets].float().cpu().numpy().astype(np.float64)
         rms = math.sqrt(float(np.mean(yo ** 2)))
-        out["parity"] = {"max_err_over_rms": float(np.max(np.abs(yg - yo)) / rms), "tol": w.tol}
+        out["parity"] = {"max_err_over_rms": float(np.max(np.abs(yg_main - yo)) / rms), "tol": w.tol}
     print(json.dumps(out), flush=True)
     return 0
 

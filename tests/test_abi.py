@@ -41,6 +41,26 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+def test_peak_library_exports_its_probes():
+    """libs5_peak.so (the roofline report's peak-rate probes) exports what
+    include/s5_peak.h declares, and refuses bad arguments on the host."""
+    from diagonal_state_space_amd import build_lib
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "s5_peak.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(s5_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["s5_peak_copy", "s5_peak_mfma_bf16"]
+    L = ctypes.CDLL(build_lib.PEAK_LIB_PATH)
+    for name in names:
+        assert hasattr(L, name)
+    L.s5_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    L.s5_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.s5_peak_copy(FAKE, FAKE + 0x100000, 24, 0, None) == -1       # not a multiple of 16
+    assert L.s5_peak_copy(FAKE, FAKE + 16, 64, 0, None) == -1             # overlapping
+    assert L.s5_peak_copy(None, FAKE, 64, 1, None) == -1
+    assert L.s5_peak_mfma_bf16(0, 10, FAKE, None) == -1
+    assert L.s5_peak_mfma_bf16(4, 12, None, None) == -1
+    assert L.s5_peak_mfma_bf16(4, 10, FAKE, None) == -1                  # not a multiple of 4
+
+
 def test_status_strings():
     assert s5.status_string(OK) == "S5_OK"
     assert s5.status_string(INVALID) == "S5_ERR_INVALID_ARGUMENT"
