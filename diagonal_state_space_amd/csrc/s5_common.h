@@ -33,83 +33,50 @@ __device__ __forceinline__ cf cfma(cf a, cf x, cf b) {
   return {fmaf(a.re, x.re, fmaf(-a.im, x.im, b.re)), fmaf(a.re, x.im, fmaf(a.im, x.re, b.im))};
 }
 
-// sin and cos of 2*pi*t for t in revolutions, any finite t: quarter-turn
-// reduction to |x| <= pi/4 (f = t - q/4 is exact: for |t| > 1/8, q/4 is a
-// multiple of ulp(t) and |f| <= 1/8 < |t|; otherwise q = 0), then Taylor
-// polynomials (truncation below 3e-8 absolute; relative accuracy is kept for
-// small t). The quadrant count q = rint(4t) is reduced modulo 4 while still a
-// float (exactly: both terms are integers and their difference is in
-// [-2, 2]), so that its conversion to an integer cannot saturate.
-__device__ __forceinline__ void sincos_rev(float t, float& s, float& c) {
-  const float qf = rintf(4.0f * t);               // quadrant count
-  const float f = fmaf(-0.25f, qf, t);            // exact: |f| <= 1/8
-  const float x = 6.28318530717958647692f * f;
-  const float x2 = x * x;
-  float sp = fmaf(x2, 2.7557319e-6f, -1.98412698e-4f);
-  sp = fmaf(x2, sp, 8.33333333e-3f);
-  sp = fmaf(x2, sp, -1.66666667e-1f);
-  const float sx = fmaf(x * x2, sp, x);
-  float cp = fmaf(x2, 2.48015873e-5f, -1.38888889e-3f);
-  cp = fmaf(x2, cp, 4.16666667e-2f);
-  cp = fmaf(x2, cp, -0.5f);
-  const float cx = fmaf(x2, cp, 1.0f);
-  // quadrant q (mod 4): odd q swaps the pair; bit 1 of q flips the sine's
-  // sign, bit 1 of q + 1 the cosine's (exact, and without branches)
-  const int q = __float2int_rz(fmaf(-4.0f, rintf(0.25f * qf), qf));   // -2..2
-  const bool swap = (q & 1) != 0;
-  const float s0 = swap ? cx : sx;
-  const float c0 = swap ? sx : cx;
-  s = __uint_as_float(__float_as_uint(s0) ^ (static_cast<uint32_t>(q & 2) << 30));
-  c = __uint_as_float(__float_as_uint(c0) ^ (static_cast<uint32_t>((q + 1) & 2) << 30));
-}
-
-// e^r - 1: degree-8 Taylor polynomial for |r| < 1/2 (truncation < 3e-9
-// relative), exp(r) - 1 otherwise (no cancellation there).
-__device__ __forceinline__ float expm1_small(float r) {
-  // both forms, then a select: a branch would split the wave's scan loop
-  float p = fmaf(r, 2.48015873e-5f, 1.98412698e-4f);
-  p = fmaf(r, p, 1.38888889e-3f);
+// e^r - 1 for r <= 0 (Re(lambda) <= 0 and dt >= 0): degree-6 Taylor
+// polynomial for r > -1/8 (truncation below 1e-9 relative), exp(r) - 1
+// otherwise (no cancellation there: |e^r - 1| > 0.117). Both forms are
+// computed and one selected: a branch would split the caller's scan loop.
+__device__ __forceinline__ float expm1_neg(float r, float er) {
+  float p = fmaf(r, 1.98412698e-4f, 1.38888889e-3f);
   p = fmaf(r, p, 8.33333333e-3f);
   p = fmaf(r, p, 4.16666667e-2f);
   p = fmaf(r, p, 1.66666667e-1f);
   p = fmaf(r, p, 0.5f);
   const float series = fmaf(r * r, p, r);
-  const float direct = __expf(r) - 1.0f;
-  return fabsf(r) < 0.5f ? series : direct;
+  return r > -0.125f ? series : er - 1.0f;
 }
 
 // Zero-order hold of one mode for a per-step interval dt >= 0 (the
-// time-varying path), with the half-angle taken in revolutions:
+// time-varying path), with the half-angle taken in turns:
 //   w/2 = Im(lam) dt / 2 = 2 pi th,  th = dt * Im(lam)/(4 pi) = dt * hrev.
-// Whole turns of th drop out exactly in the quarter-turn reduction, so the
-// angle's only error is the rounding of th itself, the same as rounding w.
-// Then as zoh_f32:
-//   abar - 1 = (expm1(r)(1 - 2 s^2) - 2 s^2,  e^r 2 s c),  gain = (abar - 1)/lam.
-// SEL computes the small-|z| form on every lane and selects it (no branch in
-// the caller's loop); otherwise it sits behind a branch that waves skip when
-// no lane needs it. Both give the same values.
-template <bool SEL = false>
-__device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
+// Whole turns of th drop out exactly (th - rint(th), any finite th), so the
+// angle's only error is the rounding of th itself, the same as rounding w;
+// the sine and cosine of the remaining fraction come from the hardware's
+// transcendental unit, which takes its argument in turns (measured on this
+// chip: absolute error below 1.3e-7 over a turn, relative error below 9e-7
+// for small angles).
+// With s, c = sin, cos(w/2) and r = Re(lam) dt:
+//   abar - 1 = ((e^r - 1)(1 - 2 s^2) - 2 s^2,  e^r 2 s c)
+// has no cancellation (for Re(lam) <= 0 the two terms of the real part have
+// the same sign while cos w >= 0, and otherwise the real part is below -1),
+// and gain = (abar - 1)/lam keeps the relative accuracy of abar - 1 down to
+// the smallest |lam dt|. At lam = 0 the packing stores
+// 1/lam as 0 and fz = 1, so that gain = dt there (the removable singularity).
+__device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float fz, float dt, cf& abar, cf& gain) {
   const float r = lam.re * dt;
   const float th = hrev * dt;
-  float s, c;
-  sincos_rev(th, s, c);
-  const float em1 = expm1_small(r);
-  const float er = em1 + 1.0f;
+  const float f = th - rintf(th);                 // exact: whole turns dropped, |f| <= 1/2
+  const float s = __builtin_amdgcn_sinf(f);       // hardware sine and cosine of 2 pi f
+  const float c = __builtin_amdgcn_cosf(f);
+  const float er = __expf(r);
+  const float em1 = expm1_neg(r, er);
   const float two_s2 = 2.0f * s * s;
   const float cosw = 1.0f - two_s2;
   const float sinw = 2.0f * s * c;
-  abar = {er * cosw, er * sinw};
   const cf am1 = {fmaf(em1, cosw, -two_s2), er * sinw};
-  gain = cmul(am1, inv_lam);
-  // |z| < 1e-4 (also covers lam = 0): dt * (1 + z/2 + z^2/6)
-  const float w = lam.im * dt;
-  const bool tiny = fabsf(r) + fabsf(w) < 1e-4f;
-  if (SEL || tiny) {
-    const float hr = 0.5f * r + (r * r - w * w) * (1.0f / 6.0f);
-    const float hi = 0.5f * w + (2.0f * r * w) * (1.0f / 6.0f);
-    gain = {tiny ? dt * (1.0f + hr) : gain.re, tiny ? dt * hi : gain.im};
-  }
+  abar = {1.0f + am1.re, am1.im};
+  gain = {fmaf(am1.re, inv_lam.re, fmaf(-am1.im, inv_lam.im, fz * dt)), fmaf(am1.re, inv_lam.im, am1.im * inv_lam.re)};
 }
 
 // Bilinear map of one mode for a per-step interval dt >= 0, z = lam dt:
@@ -124,13 +91,20 @@ __device__ __forceinline__ void bilinear_step(cf lam, float dt, cf& abar, cf& ga
   gain = {dt * w.re, dt * w.im};
 }
 
+// per-mode constants of the per-step discretisation: lambda, 1/lambda (0 for
+// lambda = 0), the half-angle turns per unit interval Im(lambda)/(4 pi), and
+// fz = 1 for lambda = 0 (else 0)
+struct StepMode {
+  cf lam, inv;
+  float hrev, fz;
+};
+
 // one per-step discretisation: bilinear when `bil`, else zero-order hold
-template <bool SEL = false>
-__device__ __forceinline__ void disc_step(bool bil, cf lam, cf inv_lam, float hrev, float dt, cf& abar, cf& gain) {
+__device__ __forceinline__ void disc_step(bool bil, const StepMode& m, float dt, cf& abar, cf& gain) {
   if (bil) {
-    bilinear_step(lam, dt, abar, gain);
+    bilinear_step(m.lam, dt, abar, gain);
   } else {
-    zoh_step<SEL>(lam, inv_lam, hrev, dt, abar, gain);
+    zoh_step(m.lam, m.inv, m.hrev, m.fz, dt, abar, gain);
   }
 }
 

@@ -32,7 +32,7 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
     const bool ks = keep_scan && R == 2;
     const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
                       (time_varying ? fused::mode_table_bytes(Ppad, Hpad, true, false) : 0);
-    const size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
+    size_t ls = 3 * fused::u_tile_bytes(KS, R, bf16_io) + 2 * fused::x_tile_bytes(K2, R, bf16_io) +
                       (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
     // eight-wave pass 1: two groups of u tiles and the mode table
@@ -42,6 +42,22 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
     p.R = R;
     p.keep = k;
     p.keep_scan = ks;
+    // the symmetric eight-wave pass 2: weights of a wave's share in registers
+    // (at most 128 VGPRs of them), four u tiles (three bf16 planes for float32
+    // u), two x tiles and the mode table in LDS
+    {
+      const int NT = 4 * MPW, MT = (NT + 7) / 8, HT = 2 * KS, ET = (HT + 7) / 8;
+      const int wregs = 4 * (KS * MT * 2 * NP + ET * NT * NP);
+      const size_t l8 = 4 * static_cast<size_t>(KS) * R * (bf16_io ? 1 : 3) * fused::kBlock +
+                        2 * fused::x_tile_bytes(K2, R, bf16_io) + fused::mode_table_bytes(Ppad, Hpad, time_varying, true);
+      // taken for the time-varying step, whose per-step vector work the
+      // symmetric split spreads over both waves of each SIMD; the
+      // time-invariant pass 2 is matrix-core bound and runs faster with its
+      // roles specialized
+      p.scan8 = ks && time_varying && R == 2 && KS <= 4 && MPW <= (bf16_io ? 4 : 2) && wregs <= 128 && l8 <= lds_max;
+      p.ks = KS;
+      if (p.scan8) ls = l8;
+    }
     p.group = k ? fused::reduce_group(bf16_io, time_varying) : 1;
     p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;

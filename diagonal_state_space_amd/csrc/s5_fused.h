@@ -18,10 +18,10 @@ __host__ __device__ constexpr size_t u_tile_bytes(int KS, int R, bool bf16) {
 __host__ __device__ constexpr size_t x_tile_bytes(int K2, int R, bool bf16) {
   return static_cast<size_t>(K2) * R * (bf16 ? 1 : 2) * kBlock;
 }
-// LDS bytes of the per-mode constants (abar, or lambda, 1/lambda and hrev for
-// the time-varying path) and optionally D.
+// LDS bytes of the per-mode constants (abar, or lambda, 1/lambda, hrev and fz
+// for the time-varying path) and optionally D.
 __host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool tv, bool with_d) {
-  return static_cast<size_t>(Ppad) * (tv ? 20 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
+  return static_cast<size_t>(Ppad) * (tv ? 24 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
 }
 // chunks between two barriers of the eight-wave pass 1 (u tiles of two such
 // groups in LDS; the chunk count is padded to a multiple of it). Smaller for
@@ -32,11 +32,11 @@ __host__ __device__ constexpr int reduce_group(bool bf16, bool tv) { return tv ?
 // Per-mode constants written by the packing kernel.
 struct ModeParams {
   float2 lam;      // continuous eigenvalue
-  float2 inv_lam;  // 1/lambda
+  float2 inv_lam;  // 1/lambda (0 for lambda = 0)
   float2 abar;     // exp(lambda Delta)                         (time-invariant)
   float2 aseg;     // exp(Lseg lambda Delta): one whole stream   (time-invariant)
   float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval
-  float pad_;
+  float fz;        // 1 for lambda = 0, else 0 (the per-step gain is then the interval)
   float2 alast;    // abar^m, m = ((L-1) mod Lseg) + 1: the stream holding token
                    // L-1, from its first token through L-1  (time-invariant)
 };
@@ -89,6 +89,8 @@ struct FusedPlan {
   int R = 0, nck = 0, Lseg = 0, Q = 0;
   bool keep = false;        // pass 1 holds B_bar in registers (eight-wave kernel)
   bool keep_scan = false;   // pass 2 holds B_bar and C' in registers (wave-specialized kernel)
+  bool scan8 = false;       // pass 2 on the symmetric eight-wave kernel (with keep_scan)
+  int ks = 0;               // its drive K-steps (Hpad / 32)
   int group = 1;            // nck is a multiple of this (reduce_group with `keep`)
   size_t lds_reduce = 0, lds_scan = 0, lds_reduce_ws = 0;
 };

@@ -20,10 +20,43 @@ constexpr bool kTV = S5_INST_TV != 0;
 // every operand, so there only up to two mode tiles per wave.
 constexpr int kKeepMaxMPW = kBF16 ? 4 : 2;
 
+// the symmetric pass-2 kernel, instanced for 1..4 drive K-steps (H <= 128)
+// and the time-varying step
+template <int MPW, int KS>
+hipError_t scan8_ks(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  // instances whose LDS (four u tiles, two x tiles, the mode table) fits
+  constexpr size_t lds = 4 * fused::u8_tile_bytes(KS, 2, kBF16) + 2 * fused::x_tile_bytes(4 * MPW, 2, kBF16) +
+                         fused::mode_table_bytes(64 * MPW, 32 * KS, kTV, true);
+  if constexpr (lds > 160 * 1024) {
+    return hipErrorInvalidValue;
+  } else {
+    return fused::launch_scan8_t<MPW, KS, kTV, kBF16>(q, p, s);
+  }
+}
+
+template <int MPW>
+hipError_t scan8(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  // the plan takes it for the time-varying step with at most two mode tiles per wave
+  if constexpr (MPW > kKeepMaxMPW || !kTV || MPW > 2) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (p.ks) {
+      case 1: return scan8_ks<MPW, 1>(q, p, s);
+      case 2: return scan8_ks<MPW, 2>(q, p, s);
+      case 3: return scan8_ks<MPW, 3>(q, p, s);
+      case 4: return scan8_ks<MPW, 4>(q, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
 template <bool REDUCE, int MPW, int R, bool KEEP>
 hipError_t one(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   if constexpr (KEEP && (MPW > kKeepMaxMPW || R != 2)) {
     return hipErrorInvalidValue;
+  } else if constexpr (!REDUCE && KEEP) {
+    if (p.scan8) return scan8<MPW>(q, p, s);
+    return fused::launch_scan_t<MPW, R, kTV, kBF16, KEEP>(q, p, s);
   } else if constexpr (REDUCE) {
     return fused::launch_reduce_t<MPW, R, kTV, kBF16, KEEP>(q, p, s);
   } else {

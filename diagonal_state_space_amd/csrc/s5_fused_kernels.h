@@ -546,7 +546,13 @@ struct ModeTable {
   S5_LDS pf2* ab;      // abar (time-invariant) or lambda (time-varying)   [Ppad]
   S5_LDS pf2* il;      // 1/lambda (time-varying)                          [Ppad]
   S5_LDS float* hr;    // hrev (time-varying)                              [Ppad]
+  S5_LDS float* fz;    // 1 for lambda = 0 (time-varying)                  [Ppad]
   S5_LDS float* d;     // D, zero past H (pass 2)                          [Hpad]
+
+  // the per-step discretisation's constants of mode p (time-varying)
+  __device__ __forceinline__ StepMode step_mode(int p) const {
+    return {ld_pf2(ab + p), ld_pf2(il + p), hr[p], fz[p]};
+  }
 };
 
 template <bool TV>
@@ -555,13 +561,15 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
   mt.ab = reinterpret_cast<S5_LDS pf2*>(base);
   mt.il = mt.ab + q.Ppad;
   mt.hr = reinterpret_cast<S5_LDS float*>(TV ? mt.il + q.Ppad : mt.ab + q.Ppad);
-  mt.d = TV ? mt.hr + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
+  mt.fz = mt.hr + (TV ? q.Ppad : 0);
+  mt.d = TV ? mt.fz + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
   for (int p = threadIdx.x; p < q.Ppad; p += kThreads) {
     const ModeParams& mq = q.modes[p];
     if constexpr (TV) {
       st_pf2(mt.ab + p, mq.lam.x, mq.lam.y);
       st_pf2(mt.il + p, mq.inv_lam.x, mq.inv_lam.y);
       mt.hr[p] = mq.hrev;
+      mt.fz[p] = mq.fz;
     } else {
       st_pf2(mt.ab + p, mq.abar.x, mq.abar.y);
     }
@@ -644,15 +652,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
         cf x = z[jj][r];
         const int pmr = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
         if constexpr (TV) {
-          const int pm = pmr;
-          const cf lam = ld_pf2(mt.ab + pm);
-          const cf inv = ld_pf2(mt.il + pm);
-          const float hrev = mt.hr[pm];
+          const StepMode sm = mt.step_mode(pmr);
           cf Ar = A[jj][r];
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            disc_step(bil, lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
+            disc_step(bil, sm, f4_at(dl[jj][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
             Ar = cmul(a, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pmr, x, Ar);
@@ -840,14 +845,12 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         const int pm = 16 * j + 4 * ln.g + r;
         cf x = z[m][r];
         if constexpr (TV) {
-          const cf lam = ld_pf2(mt.ab + pm);
-          const cf inv = ld_pf2(mt.il + pm);
-          const float hrev = mt.hr[pm];
+          const StepMode sm = mt.step_mode(pm);
           cf Ar = A[m][r];
 #pragma unroll
           for (int n = 0; n < R; ++n) {
             cf a, gn;
-            disc_step(bil, lam, inv, hrev, f4_at(dl[m][n], r), a, gn);
+            disc_step(bil, sm, f4_at(dl[m][n], r), a, gn);
             x = cfma(a, x, cmul(gn, {acc[m][0][n][r], acc[m][1][n][r]}));
             Ar = cmul(a, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, Ar);
@@ -881,6 +884,11 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       for (int c = 0; c < G; ++c) stash_u<R, BF16, NB, NW8, !BF16>(q, ust[c], lds + c * ut);
     }
     lds_barrier();   // mode table, u tiles of group 0
+    // Delta of the chunk being scanned (time-varying), loaded a chunk ahead:
+    // waiting for a global load issued right before its use exposed its
+    // whole latency on every chunk
+    float4 dl[TV ? M8 : 1][TV ? R : 1];
+    delta(0, dl);
     for (int i0 = 0; i0 < q.nck; i0 += G) {
       const int half = (i0 / G) & 1;
       UStage<NB> ust[G];
@@ -891,15 +899,26 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll 1
       for (int c = 0; c < G; ++c) {
         f32x4 acc[M8][2][R];
-        float4 dl[TV ? M8 : 1][TV ? R : 1];
-        delta(i0 + c, dl);
+        float4 dnext[TV ? M8 : 1][TV ? R : 1];
+        delta(i0 + c + 1, dnext);
         mma(lds + (half * G + c) * ut, acc);
+        // the MFMAs as one burst, then the discretisation and scan: the two
+        // waves of a SIMD alternate between the matrix core and the vector
+        // unit (interleaving them in both waves made each wave's vector work
+        // wait behind the other wave's MFMAs)
+        if constexpr (TV) __builtin_amdgcn_sched_barrier(0);
         if constexpr (TV) {
           scan(std::false_type{}, EXT && cap_chunk == i0 + c, acc, dl);
         } else if (EXT && cap_chunk == i0 + c) {
           scan(std::true_type{}, false, acc, dl);
         } else {
           scan(std::false_type{}, false, acc, dl);
+        }
+        if constexpr (TV) {
+#pragma unroll
+          for (int m = 0; m < M8; ++m)
+#pragma unroll
+            for (int n = 0; n < R; ++n) dl[m][n] = dnext[m][n];
         }
       }
       // the next group's tiles into the other half (read by the previous group
@@ -1391,22 +1410,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
     cf x = st[jj][r];
     if constexpr (TV) {
       const int pm = 16 * (ln.w + kWaves * jj) + 4 * ln.g + r;
-      cf lam, inv;
-      float hrev;
+      StepMode sm;
       if constexpr (KEEP) {
-        lam = ld_pf2(mt.ab + pm);
-        inv = ld_pf2(mt.il + pm);
-        hrev = mt.hr[pm];
+        sm = mt.step_mode(pm);
       } else {
         const ModeParams& mq = q.modes[pm];
-        lam = {mq.lam.x, mq.lam.y};
-        inv = {mq.inv_lam.x, mq.inv_lam.y};
-        hrev = mq.hrev;
+        sm = {{mq.lam.x, mq.lam.y}, {mq.inv_lam.x, mq.inv_lam.y}, mq.hrev, mq.fz};
       }
 #pragma unroll
       for (int n = 0; n < R; ++n) {
         cf a, gn;
-        disc_step(bil, lam, inv, hrev, f4_at(dl[jj][n], r), a, gn);
+        disc_step(bil, sm, f4_at(dl[jj][n], r), a, gn);
         x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
         acc[jj][0][n][r] = x.re;
         acc[jj][1][n][r] = x.im;
@@ -1609,13 +1623,11 @@ __device__ __forceinline__ void drive_scan_tiles(bool bil, int j0, int KS, const
       const int pm = 16 * (ln.w + kWaves * j) + 4 * ln.g + r;
       cf x = st[j][r];
       if constexpr (TV) {
-        const cf lam = ld_pf2(mt.ab + pm);
-        const cf inv = ld_pf2(mt.il + pm);
-        const float hrev = mt.hr[pm];
+        const StepMode sm = mt.step_mode(pm);
 #pragma unroll
         for (int n = 0; n < R; ++n) {
           cf a, gn;
-          disc_step<true>(bil, lam, inv, hrev, f4_at(dl[j][n], r), a, gn);
+          disc_step(bil, sm, f4_at(dl[j][n], r), a, gn);
           x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
           acc[jj][0][n][r] = x.re;
           acc[jj][1][n][r] = x.im;
@@ -1827,6 +1839,14 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   }
 }
 
+}  // namespace fused
+}  // namespace s5
+
+#include "s5_scan8.h"
+
+namespace s5 {
+namespace fused {
+
 // ---- launch -----------------------------------------------------------------------------
 
 template <auto Kern>
@@ -1856,18 +1876,43 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
   }
 }
 
+// pass 2 on the symmetric eight-wave kernel (KS drive K-steps)
+template <int MPW, int KS, bool TV, bool BF16>
+hipError_t launch_scan8_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
+  const int blocks = q.B * q.Q;
+  if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
+  const int xm = q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
+  if constexpr (TV) {
+    if (xm == 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
+  } else {
+    if (xm == 3) return launch_one<k_scan8<MPW, KS, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+  }
+  if (xm == 2) return launch_one<k_scan8<MPW, KS, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+  if (xm == 1) return launch_one<k_scan8<MPW, KS, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+  return launch_one<k_scan8<MPW, KS, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+}
+
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
   if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
   const int xm = q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
-  if constexpr (KEEP) {
-    if (xm == 3) return launch_one<k_scan_ws<MPW, R, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+  if constexpr (TV) {
+    if (xm == 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
+  }
+  if constexpr (KEEP && TV && MPW > 2) {
+    return hipErrorInvalidValue;   // not planned: the time-varying step keeps at most two tiles per wave
+  } else if constexpr (KEEP) {
+    if constexpr (!TV) {
+      if (xm == 3) return launch_one<k_scan_ws<MPW, R, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    }
     if (xm == 2) return launch_one<k_scan_ws<MPW, R, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
     if (xm == 1) return launch_one<k_scan_ws<MPW, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
     return launch_one<k_scan_ws<MPW, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_scan, s, q);
   } else {
-    if (xm == 3) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 3>>(blocks, kThreads, p.lds_scan, s, q);
+    if constexpr (!TV) {
+      if (xm == 3) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 3>>(blocks, kThreads, p.lds_scan, s, q);
+    }
     if (xm == 2) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 2>>(blocks, kThreads, p.lds_scan, s, q);
     if (xm == 1) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_scan, s, q);
     return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 0>>(blocks, kThreads, p.lds_scan, s, q);

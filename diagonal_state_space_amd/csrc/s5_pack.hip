@@ -80,8 +80,10 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
         mp.lam = make_float2(q.lam[p].x, q.lam[p].y);
-        const zd il = f64::zdiv({1.0, 0.0}, lam);
+        const bool zero = lam.re == 0.0 && lam.im == 0.0;
+        const zd il = zero ? zd{0.0, 0.0} : f64::zdiv({1.0, 0.0}, lam);
         mp.inv_lam = make_float2(static_cast<float>(il.re), static_cast<float>(il.im));
+        mp.fz = zero ? 1.0f : 0.0f;
         mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
         if (!q.time_varying) {
           const double dt = exp(static_cast<double>(q.log_delta[p]));

@@ -1,0 +1,498 @@
+// Pass 2 of the fused S5 forward path with eight symmetric waves (gfx950).
+// Included by s5_fused_kernels.h after the helpers it uses.
+//
+// Every wave does, for each chunk, the same three kinds of work on its own
+// share: the drive (B_bar u on MFMA) and the scan of its mode tiles
+// j = w + 8 m, the readout (C' x on MFMA) of its h-tiles ht = w + 8 e with
+// their D u feedthrough and y stores, and a share of staging the next u tiles.
+// Both waves of a SIMD therefore mix matrix-core and vector work, and the y
+// epilogue of chunk i-1 is issued beside the readout MFMAs of chunk i (it
+// needs only that chunk's sums, kept in registers across the barrier), so the
+// epilogue's vector work and stores hide under matrix-core work instead of
+// following it. The drive's K-step count KS (Hpad = 32 KS) is a template
+// parameter: no MFMA multiplies padding.
+//
+// LDS: four u tiles (tile c in buffer c & 3: staged in iteration c-2, driven
+// in iteration c-1, its feedthrough read in iteration c+1), two x tiles and
+// the per-mode table with D. Float32 u is staged as three bf16 planes hi,
+// lo = bf16(u - hi), lo2 = bf16(u - hi - lo): u = hi + lo + lo2 exactly (each
+// residual is exact in float32 and has at most 16, then 8, significant
+// bits), so the drive's operands hi and lo are split once per tile and the
+// feedthrough still reads u exactly.
+#pragma once
+
+namespace s5 {
+namespace fused {
+
+constexpr int kW8 = 2 * kWaves;   // waves of the symmetric kernel
+
+// bytes of one u tile (KS K-steps x R steps; one bf16 plane, or three for float32 u)
+__host__ __device__ constexpr size_t u8_tile_bytes(int KS, int R, bool bf16) {
+  return static_cast<size_t>(KS) * R * (bf16 ? 1 : 3) * kBlock;
+}
+
+template <int R, bool BF16, int NB>
+__device__ __forceinline__ void stash8(const FusedParams& q, const UStage<NB>& st, lds_byte* ub, int w, int l) {
+  const int nblk = (q.Hpad >> 5) * R * (BF16 ? 1 : 2);
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int blk = w + kW8 * e;
+    if (blk >= nblk) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): see stash_u
+      continue;
+    }
+    if constexpr (BF16) {
+      lds_st<uint4>(ub + blk * kBlock + l * 16, st.v[e]);
+    } else {
+      // half-block: elements 4 half .. 4 half + 3 of fragment f = s R + n
+      const int half = blk & 1;
+      const int f = blk >> 1;
+      const f32x4 v = {__uint_as_float(st.v[e].x), __uint_as_float(st.v[e].y), __uint_as_float(st.v[e].z),
+                       __uint_as_float(st.v[e].w)};
+      const bf16x4 hi = __builtin_convertvector(v, bf16x4);
+      const f32x4 r1 = v - __builtin_convertvector(hi, f32x4);
+      const bf16x4 lo = __builtin_convertvector(r1, bf16x4);
+      const bf16x4 lo2 = __builtin_convertvector(r1 - __builtin_convertvector(lo, f32x4), bf16x4);
+      lds_byte* p = ub + (f * 3) * kBlock + l * 16 + 8 * half;
+      lds_st<uint2>(p, __builtin_bit_cast(uint2, hi));
+      lds_st<uint2>(p + kBlock, __builtin_bit_cast(uint2, lo));
+      lds_st<uint2>(p + 2 * kBlock, __builtin_bit_cast(uint2, lo2));
+    }
+  }
+}
+
+// y already in memory for the wave's readout outputs of chunk i (the backward
+// scan adds to it), loaded an iteration ahead of its use (see load_y_old)
+template <int R, bool BF16, bool VEC, int ET>
+__device__ __forceinline__ void load_y_old8(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm, int i,
+                                            int w, const Lane& ln, YOld<BF16>& o) {
+  static_assert(R <= 2 && ET <= kKeepHT, "YOld holds two steps of two h-tiles");
+  constexpr int esz = BF16 ? 2 : 4;
+#pragma unroll
+  for (int e = 0; e < ET; ++e) {
+    const int h0 = 16 * (w + kW8 * e) + 4 * ln.g;
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      const int roff = rm(rel_row<R>(q, ln.t, i, n)) * q.H;
+      if constexpr (VEC) {
+        const int off = h0 < q.H ? (roff + h0) * esz : kBufferOOB;
+        if constexpr (BF16) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0);
+          o.v[e][n] = make_uint2(v[0], v[1]);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0);
+          o.v[e][n] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+        uint32_t v4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int off = h0 + m < q.H ? (roff + h0 + m) * esz : kBufferOOB;
+          v4[m] = BF16 ? static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(yr, off, 0, 0))
+                       : __builtin_amdgcn_raw_buffer_load_b32(yr, off, 0, 0);
+        }
+        if constexpr (BF16) {
+          o.v[e][n] = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
+        } else {
+          o.v[e][n] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+        }
+      }
+    }
+  }
+}
+
+// drive operand fragments of K-step s: [plane][n] (hi, and lo for float32 u)
+template <int R, bool BF16>
+__device__ __forceinline__ void get_u8(const lds_byte* ub, int s, int l, bf16x8 (&uf)[BF16 ? 1 : 2][R]) {
+#pragma unroll
+  for (int n = 0; n < R; ++n) {
+    if constexpr (BF16) {
+      uf[0][n] = as_bf16x8(lds_ld<uint4>(ub + (s * R + n) * kBlock + l * 16));
+    } else {
+      uf[0][n] = as_bf16x8(lds_ld<uint4>(ub + ((s * R + n) * 3) * kBlock + l * 16));
+      uf[1][n] = as_bf16x8(lds_ld<uint4>(ub + ((s * R + n) * 3 + 1) * kBlock + l * 16));
+    }
+  }
+}
+
+// u of the readout lane's 4 outputs, features 16 ht + 4 g + 0..3 of token
+// (t, n): K-step ht/2, lane t + 16 (2 (ht & 1) + g/2), elements 4 (g & 1)..+3
+template <int R, bool BF16>
+__device__ __forceinline__ void u_for_y8(const lds_byte* ub, int ht, int n, int t, int g, float (&uv)[4]) {
+  const int s = ht >> 1;
+  const int lp = t + 16 * (2 * (ht & 1) + (g >> 1));
+  const int off = lp * 16 + 8 * (g & 1);
+  auto four = [](uint2 p, float (&o)[4]) {
+    o[0] = __uint_as_float(p.x << 16);
+    o[1] = __uint_as_float(p.x & 0xffff0000u);
+    o[2] = __uint_as_float(p.y << 16);
+    o[3] = __uint_as_float(p.y & 0xffff0000u);
+  };
+  if constexpr (BF16) {
+    four(lds_ld<uint2>(ub + (s * R + n) * kBlock + off), uv);
+  } else {
+    const lds_byte* p = ub + ((s * R + n) * 3) * kBlock + off;
+    float hi[4], lo[4], lo2[4];
+    four(lds_ld<uint2>(p), hi);
+    four(lds_ld<uint2>(p + kBlock), lo);
+    four(lds_ld<uint2>(p + 2 * kBlock), lo2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) uv[r] = (hi[r] + lo[r]) + lo2[r];   // exact: u itself
+  }
+}
+
+// Delta of chunk i for the lane's 4 modes of each of the wave's tiles
+template <int MT, int NT, int R>
+__device__ __forceinline__ void load_delta8(const FusedParams& q, int b, int qq, int i, int w, const Lane& ln,
+                                            float4 (&dl)[MT][R]) {
+  const bool vec = (q.P & 3) == 0;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int pm0 = 16 * (w + kW8 * m) + 4 * ln.g;
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      const int tok = tok_of<R>(q, qq, ln.t, i, n);
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (w + kW8 * m < NT && tok < q.L && pm0 < q.P) {
+        const float* dp = q.delta + range_row0(q, b, qq) * q.P +
+                          (rel_row<R>(q, ln.t, i, n) * static_cast<uint32_t>(q.P) + pm0);
+        if (vec) {
+          const float4 x = *reinterpret_cast<const float4*>(dp);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = pm0 + r < q.P ? dp[r] : 0.0f;
+        }
+      }
+      dl[m][n] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// state entering the lane's stream for the wave's tiles (see stream_start)
+template <int MT, int NT, bool TV>
+__device__ __forceinline__ void stream_start8(const FusedParams& q, int bq, int w, const Lane& ln,
+                                              const S5_LDS pf2* s_c0, cf (&st)[MT][4]) {
+  float2 xv[MT][4], av[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = w + kW8 * m;
+      const int pm = 16 * j + 4 * ln.g + r;
+      xv[m][r] = make_float2(0.0f, 0.0f);
+      av[m][r] = make_float2(1.0f, 0.0f);
+      if (j < NT) {
+        const size_t si = (static_cast<size_t>(bq) * kStreams + ln.t) * q.Ppad + pm;
+        xv[m][r] = q.sagg[si];
+        av[m][r] = TV ? q.sagg_a[si] : q.modes[pm].aseg;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = w + kW8 * m;
+      cf X = {xv[m][r].x, xv[m][r].y};
+      cf A = {av[m][r].x, av[m][r].y};
+      row_scan(A, X);
+      const cf Ae = {row_shr<1>(A.re, 1.0f), row_shr<1>(A.im, 0.0f)};
+      const cf Xe = {row_shr<1>(X.re, 0.0f), row_shr<1>(X.im, 0.0f)};
+      st[m][r] = j < NT ? cfma(Ae, ld_pf2(s_c0 + (16 * j + 4 * ln.g + r)), Xe) : cf{0.0f, 0.0f};
+    }
+  }
+}
+
+// the state after token L-1 for the wave's modes (see write_final_state)
+template <int R, int MT, int NT, bool TV>
+__device__ __forceinline__ void write_final_state8(const FusedParams& q, int b, const LastTok& lt, int w,
+                                                   const Lane& ln, const cf (&st)[MT][4]) {
+  if (ln.t != lt.t) return;
+  const float2* c = q.cap + static_cast<size_t>(b) * 2 * q.Ppad;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = w + kW8 * m;
+      const int pm = 16 * j + 4 * ln.g + r;
+      if (j >= NT || pm >= q.P) continue;
+      const cf X = {c[pm].x, c[pm].y};
+      cf A;
+      if constexpr (TV) {
+        A = {c[q.Ppad + pm].x, c[q.Ppad + pm].y};
+      } else {
+        const float2 al = q.modes[pm].alast;
+        A = {al.x, al.y};
+      }
+      const cf x = cfma(A, st[m][r], X);
+      q.xlast[static_cast<size_t>(b) * q.P + pm] = make_float2(x.re, x.im);
+    }
+}
+
+// Drive, scan and x tile of the wave's mode tiles for one chunk (u tile ub,
+// x tile xb). Tile by tile, so that one tile's scan runs beside the next
+// tile's MFMAs. bf16: the chunk's u fragments are read once for all tiles.
+template <int MT, int NT, int KS, int R, bool TV, bool BF16>
+__device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[KS][MT][2][BF16 ? 1 : 2],
+                                            const lds_byte* ub, const ModeTable& mtab, const Lane& ln,
+                                            const float4 (&dl)[TV ? MT : 1][TV ? R : 1], cf (&st)[MT][4],
+                                            lds_byte* xb) {
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int K2 = NT;   // readout K-steps = mode tiles
+  constexpr bool kOnce = BF16 && MT > 1;
+  bf16x8 ua[kOnce ? KS : 1][NP][R];
+  if constexpr (kOnce) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) get_u8<R, BF16>(ub, s, ln.l, ua[s]);
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int j = w + kW8 * m;
+    if ((NT % kW8) != 0 && j >= NT) continue;   // wave-uniform
+    f32x4 acc[2][R];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int n = 0; n < R; ++n) acc[cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 uk[NP][R];
+      if constexpr (kOnce) {
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+          for (int n = 0; n < R; ++n) uk[pl][n] = ua[s][pl][n];
+      } else {
+        get_u8<R, BF16>(ub, s, ln.l, uk);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          acc[cc][n] = mfma(bw[s][m][cc][0], uk[0][n], acc[cc][n]);
+          if constexpr (NP == 2) {
+            acc[cc][n] = mfma(bw[s][m][cc][0], uk[1][n], acc[cc][n]);
+            acc[cc][n] = mfma(bw[s][m][cc][1], uk[0][n], acc[cc][n]);
+          }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pm = 16 * j + 4 * ln.g + r;
+      cf x = st[m][r];
+      if constexpr (TV) {
+        const StepMode sm = mtab.step_mode(pm);
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          cf a, gn;
+          disc_step(bil, sm, f4_at(dl[m][n], r), a, gn);
+          x = cfma(a, x, cmul(gn, {acc[0][n][r], acc[1][n][r]}));
+          acc[0][n][r] = x.re;
+          acc[1][n][r] = x.im;
+        }
+      } else {
+        const cf ab = ld_pf2(mtab.ab + pm);
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          x = cfma(ab, x, {acc[0][n][r], acc[1][n][r]});
+          acc[0][n][r] = x.re;
+          acc[1][n][r] = x.im;
+        }
+      }
+      st[m][r] = x;
+    }
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[2 * r] = acc[0][n][r];
+        v[2 * r + 1] = acc[1][n][r];
+      }
+      const int blk = j * R + n;
+      uint4 hi, lo;
+      put_frag(v, &hi, BF16 ? nullptr : &lo);
+      lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
+      if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+    }
+  }
+}
+
+template <int MPW, int KS, bool TV, bool BF16, int XM>
+__global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
+  constexpr bool EXT = XM != 0;   // options of the extended entry point
+  constexpr int R = 2;
+  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int NT = 4 * MPW;                   // mode tiles (= readout K-steps)
+  constexpr int K2 = NT;
+  constexpr int MT = (NT + kW8 - 1) / kW8;      // mode tiles per wave, at most
+  constexpr int HT = 2 * KS;                    // h-tiles
+  constexpr int ET = (HT + kW8 - 1) / kW8;      // h-tiles per wave, at most
+  constexpr bool kAcc = XM == 3;                // backward scan: add to y
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R) return;   // dispatch mismatch: do nothing
+  Lane ln = lane_ids();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (kW8 - 1);
+  ln.w = w;
+  const int bq = blockIdx.x;
+  const int b = bq / q.Q;
+  const int qq = bq - b * q.Q;
+  const bool bil = EXT && q.bilinear;
+  const RowMap rmap = row_map<XM == 3>(q, qq);
+  constexpr int ut = static_cast<int>(u8_tile_bytes(KS, R, BF16));
+  constexpr int xt = static_cast<int>(x_tile_bytes(K2, R, BF16));
+  lds_byte* lds = (lds_byte*)smem;
+  lds_byte* xlds = lds + 4 * ut;
+  const ModeTable mtab = fill_mode_table<TV>(q, xlds + 2 * xt, true);
+  S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
+  if (threadIdx.x < static_cast<unsigned>(q.Ppad)) range_carry<EXT>(q, b, qq, threadIdx.x, s_c0);
+
+  // weights: B_bar fragments of the wave's mode tiles, C' fragments of its h-tiles
+  bf16x8 bw[KS][MT][2][NP];
+  bf16x8 cw[ET][K2][NP];
+  {
+    const int nb = (q.Ppad / 16) * 2 * KS * 64;
+    const int nc = (q.Hpad / 16) * K2 * 64;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) {
+            const int j = w + kW8 * m;
+            bw[s][m][cc][pl] = j < NT ? as_bf16x8(ldg16(q.bpack + pl * nb + ((j * 2 + cc) * KS + s) * 64 + ln.l))
+                                      : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+          }
+#pragma unroll
+    for (int e = 0; e < ET; ++e)
+#pragma unroll
+      for (int s = 0; s < K2; ++s)
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) {
+          const int ht = w + kW8 * e;
+          cw[e][s][pl] = ht < HT ? as_bf16x8(ldg16(q.cpack + pl * nc + (ht * K2 + s) * 64 + ln.l))
+                                 : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+        }
+  }
+
+  constexpr int NB = (KS * R * (BF16 ? 1 : 2) + kW8 - 1) / kW8;
+  const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
+  const int HTv = (q.H + 15) >> 4;   // h-tiles holding a feature < H
+  const Epi ep = epilogue<XM>(q);
+
+  auto chunks = [&](auto vec_c) {
+    constexpr bool VEC = decltype(vec_c)::value;
+    {
+      UStage<NB> ust;
+      fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, 0, ust);
+      stash8<R, BF16, NB>(q, ust, lds, w, ln.l);
+      fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, 1, ust);
+      stash8<R, BF16, NB>(q, ust, lds + ut, w, ln.l);
+    }
+    lds_barrier();   // carry, mode table, u tiles 0 and 1
+    float4 dk[ET];   // D of the wave's h-tiles: features 16 ht + 4 g + 0..3
+#pragma unroll
+    for (int e = 0; e < ET; ++e) {
+      const int h0 = 16 * (w + kW8 * e) + 4 * ln.g;
+      dk[e] = h0 < q.Hpad ? lds_ld<float4>(reinterpret_cast<const lds_byte*>(mtab.d + h0))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    cf st[MT][4];
+    stream_start8<MT, NT, TV>(q, bq, w, ln, s_c0, st);
+    if (EXT && q.xlast != nullptr) {
+      const LastTok lt = last_token<R>(q);
+      if (qq == lt.qq) write_final_state8<R, MT, NT, TV>(q, b, lt, w, ln, st);
+    }
+    float4 dl[TV ? MT : 1][TV ? R : 1];
+    if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, 0, w, ln, dl);
+    drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
+    // Delta of chunk i+1 is loaded an iteration ahead (before that
+    // iteration's u loads), so that waiting for it never waits for them
+    if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, 1, w, ln, dl);
+    lds_barrier();   // x tile 0 (and the carry read before x tile 1 is written)
+
+    // Iteration i: readout of chunk i (x tile i & 1), y of chunk i-1 (its
+    // sums from the previous iteration, u tile i-1), drive and scan of chunk
+    // i+1 (u tile i+1 -> x tile (i+1) & 1), u tile i+2 staged. The drive of
+    // the chunk after the last reads a tile of zeros (harmless, unread).
+    f32x4 yprev[ET][R];
+    YOld<BF16> yold_prev, yold_cur;
+#pragma unroll
+    for (int e = 0; e < ET; ++e)
+#pragma unroll
+      for (int n = 0; n < R; ++n) yprev[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto epilogue_of = [&](int c, const f32x4 (&ya)[ET][R], const YOld<BF16>& yo) __attribute__((always_inline)) {
+      const lds_byte* ub = lds + (c & 3) * ut;
+#pragma unroll
+      for (int e = 0; e < ET; ++e) {
+        const int ht = w + kW8 * e;
+        if (ht >= HTv) continue;   // wave-uniform
+        const int h0 = 16 * ht + 4 * ln.g;
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          float uv[4];
+          u_for_y8<R, BF16>(ub, ht, n, ln.t, ln.g, uv);
+          f32x4 a = ya[e][n];
+          if constexpr (kAcc) a += y_old_f32<BF16>(yo.v[e][n]);
+          store_y<BF16, VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, a, dk[e], uv,
+                             Epi{false, ep.gelu, ep.tanh_form});
+        }
+      }
+    };
+    for (int i = 0; i < q.nck; ++i) {
+      float4 dnext[TV ? MT : 1][TV ? R : 1];
+      if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, i + 2, w, ln, dnext);
+      UStage<NB> ust;
+      fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, i + 2, ust);
+      if constexpr (kAcc) load_y_old8<R, BF16, VEC, ET>(q, yrsrc, rmap, i, w, ln, yold_cur);
+      // readout of chunk i
+      f32x4 yacc[ET][R];
+#pragma unroll
+      for (int e = 0; e < ET; ++e)
+#pragma unroll
+        for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const lds_byte* xr = xlds + (i & 1) * xt;
+      if (w < HT) {   // wave-uniform: waves past the h-tiles read nothing out
+#pragma unroll
+        for (int s = 0; s < K2; ++s) {
+          bf16x8 xf[NP][R];
+          get_x<R, NP>(xr, K2, s, ln.l, xf);
+#pragma unroll
+          for (int e = 0; e < ET; ++e) mfma_read<R, NP>(cw[e][s], xf, yacc[e]);
+        }
+      }
+      // y of chunk i-1 beside those MFMAs
+      if (i > 0) epilogue_of(i - 1, yprev, yold_prev);
+      // drive and scan of chunk i+1
+      drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
+                                           xlds + ((i + 1) & 1) * xt);
+      __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the chunk's work
+      stash8<R, BF16, NB>(q, ust, lds + ((i + 2) & 3) * ut, w, ln.l);
+#pragma unroll
+      for (int e = 0; e < ET; ++e)
+#pragma unroll
+        for (int n = 0; n < R; ++n) yprev[e][n] = yacc[e][n];
+      if constexpr (kAcc) yold_prev = yold_cur;
+      if constexpr (TV) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int n = 0; n < R; ++n) dl[m][n] = dnext[m][n];
+      }
+      lds_barrier();   // x tile i+1, u tile i+2 complete; x tile i, u tile i-2 free
+    }
+    epilogue_of(q.nck - 1, yprev, yold_prev);
+  };
+  if (u_rows_vectorized(q.H, BF16)) {
+    chunks(std::true_type{});
+  } else {
+    chunks(std::false_type{});
+  }
+}
+
+}  // namespace fused
+}  // namespace s5
