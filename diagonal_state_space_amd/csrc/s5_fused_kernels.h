@@ -722,7 +722,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 // Wave w (0..7) owns mode tiles j = w + 8 jj (j < 4 MPW): half the weights
 // and states of a four-wave split, so two waves fit on each SIMD and one
 // wave's scan overlaps the other's MFMAs. All waves share each u tile.
-template <int MPW, int R, bool TV, bool BF16, int XM>
+// KS: the drive's K-steps (Hpad = 32 KS, at most 4), so that no MFMA multiplies padding.
+template <int MPW, int KS, int R, bool TV, bool BF16, int XM>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr bool EXT = XM != 0;   // options of the extended entry point
   constexpr int NP = BF16 ? 1 : 2;
@@ -730,7 +731,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NT = 4 * MPW;                 // mode tiles
   constexpr int M8 = (NT + NW8 - 1) / NW8;    // tiles per wave, at most
   extern __shared__ __align__(16) unsigned char smem[];
-  if (q.Ppad != 64 * MPW || q.R != R || q.nck % reduce_group(BF16, TV) != 0) return;   // dispatch mismatch
+  if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R || q.nck % reduce_group(BF16, TV) != 0) return;   // dispatch mismatch
   Lane ln = lane_ids();
   ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW8 - 1);   // 0..7
   const int bq = blockIdx.x;
@@ -740,17 +741,16 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   const RowMap rmap = row_map<EXT>(q, qq);     // forward or reverse time
   const LastTok lt = last_token<R>(q);
   const int cap_chunk = EXT && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
-  const int KS = q.Hpad >> 5;
-  const int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
+  constexpr int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
   const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16, TV) * ut, false);
 
   // B_bar fragments of the wave's tiles, all K-steps: [s][m][cc][pl]
-  bf16x8 bw[kKeepKS][M8][2][NP];
+  bf16x8 bw[KS][M8][2][NP];
   {
     const int nb = (q.Ppad / 16) * 2 * KS * 64;
 #pragma unroll
-    for (int s = 0; s < kKeepKS; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int m = 0; m < M8; ++m)
 #pragma unroll
@@ -758,7 +758,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll
           for (int pl = 0; pl < NP; ++pl) {
             const int j = ln.w + NW8 * m;
-            bw[s][m][cc][pl] = (s < KS && j < NT)
+            bw[s][m][cc][pl] = j < NT
                 ? as_bf16x8(ldg16(q.bpack + pl * nb + ((j * 2 + cc) * KS + s) * 64 + ln.l))
                 : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
           }
@@ -773,7 +773,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       if constexpr (TV) A[m][r] = {1.0f, 0.0f};
     }
 
-  constexpr int NB = u_stage_blocks<R, BF16, true, NW8>();
+  constexpr int NB = (KS * R * (BF16 ? 1 : 2) + NW8 - 1) / NW8;   // u staging blocks per wave
   constexpr int G = reduce_group(BF16, TV);   // chunks per barrier (nck is a multiple of G)
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
 
@@ -812,9 +812,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
 #pragma unroll
         for (int n = 0; n < R; ++n) acc[m][cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < kKeepKS; ++s) {
+    for (int s = 0; s < KS; ++s) {
       bf16x8 uf[NP][R];
-      get_u<R, BF16, !BF16>(ub, s < KS ? s : KS - 1, ln.l, uf);
+      get_u<R, BF16, !BF16>(ub, s, ln.l, uf);
 #pragma unroll
       for (int m = 0; m < M8; ++m)
 #pragma unroll
@@ -1868,8 +1868,18 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
   const int blocks = q.B * q.Q;
   const bool xm = q.x0 != nullptr || q.xlast != nullptr || q.rev || (q.bilinear && TV);
   if constexpr (KEEP) {
-    if (xm) return launch_one<k_reduce_ws<MPW, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
-    return launch_one<k_reduce_ws<MPW, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+    auto go = [&](auto ks_c) {
+      constexpr int KS = decltype(ks_c)::value;
+      if (xm) return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+      return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+    };
+    switch (p.ks) {   // the drive's K-steps (H <= 128)
+      case 1: return go(std::integral_constant<int, 1>{});
+      case 2: return go(std::integral_constant<int, 2>{});
+      case 3: return go(std::integral_constant<int, 3>{});
+      case 4: return go(std::integral_constant<int, 4>{});
+      default: return hipErrorInvalidValue;
+    }
   } else {
     if (xm) return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_reduce, s, q);
     return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 0>>(blocks, kThreads, p.lds_reduce, s, q);

@@ -255,6 +255,9 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int n = 0; n < R; ++n) acc[cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // (read per K-step: one K-step ahead of its MFMAs)
+    bf16x8 uq[kOnce ? 1 : 2][NP][R];
+    if constexpr (!kOnce) get_u8<R, BF16>(ub, 0, ln.l, uq[0]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       bf16x8 uk[NP][R];
@@ -264,7 +267,11 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
 #pragma unroll
           for (int n = 0; n < R; ++n) uk[pl][n] = ua[s][pl][n];
       } else {
-        get_u8<R, BF16>(ub, s, ln.l, uk);
+        if (s + 1 < KS) get_u8<R, BF16>(ub, s + 1, ln.l, uq[(s + 1) & 1]);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+          for (int n = 0; n < R; ++n) uk[pl][n] = uq[s & 1][pl][n];
       }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -457,12 +464,20 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
         for (int n = 0; n < R; ++n) yacc[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const lds_byte* xr = xlds + (i & 1) * xt;
       if (w < HT) {   // wave-uniform: waves past the h-tiles read nothing out
+        // x fragments read kAhead K-steps ahead of their MFMAs (left alone,
+        // the scheduler puts each read next to its use and waits there)
+        constexpr int kAhead = NP == 2 ? 1 : 3;
+        bf16x8 xf[K2][NP][R];
+#pragma unroll
+        for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
+        __builtin_amdgcn_sched_group_barrier(0x100, (kAhead < K2 ? kAhead : K2) * NP * R, 0);
 #pragma unroll
         for (int s = 0; s < K2; ++s) {
-          bf16x8 xf[NP][R];
-          get_x<R, NP>(xr, K2, s, ln.l, xf);
+          if (s + kAhead < K2) get_x<R, NP>(xr, K2, s + kAhead, ln.l, xf[s + kAhead]);
 #pragma unroll
-          for (int e = 0; e < ET; ++e) mfma_read<R, NP>(cw[e][s], xf, yacc[e]);
+          for (int e = 0; e < ET; ++e) mfma_read<R, NP>(cw[e][s], xf[s], yacc[e]);
+          if (s + kAhead < K2) __builtin_amdgcn_sched_group_barrier(0x100, NP * R, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, ET * R * (NP == 2 ? 3 : 1), 0);
         }
       }
       // y of chunk i-1 beside those MFMAs
