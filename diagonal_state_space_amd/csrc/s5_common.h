@@ -59,12 +59,13 @@ __device__ __forceinline__ float expm1_neg(float r, float er) {
 // With s, c = sin, cos(w/2) and r = Re(lam) dt:
 //   abar - 1 = ((e^r - 1)(1 - 2 s^2) - 2 s^2,  e^r 2 s c)
 // has no cancellation (for Re(lam) <= 0 the two terms of the real part have
-// the same sign while cos w >= 0, and otherwise the real part is below -1),
-// and gain = (abar - 1)/lam keeps the relative accuracy of abar - 1 down to
-// the smallest |lam dt|. At lam = 0 the packing stores
-// 1/lam as 0 and fz = 1, so that gain = dt there (the removable singularity).
-__device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float fz, float dt, cf& abar, cf& gain) {
-  const float r = lam.re * dt;
+// the same sign while cos w >= 0, and otherwise the real part is below -1).
+// Returned with abar: lg = lam * gain = abar - 1, or dt where fz = 1
+// (lambda = 0, the removable singularity of gain = (abar - 1)/lam, where
+// abar - 1 = 0). The fused kernels divide B~ by lambda once when packing
+// it, so that the drive gives (B~/lam) u and the step needs no division.
+__device__ __forceinline__ void zoh_step_lg(float lam_re, float hrev, float fz, float dt, cf& abar, cf& lg) {
+  const float r = lam_re * dt;
   const float th = hrev * dt;
   const float f = th - rintf(th);                 // exact: whole turns dropped, |f| <= 1/2
   const float s = __builtin_amdgcn_sinf(f);       // hardware sine and cosine of 2 pi f
@@ -73,10 +74,17 @@ __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float f
   const float em1 = expm1_neg(r, er);
   const float two_s2 = 2.0f * s * s;
   const float cosw = 1.0f - two_s2;
-  const float sinw = 2.0f * s * c;
-  const cf am1 = {fmaf(em1, cosw, -two_s2), er * sinw};
+  const cf am1 = {fmaf(em1, cosw, -two_s2), er * (2.0f * s * c)};
   abar = {1.0f + am1.re, am1.im};
-  gain = {fmaf(am1.re, inv_lam.re, fmaf(-am1.im, inv_lam.im, fz * dt)), fmaf(am1.re, inv_lam.im, am1.im * inv_lam.re)};
+  lg = {fmaf(fz, dt, am1.re), am1.im};
+}
+
+// The gain itself, (abar - 1)/lam (dt at lambda = 0: inv_lam = 0, fz = 1),
+// for a drive by B~ u (the single-step kernel).
+__device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float fz, float dt, cf& abar, cf& gain) {
+  cf lg;
+  zoh_step_lg(lam.re, hrev, fz, dt, abar, lg);
+  gain = {fmaf(lg.re, inv_lam.re, fmaf(-lg.im, inv_lam.im, fz * dt)), fmaf(lg.re, inv_lam.im, lg.im * inv_lam.re)};
 }
 
 // Bilinear map of one mode for a per-step interval dt >= 0, z = lam dt:
@@ -91,20 +99,22 @@ __device__ __forceinline__ void bilinear_step(cf lam, float dt, cf& abar, cf& ga
   gain = {dt * w.re, dt * w.im};
 }
 
-// per-mode constants of the per-step discretisation: lambda, 1/lambda (0 for
-// lambda = 0), the half-angle turns per unit interval Im(lambda)/(4 pi), and
-// fz = 1 for lambda = 0 (else 0)
+// per-mode constants of the per-step discretisation: lambda, the half-angle
+// turns per unit interval Im(lambda)/(4 pi), and fz = 1 for lambda = 0 (else 0)
 struct StepMode {
-  cf lam, inv;
+  cf lam;
   float hrev, fz;
 };
 
-// one per-step discretisation: bilinear when `bil`, else zero-order hold
+// One per-step discretisation of the fused kernels: abar, and the factor for
+// the drive's sum. Zero-order hold: lam * gain (the drive was packed from
+// B~/lam, see zoh_step_lg); bilinear (when `bil`): the gain itself (packed
+// from B~).
 __device__ __forceinline__ void disc_step(bool bil, const StepMode& m, float dt, cf& abar, cf& gain) {
   if (bil) {
     bilinear_step(m.lam, dt, abar, gain);
   } else {
-    zoh_step(m.lam, m.inv, m.hrev, m.fz, dt, abar, gain);
+    zoh_step_lg(m.lam.re, m.hrev, m.fz, dt, abar, gain);
   }
 }
 

@@ -544,30 +544,25 @@ __device__ __forceinline__ float f4_at(const float4& v, int r) {
 // load there would wait (in-order vmcnt) behind the asynchronous u copies.
 struct ModeTable {
   S5_LDS pf2* ab;      // abar (time-invariant) or lambda (time-varying)   [Ppad]
-  S5_LDS pf2* il;      // 1/lambda (time-varying)                          [Ppad]
   S5_LDS float* hr;    // hrev (time-varying)                              [Ppad]
   S5_LDS float* fz;    // 1 for lambda = 0 (time-varying)                  [Ppad]
   S5_LDS float* d;     // D, zero past H (pass 2)                          [Hpad]
 
   // the per-step discretisation's constants of mode p (time-varying)
-  __device__ __forceinline__ StepMode step_mode(int p) const {
-    return {ld_pf2(ab + p), ld_pf2(il + p), hr[p], fz[p]};
-  }
+  __device__ __forceinline__ StepMode step_mode(int p) const { return {ld_pf2(ab + p), hr[p], fz[p]}; }
 };
 
 template <bool TV>
 __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_byte* base, bool with_d) {
   ModeTable mt;
   mt.ab = reinterpret_cast<S5_LDS pf2*>(base);
-  mt.il = mt.ab + q.Ppad;
-  mt.hr = reinterpret_cast<S5_LDS float*>(TV ? mt.il + q.Ppad : mt.ab + q.Ppad);
+  mt.hr = reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
   mt.fz = mt.hr + (TV ? q.Ppad : 0);
   mt.d = TV ? mt.fz + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
   for (int p = threadIdx.x; p < q.Ppad; p += kThreads) {
     const ModeParams& mq = q.modes[p];
     if constexpr (TV) {
       st_pf2(mt.ab + p, mq.lam.x, mq.lam.y);
-      st_pf2(mt.il + p, mq.inv_lam.x, mq.inv_lam.y);
       mt.hr[p] = mq.hrev;
       mt.fz[p] = mq.fz;
     } else {
@@ -1415,7 +1410,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
         sm = mt.step_mode(pm);
       } else {
         const ModeParams& mq = q.modes[pm];
-        sm = {{mq.lam.x, mq.lam.y}, {mq.inv_lam.x, mq.inv_lam.y}, mq.hrev, mq.fz};
+        sm = {{mq.lam.x, mq.lam.y}, mq.hrev, mq.fz};
       }
 #pragma unroll
       for (int n = 0; n < R; ++n) {

@@ -13,6 +13,10 @@ namespace {
 
 using f64::zd;
 
+// lambda treated as 0 by the per-step discretisation (there the gain is the
+// interval; dividing B~ by it would overflow)
+__device__ __forceinline__ bool near_zero(zd lam) { return lam.re * lam.re + lam.im * lam.im < 1e-60; }
+
 __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int KS = q.Hpad / 32;
   const int K2 = 2 * q.Ppad / 32;
@@ -36,6 +40,8 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         if (!q.time_varying) {
           zd abar;
           f64::discretize(lam, exp(static_cast<double>(q.log_delta[p])), q.bilinear, abar, g);
+        } else if (!q.bilinear && !near_zero(lam)) {
+          g = f64::zdiv({1.0, 0.0}, lam);   // per-step zero-order hold: the drive gives (B~/lambda) u
         } else {
           g = {1.0, 0.0};
         }
@@ -80,10 +86,7 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
         mp.lam = make_float2(q.lam[p].x, q.lam[p].y);
-        const bool zero = lam.re == 0.0 && lam.im == 0.0;
-        const zd il = zero ? zd{0.0, 0.0} : f64::zdiv({1.0, 0.0}, lam);
-        mp.inv_lam = make_float2(static_cast<float>(il.re), static_cast<float>(il.im));
-        mp.fz = zero ? 1.0f : 0.0f;
+        mp.fz = near_zero(lam) ? 1.0f : 0.0f;
         mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
         if (!q.time_varying) {
           const double dt = exp(static_cast<double>(q.log_delta[p]));
@@ -102,8 +105,6 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
           mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));
           mp.aseg = make_float2(static_cast<float>(as.re), static_cast<float>(as.im));
         }
-      } else {
-        mp.inv_lam = make_float2(0.0f, 0.0f);
       }
       q.modes[p] = mp;
     }

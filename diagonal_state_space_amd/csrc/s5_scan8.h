@@ -424,8 +424,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
 
     // Iteration i: readout of chunk i (x tile i & 1), y of chunk i-1 (its
     // sums from the previous iteration, u tile i-1), drive and scan of chunk
-    // i+1 (u tile i+1 -> x tile (i+1) & 1), u tile i+2 staged. The drive of
-    // the chunk after the last reads a tile of zeros (harmless, unread).
+    // i+1 (u tile i+1 -> x tile (i+1) & 1), u tile i+2 staged.
     f32x4 yprev[ET][R];
     YOld<BF16> yold_prev, yold_cur;
 #pragma unroll
@@ -482,9 +481,11 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       }
       // y of chunk i-1 beside those MFMAs
       if (i > 0) epilogue_of(i - 1, yprev, yold_prev);
-      // drive and scan of chunk i+1
-      drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
-                                           xlds + ((i + 1) & 1) * xt);
+      // drive and scan of chunk i+1 (none after the last chunk)
+      if (i + 1 < q.nck) {
+        drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
+                                             xlds + ((i + 1) & 1) * xt);
+      }
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the chunk's work
       stash8<R, BF16, NB>(q, ust, lds + ((i + 2) & 3) * ut, w, ln.l);
 #pragma unroll

@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(kStepThreads) k_step(StepArgs q) {
       if (q.bilinear) {
         bilinear_step(lam, dt, a, g);
       } else {
-        const bool zero = lam.re == 0.0f && lam.im == 0.0f;
+        const bool zero = static_cast<double>(lam.re) * lam.re + static_cast<double>(lam.im) * lam.im < 1e-60;
         const zd il = zero ? zd{0.0, 0.0} : f64::zdiv({1.0, 0.0}, {lam.re, lam.im});
         const float hrev = static_cast<float>(static_cast<double>(lam.im) / (4.0 * 3.14159265358979323846));
         zoh_step(lam, {static_cast<float>(il.re), static_cast<float>(il.im)}, hrev, zero ? 1.0f : 0.0f, dt, a, g);
