@@ -47,8 +47,8 @@ __device__ __forceinline__ float expm1_neg(float r, float er) {
   return r > -0.125f ? series : er - 1.0f;
 }
 
-// Zero-order hold of one mode for a per-step interval dt >= 0 (the
-// time-varying path), with the half-angle taken in turns:
+// abar - 1 of the zero-order hold of one mode for a per-step interval dt >= 0
+// (the time-varying path), with the half-angle taken in turns:
 //   w/2 = Im(lam) dt / 2 = 2 pi th,  th = dt * Im(lam)/(4 pi) = dt * hrev.
 // Whole turns of th drop out exactly (th - rint(th), any finite th), so the
 // angle's only error is the rounding of th itself, the same as rounding w;
@@ -60,11 +60,7 @@ __device__ __forceinline__ float expm1_neg(float r, float er) {
 //   abar - 1 = ((e^r - 1)(1 - 2 s^2) - 2 s^2,  e^r 2 s c)
 // has no cancellation (for Re(lam) <= 0 the two terms of the real part have
 // the same sign while cos w >= 0, and otherwise the real part is below -1).
-// Returned with abar: lg = lam * gain = abar - 1, or dt where fz = 1
-// (lambda = 0, the removable singularity of gain = (abar - 1)/lam, where
-// abar - 1 = 0). The fused kernels divide B~ by lambda once when packing
-// it, so that the drive gives (B~/lam) u and the step needs no division.
-__device__ __forceinline__ void zoh_step_lg(float lam_re, float hrev, float fz, float dt, cf& abar, cf& lg) {
+__device__ __forceinline__ cf zoh_am1(float lam_re, float hrev, float dt) {
   const float r = lam_re * dt;
   const float th = hrev * dt;
   const float f = th - rintf(th);                 // exact: whole turns dropped, |f| <= 1/2
@@ -73,18 +69,16 @@ __device__ __forceinline__ void zoh_step_lg(float lam_re, float hrev, float fz, 
   const float er = __expf(r);
   const float em1 = expm1_neg(r, er);
   const float two_s2 = 2.0f * s * s;
-  const float cosw = 1.0f - two_s2;
-  const cf am1 = {fmaf(em1, cosw, -two_s2), er * (2.0f * s * c)};
-  abar = {1.0f + am1.re, am1.im};
-  lg = {fmaf(fz, dt, am1.re), am1.im};
+  return {fmaf(em1, 1.0f - two_s2, -two_s2), er * (2.0f * s * c)};
 }
 
-// The gain itself, (abar - 1)/lam (dt at lambda = 0: inv_lam = 0, fz = 1),
-// for a drive by B~ u (the single-step kernel).
+// Zero-order hold for the single-step kernel, which drives with B~ u: abar and
+// the gain (abar - 1)/lam (dt at lambda = 0: inv_lam = 0, fz = 1, the
+// removable singularity, where abar - 1 = 0).
 __device__ __forceinline__ void zoh_step(cf lam, cf inv_lam, float hrev, float fz, float dt, cf& abar, cf& gain) {
-  cf lg;
-  zoh_step_lg(lam.re, hrev, fz, dt, abar, lg);
-  gain = {fmaf(lg.re, inv_lam.re, fmaf(-lg.im, inv_lam.im, fz * dt)), fmaf(lg.re, inv_lam.im, lg.im * inv_lam.re)};
+  const cf am1 = zoh_am1(lam.re, hrev, dt);
+  abar = {1.0f + am1.re, am1.im};
+  gain = {fmaf(am1.re, inv_lam.re, fmaf(-am1.im, inv_lam.im, fz * dt)), fmaf(am1.re, inv_lam.im, am1.im * inv_lam.re)};
 }
 
 // Bilinear map of one mode for a per-step interval dt >= 0, z = lam dt:
@@ -99,23 +93,36 @@ __device__ __forceinline__ void bilinear_step(cf lam, float dt, cf& abar, cf& ga
   gain = {dt * w.re, dt * w.im};
 }
 
-// per-mode constants of the per-step discretisation: lambda, the half-angle
-// turns per unit interval Im(lambda)/(4 pi), and fz = 1 for lambda = 0 (else 0)
+// abar - 1 = z w of the bilinear map (no cancellation for small z, unlike 2w - 2).
+__device__ __forceinline__ cf bilinear_am1(cf lam, float dt) {
+  const float zr = lam.re * dt, zi = lam.im * dt;
+  const float br = fmaf(-0.5f, zr, 1.0f);
+  const float bi = -0.5f * zi;
+  const float inv = 1.0f / fmaf(br, br, bi * bi);
+  return {fmaf(zr, br, zi * bi) * inv, fmaf(zi, br, -zr * bi) * inv};
+}
+
+// per-mode constants of the fused kernels' per-step discretisation: lambda
+// and the half-angle turns per unit interval Im(lambda)/(4 pi)
 struct StepMode {
   cf lam;
-  float hrev, fz;
+  float hrev;
 };
 
-// One per-step discretisation of the fused kernels: abar, and the factor for
-// the drive's sum. Zero-order hold: lam * gain (the drive was packed from
-// B~/lam, see zoh_step_lg); bilinear (when `bil`): the gain itself (packed
-// from B~).
-__device__ __forceinline__ void disc_step(bool bil, const StepMode& m, float dt, cf& abar, cf& gain) {
-  if (bil) {
-    bilinear_step(m.lam, dt, abar, gain);
-  } else {
-    zoh_step_lg(m.lam.re, m.hrev, m.fz, dt, abar, gain);
-  }
+// The fused kernels' per-step discretisation, as am1 = abar - 1. Both maps
+// have gain = (abar - 1)/lambda (zero-order hold by definition; bilinear:
+// abar - 1 = z w and gain = dt w), so with the drive packed from B~/lambda,
+// bu = (B~/lambda) u, one step is
+//   x <- abar x + gain B~u = x + am1 (x + bu)           (step_am1)
+// and needs neither abar nor the gain. lambda = 0 is packed as a tiny
+// negative real lambda, for which x + am1 (x + bu) is x + dt B~u to float
+// precision.
+__device__ __forceinline__ cf disc_am1(bool bil, const StepMode& m, float dt) {
+  return bil ? bilinear_am1(m.lam, dt) : zoh_am1(m.lam.re, m.hrev, dt);
+}
+
+__device__ __forceinline__ cf step_am1(cf am1, cf x, cf bu) {
+  return cfma(am1, {x.re + bu.re, x.im + bu.im}, x);
 }
 
 // ---- GELU epilogue forms -------------------------------------------------------

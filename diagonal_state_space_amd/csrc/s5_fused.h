@@ -18,10 +18,10 @@ __host__ __device__ constexpr size_t u_tile_bytes(int KS, int R, bool bf16) {
 __host__ __device__ constexpr size_t x_tile_bytes(int K2, int R, bool bf16) {
   return static_cast<size_t>(K2) * R * (bf16 ? 1 : 2) * kBlock;
 }
-// LDS bytes of the per-mode constants (abar, or lambda, hrev and fz for the
-// time-varying path) and optionally D.
+// LDS bytes of the per-mode constants (abar, or lambda and hrev for the
+// time-varying path) and optionally D (16-byte aligned: Ppad is a multiple of 64).
 __host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool tv, bool with_d) {
-  return static_cast<size_t>(Ppad) * (tv ? 16 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
+  return static_cast<size_t>(Ppad) * (tv ? 12 : 8) + (with_d ? static_cast<size_t>(Hpad) * 4 : 0);
 }
 // chunks between two barriers of the eight-wave pass 1 (u tiles of two such
 // groups in LDS; the chunk count is padded to a multiple of it). Smaller for
@@ -31,11 +31,10 @@ __host__ __device__ constexpr int reduce_group(bool bf16, bool tv) { return tv ?
 
 // Per-mode constants written by the packing kernel.
 struct ModeParams {
-  float2 lam;      // continuous eigenvalue
+  float2 lam;      // continuous eigenvalue (time-varying: -1e-20 where |lambda| < 1e-20)
   float2 abar;     // exp(lambda Delta)                         (time-invariant)
   float2 aseg;     // exp(Lseg lambda Delta): one whole stream   (time-invariant)
-  float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval
-  float fz;        // 1 for lambda = 0 (|lambda| < 1e-30), else 0: the per-step gain is then the interval
+  float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval  (time-varying)
   float2 alast;    // abar^m, m = ((L-1) mod Lseg) + 1: the stream holding token
                    // L-1, from its first token through L-1  (time-invariant)
 };
@@ -73,8 +72,7 @@ struct FusedParams {
   int gelu;           // y = GELU(y) after the sum: 0 no, 1 exact form, 2 tanh form
   // workspace
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O):
-                      // B_bar; time-varying zero-order hold B~/lambda (B~ where fz = 1),
-                      // time-varying bilinear B~
+                      // B_bar, or B~/lambda for the time-varying path
   uint4* cpack;       // readout operand fragments (hi, then lo)
   ModeParams* modes;  // [Ppad]
   float2* sagg;       // [B*Q][16][Ppad] stream state from a zero start

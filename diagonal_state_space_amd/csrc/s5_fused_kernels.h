@@ -545,11 +545,10 @@ __device__ __forceinline__ float f4_at(const float4& v, int r) {
 struct ModeTable {
   S5_LDS pf2* ab;      // abar (time-invariant) or lambda (time-varying)   [Ppad]
   S5_LDS float* hr;    // hrev (time-varying)                              [Ppad]
-  S5_LDS float* fz;    // 1 for lambda = 0 (time-varying)                  [Ppad]
   S5_LDS float* d;     // D, zero past H (pass 2)                          [Hpad]
 
   // the per-step discretisation's constants of mode p (time-varying)
-  __device__ __forceinline__ StepMode step_mode(int p) const { return {ld_pf2(ab + p), hr[p], fz[p]}; }
+  __device__ __forceinline__ StepMode step_mode(int p) const { return {ld_pf2(ab + p), hr[p]}; }
 };
 
 template <bool TV>
@@ -557,14 +556,12 @@ __device__ __forceinline__ ModeTable fill_mode_table(const FusedParams& q, lds_b
   ModeTable mt;
   mt.ab = reinterpret_cast<S5_LDS pf2*>(base);
   mt.hr = reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
-  mt.fz = mt.hr + (TV ? q.Ppad : 0);
-  mt.d = TV ? mt.fz + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
+  mt.d = TV ? mt.hr + q.Ppad : reinterpret_cast<S5_LDS float*>(mt.ab + q.Ppad);
   for (int p = threadIdx.x; p < q.Ppad; p += kThreads) {
     const ModeParams& mq = q.modes[p];
     if constexpr (TV) {
       st_pf2(mt.ab + p, mq.lam.x, mq.lam.y);
       mt.hr[p] = mq.hrev;
-      mt.fz[p] = mq.fz;
     } else {
       st_pf2(mt.ab + p, mq.abar.x, mq.abar.y);
     }
@@ -651,10 +648,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
           cf Ar = A[jj][r];
 #pragma unroll
           for (int n = 0; n < R; ++n) {
-            cf a, gn;
-            disc_step(bil, sm, f4_at(dl[jj][n], r), a, gn);
-            x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
-            Ar = cmul(a, Ar);
+            const cf am1 = disc_am1(bil, sm, f4_at(dl[jj][n], r));
+            x = step_am1(am1, x, {acc[jj][0][n][r], acc[jj][1][n][r]});
+            Ar = cfma(am1, Ar, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pmr, x, Ar);
           }
           A[jj][r] = Ar;
@@ -844,10 +840,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
           cf Ar = A[m][r];
 #pragma unroll
           for (int n = 0; n < R; ++n) {
-            cf a, gn;
-            disc_step(bil, sm, f4_at(dl[m][n], r), a, gn);
-            x = cfma(a, x, cmul(gn, {acc[m][0][n][r], acc[m][1][n][r]}));
-            Ar = cmul(a, Ar);
+            const cf am1 = disc_am1(bil, sm, f4_at(dl[m][n], r));
+            x = step_am1(am1, x, {acc[m][0][n][r], acc[m][1][n][r]});
+            Ar = cfma(am1, Ar, Ar);
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, Ar);
           }
           A[m][r] = Ar;
@@ -1410,13 +1405,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
         sm = mt.step_mode(pm);
       } else {
         const ModeParams& mq = q.modes[pm];
-        sm = {{mq.lam.x, mq.lam.y}, mq.hrev, mq.fz};
+        sm = {{mq.lam.x, mq.lam.y}, mq.hrev};
       }
 #pragma unroll
       for (int n = 0; n < R; ++n) {
-        cf a, gn;
-        disc_step(bil, sm, f4_at(dl[jj][n], r), a, gn);
-        x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+        x = step_am1(disc_am1(bil, sm, f4_at(dl[jj][n], r)), x, {acc[jj][0][n][r], acc[jj][1][n][r]});
         acc[jj][0][n][r] = x.re;
         acc[jj][1][n][r] = x.im;
       }
@@ -1621,9 +1614,7 @@ __device__ __forceinline__ void drive_scan_tiles(bool bil, int j0, int KS, const
         const StepMode sm = mt.step_mode(pm);
 #pragma unroll
         for (int n = 0; n < R; ++n) {
-          cf a, gn;
-          disc_step(bil, sm, f4_at(dl[j][n], r), a, gn);
-          x = cfma(a, x, cmul(gn, {acc[jj][0][n][r], acc[jj][1][n][r]}));
+          x = step_am1(disc_am1(bil, sm, f4_at(dl[j][n], r)), x, {acc[jj][0][n][r], acc[jj][1][n][r]});
           acc[jj][0][n][r] = x.re;
           acc[jj][1][n][r] = x.im;
         }

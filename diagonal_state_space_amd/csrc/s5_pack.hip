@@ -13,9 +13,14 @@ namespace {
 
 using f64::zd;
 
-// lambda treated as 0 by the per-step discretisation (there the gain is the
-// interval; dividing B~ by it would overflow)
-__device__ __forceinline__ bool near_zero(zd lam) { return lam.re * lam.re + lam.im * lam.im < 1e-60; }
+// lambda of the per-step discretisation: a tiny negative real value in place
+// of |lambda| < 1e-20, so that B~/lambda stays finite (the kernels step with
+// x + (abar - 1)(x + (B~/lambda) u), which for such lambda is x + dt B~u to
+// float precision, the lambda = 0 step)
+__device__ __forceinline__ zd step_lambda(float2 l) {
+  const zd lam = {l.x, l.y};
+  return lam.re * lam.re + lam.im * lam.im < 1e-40 ? zd{-1e-20, 0.0} : lam;
+}
 
 __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int KS = q.Hpad / 32;
@@ -36,14 +41,12 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       float v[8];
       zd g = {0.0, 0.0};
       if (p < q.P) {
-        const zd lam = {q.lam[p].x, q.lam[p].y};
         if (!q.time_varying) {
           zd abar;
-          f64::discretize(lam, exp(static_cast<double>(q.log_delta[p])), q.bilinear, abar, g);
-        } else if (!q.bilinear && !near_zero(lam)) {
-          g = f64::zdiv({1.0, 0.0}, lam);   // per-step zero-order hold: the drive gives (B~/lambda) u
+          f64::discretize({q.lam[p].x, q.lam[p].y}, exp(static_cast<double>(q.log_delta[p])), q.bilinear,
+                          abar, g);
         } else {
-          g = {1.0, 0.0};
+          g = f64::zdiv({1.0, 0.0}, step_lambda(q.lam[p]));   // per-step: the drive gives (B~/lambda) u
         }
       }
 #pragma unroll
@@ -86,9 +89,11 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
       if (p < q.P) {
         const zd lam = {q.lam[p].x, q.lam[p].y};
         mp.lam = make_float2(q.lam[p].x, q.lam[p].y);
-        mp.fz = near_zero(lam) ? 1.0f : 0.0f;
-        mp.hrev = static_cast<float>(lam.im / (4.0 * 3.14159265358979323846));
-        if (!q.time_varying) {
+        if (q.time_varying) {
+          const zd ls = step_lambda(q.lam[p]);
+          mp.lam = make_float2(static_cast<float>(ls.re), static_cast<float>(ls.im));
+          mp.hrev = static_cast<float>(ls.im / (4.0 * 3.14159265358979323846));
+        } else {
           const double dt = exp(static_cast<double>(q.log_delta[p]));
           // log of Lambda_bar: z itself for zero-order hold
           zd z = {lam.re * dt, lam.im * dt};

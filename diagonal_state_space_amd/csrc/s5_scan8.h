@@ -292,9 +292,7 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
         const StepMode sm = mtab.step_mode(pm);
 #pragma unroll
         for (int n = 0; n < R; ++n) {
-          cf a, gn;
-          disc_step(bil, sm, f4_at(dl[m][n], r), a, gn);
-          x = cfma(a, x, cmul(gn, {acc[0][n][r], acc[1][n][r]}));
+          x = step_am1(disc_am1(bil, sm, f4_at(dl[m][n], r)), x, {acc[0][n][r], acc[1][n][r]});
           acc[0][n][r] = x.re;
           acc[1][n][r] = x.im;
         }
