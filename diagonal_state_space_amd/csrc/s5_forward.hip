@@ -19,7 +19,11 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   // SIMD, 256 registers each) up to MPW NP = 4, and with the time-varying step
   // (its interval registers and discretisation beside the weights) up to two
   // mode tiles per wave
-  const bool keep = KS <= 4 && MPW * NP <= 4;
+  // pass 1's eight waves hold M8 = ceil(4 MPW / 8) mode tiles each: at most
+  // 128 registers of weights (M8 KS NP <= 16), so time-invariant shapes up to
+  // H = 256 (KS = 8) keep them; the time-varying step up to H = 128
+  const int M8 = (4 * MPW + 7) / 8;
+  const bool keep = MPW * NP <= 4 && M8 * KS * NP <= 16 && (KS <= 4 || !time_varying);
   const bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
   p.R = 0;
   // bf16 instances are compiled for R = 2 (which always fits); float32 ones
@@ -28,7 +32,7 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
   const int cand[2] = {2, 1};
   for (int R : cand) {
     if (bf16_io && R != 2) continue;
-    const bool k = keep && R == 2;
+    bool k = keep && R == 2;
     const bool ks = keep_scan && R == 2;
     const size_t lr = 2 * fused::u_tile_bytes(KS, R, bf16_io) +
                       (time_varying ? fused::mode_table_bytes(Ppad, Hpad, true, false) : 0);
@@ -36,9 +40,9 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
                       (ks ? fused::mode_table_bytes(Ppad, Hpad, time_varying, true) : 0);
     if (ls > lds_max || lr > lds_max) continue;
     // eight-wave pass 1: two groups of u tiles and the mode table
-    const size_t lrw = 2 * fused::reduce_group(bf16_io, time_varying) * fused::u_tile_bytes(KS, R, bf16_io) +
+    const size_t lrw = 2 * fused::reduce_group(bf16_io, time_varying, KS) * fused::u_tile_bytes(KS, R, bf16_io) +
                        fused::mode_table_bytes(Ppad, Hpad, time_varying, false);
-    if (k && lrw > lds_max) continue;
+    if (k && lrw > lds_max) k = false;   // the four-wave pass 1 instead
     p.R = R;
     p.keep = k;
     p.keep_scan = ks;
@@ -58,7 +62,7 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
       p.ks = KS;
       if (p.scan8) ls = l8;
     }
-    p.group = k ? fused::reduce_group(bf16_io, time_varying) : 1;
+    p.group = k ? fused::reduce_group(bf16_io, time_varying, KS) : 1;
     p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;
     p.lds_scan = ls;

@@ -25,8 +25,11 @@ __host__ __device__ constexpr size_t mode_table_bytes(int Ppad, int Hpad, bool t
 }
 // chunks between two barriers of the eight-wave pass 1 (u tiles of two such
 // groups in LDS; the chunk count is padded to a multiple of it). Smaller for
-// the time-varying step, whose per-token constants leave fewer registers.
-__host__ __device__ constexpr int reduce_group(bool bf16, bool tv) { return tv ? (bf16 ? 1 : 2) : (bf16 ? 4 : 2); }
+// the time-varying step, whose per-token constants leave fewer registers, and
+// for more than four drive K-steps, whose weights do.
+__host__ __device__ constexpr int reduce_group(bool bf16, bool tv, int ks) {
+  return tv ? (bf16 ? 1 : 2) : (bf16 && ks <= 4 ? 4 : 2);
+}
 }  // namespace fused
 
 // Per-mode constants written by the packing kernel.

@@ -722,7 +722,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr int NT = 4 * MPW;                 // mode tiles
   constexpr int M8 = (NT + NW8 - 1) / NW8;    // tiles per wave, at most
   extern __shared__ __align__(16) unsigned char smem[];
-  if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R || q.nck % reduce_group(BF16, TV) != 0) return;   // dispatch mismatch
+  if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R || q.nck % reduce_group(BF16, TV, KS) != 0) return;   // dispatch mismatch
   Lane ln = lane_ids();
   ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW8 - 1);   // 0..7
   const int bq = blockIdx.x;
@@ -734,7 +734,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   const int cap_chunk = EXT && q.xlast != nullptr && qq == lt.qq ? lt.i : -1;   // chunk holding token L-1
   constexpr int ut = static_cast<int>(u_tile_bytes(KS, R, BF16));
   lds_byte* lds = (lds_byte*)smem;
-  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16, TV) * ut, false);
+  const ModeTable mt = fill_mode_table<TV>(q, lds + 2 * reduce_group(BF16, TV, KS) * ut, false);
 
   // B_bar fragments of the wave's tiles, all K-steps: [s][m][cc][pl]
   bf16x8 bw[KS][M8][2][NP];
@@ -765,7 +765,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
     }
 
   constexpr int NB = (KS * R * (BF16 ? 1 : 2) + NW8 - 1) / NW8;   // u staging blocks per wave
-  constexpr int G = reduce_group(BF16, TV);   // chunks per barrier (nck is a multiple of G)
+  constexpr int G = reduce_group(BF16, TV, KS);   // chunks per barrier (nck is a multiple of G)
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
 
   // Delta of chunk i (time-varying)
@@ -1859,11 +1859,26 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
       if (xm) return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
       return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
     };
-    switch (p.ks) {   // the drive's K-steps (H <= 128)
+    // the drive's K-steps: H <= 128, and time-invariant H <= 256 where the
+    // weights fit 128 registers (M8 KS NP <= 16)
+    constexpr int M8 = (4 * MPW + 2 * kWaves - 1) / (2 * kWaves);
+    constexpr int kMaxKS = TV ? 4 : 16 / (M8 * (BF16 ? 1 : 2));
+    auto big = [&](auto ks_c) {
+      if constexpr (decltype(ks_c)::value <= kMaxKS) {
+        return go(ks_c);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    };
+    switch (p.ks) {
       case 1: return go(std::integral_constant<int, 1>{});
       case 2: return go(std::integral_constant<int, 2>{});
       case 3: return go(std::integral_constant<int, 3>{});
       case 4: return go(std::integral_constant<int, 4>{});
+      case 5: return big(std::integral_constant<int, 5>{});
+      case 6: return big(std::integral_constant<int, 6>{});
+      case 7: return big(std::integral_constant<int, 7>{});
+      case 8: return big(std::integral_constant<int, 8>{});
       default: return hipErrorInvalidValue;
     }
   } else {
