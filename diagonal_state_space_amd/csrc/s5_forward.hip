@@ -51,14 +51,19 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
     // u), two x tiles and the mode table in LDS
     {
       const int NT = 4 * MPW, MT = (NT + 7) / 8, HT = 2 * KS, ET = (HT + 7) / 8;
-      const int wregs = 4 * (KS * MT * 2 * NP + ET * NT * NP);
+      // time-invariant bf16 with more than four drive K-steps (H > 128): C'
+      // in registers, B_bar streamed from L2
+      const bool sb = !time_varying && bf16_io && KS > 4 && KS <= 8;
+      const int wregs = 4 * ((sb ? 0 : KS * MT * 2 * NP) + ET * NT * NP);
       const size_t l8 = 4 * static_cast<size_t>(KS) * R * (bf16_io ? 1 : 3) * fused::kBlock +
                         2 * fused::x_tile_bytes(K2, R, bf16_io) + fused::mode_table_bytes(Ppad, Hpad, time_varying, true);
       // taken for the time-varying step, whose per-step vector work the
-      // symmetric split spreads over both waves of each SIMD; the
-      // time-invariant pass 2 is matrix-core bound and runs faster with its
-      // roles specialized
-      p.scan8 = ks && time_varying && R == 2 && KS <= 4 && MPW <= (bf16_io ? 4 : 2) && wregs <= 128 && l8 <= lds_max;
+      // symmetric split spreads over both waves of each SIMD, and where the
+      // wave-specialized kernel's weights do not fit (H > 128); the
+      // time-invariant pass 2 with H <= 128 is matrix-core bound and runs
+      // faster with its roles specialized
+      const bool tv8 = ks && time_varying && KS <= 4 && MPW <= (bf16_io ? 4 : 2);
+      p.scan8 = (tv8 || sb) && R == 2 && wregs <= 128 && l8 <= lds_max;
       p.ks = KS;
       if (p.scan8) ls = l8;
     }

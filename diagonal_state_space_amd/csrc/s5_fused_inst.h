@@ -36,17 +36,32 @@ hipError_t scan8_ks(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
 
 template <int MPW>
 hipError_t scan8(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
-  // the plan takes it for the time-varying step with at most two mode tiles per wave
-  if constexpr (MPW > kKeepMaxMPW || !kTV || MPW > 2) {
+  // the plan takes it for the time-varying step with at most two mode tiles
+  // per wave, and for time-invariant bf16 I/O with 5..8 drive K-steps
+  if constexpr (MPW > kKeepMaxMPW) {
     return hipErrorInvalidValue;
-  } else {
+  } else if constexpr (kTV) {
+    if constexpr (MPW > 2) {
+      return hipErrorInvalidValue;
+    } else {
+      switch (p.ks) {
+        case 1: return scan8_ks<MPW, 1>(q, p, s);
+        case 2: return scan8_ks<MPW, 2>(q, p, s);
+        case 3: return scan8_ks<MPW, 3>(q, p, s);
+        case 4: return scan8_ks<MPW, 4>(q, p, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  } else if constexpr (kBF16) {
     switch (p.ks) {
-      case 1: return scan8_ks<MPW, 1>(q, p, s);
-      case 2: return scan8_ks<MPW, 2>(q, p, s);
-      case 3: return scan8_ks<MPW, 3>(q, p, s);
-      case 4: return scan8_ks<MPW, 4>(q, p, s);
+      case 5: return scan8_ks<MPW, 5>(q, p, s);
+      case 6: return scan8_ks<MPW, 6>(q, p, s);
+      case 7: return scan8_ks<MPW, 7>(q, p, s);
+      case 8: return scan8_ks<MPW, 8>(q, p, s);
       default: return hipErrorInvalidValue;
     }
+  } else {
+    return hipErrorInvalidValue;
   }
 }
 
@@ -78,7 +93,7 @@ hipError_t by_mpw(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
 template <bool REDUCE>
 hipError_t dispatch(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   if (q.bf16_io != kBF16 || q.time_varying != kTV) return hipErrorInvalidValue;
-  const bool keep = REDUCE ? p.keep : p.keep_scan;
+  const bool keep = REDUCE ? p.keep : (p.keep_scan || p.scan8);
   if (p.R == 2) return keep ? by_mpw<REDUCE, 2, true>(q, p, s) : by_mpw<REDUCE, 2, false>(q, p, s);
   if constexpr (!kBF16) {
     if (p.R == 1 && !keep) return by_mpw<REDUCE, 1, false>(q, p, s);

@@ -230,6 +230,52 @@ __device__ __forceinline__ void write_final_state8(const FusedParams& q, int b, 
     }
 }
 
+// Scan of mode tile j (slot m) of one chunk from its drive sums acc, then its
+// x tile fragments (bf16 hi [+ lo]) into LDS.
+template <int MT, int NT, int R, bool TV, bool BF16>
+__device__ __forceinline__ void scan_tile8(bool bil, int j, int m, f32x4 (&acc)[2][R], const ModeTable& mtab,
+                                           const Lane& ln, const float4 (&dl)[TV ? MT : 1][TV ? R : 1],
+                                           cf (&st)[MT][4], lds_byte* xb) {
+  constexpr int K2 = NT;   // readout K-steps = mode tiles
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pm = 16 * j + 4 * ln.g + r;
+    cf x = st[m][r];
+    if constexpr (TV) {
+      const StepMode sm = mtab.step_mode(pm);
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        x = step_am1(disc_am1(bil, sm, f4_at(dl[m][n], r)), x, {acc[0][n][r], acc[1][n][r]});
+        acc[0][n][r] = x.re;
+        acc[1][n][r] = x.im;
+      }
+    } else {
+      const cf ab = ld_pf2(mtab.ab + pm);
+#pragma unroll
+      for (int n = 0; n < R; ++n) {
+        x = cfma(ab, x, {acc[0][n][r], acc[1][n][r]});
+        acc[0][n][r] = x.re;
+        acc[1][n][r] = x.im;
+      }
+    }
+    st[m][r] = x;
+  }
+#pragma unroll
+  for (int n = 0; n < R; ++n) {
+    float v[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[2 * r] = acc[0][n][r];
+      v[2 * r + 1] = acc[1][n][r];
+    }
+    const int blk = j * R + n;
+    uint4 hi, lo;
+    put_frag(v, &hi, BF16 ? nullptr : &lo);
+    lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
+    if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+  }
+}
+
 // Drive, scan and x tile of the wave's mode tiles for one chunk (u tile ub,
 // x tile xb). Tile by tile, so that one tile's scan runs beside the next
 // tile's MFMAs. bf16: the chunk's u fragments are read once for all tiles.
@@ -239,7 +285,6 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
                                             const float4 (&dl)[TV ? MT : 1][TV ? R : 1], cf (&st)[MT][4],
                                             lds_byte* xb) {
   constexpr int NP = BF16 ? 1 : 2;
-  constexpr int K2 = NT;   // readout K-steps = mode tiles
   constexpr bool kOnce = BF16 && MT > 1;
   bf16x8 ua[kOnce ? KS : 1][NP][R];
   if constexpr (kOnce) {
@@ -284,43 +329,73 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
           }
         }
     }
+    scan_tile8<MT, NT, R, TV, BF16>(bil, j, m, acc, mtab, ln, dl, st, xb);
+  }
+}
+
+// The drive with B_bar streamed from L2 (bf16, time-invariant, more than four
+// K-steps), tile by tile: the fragments of (tile, K-step) step t + kBW are
+// loaded at step t, the first kBW steps' come in bwin (loaded by the caller
+// ahead of the chunk); each tile's scan follows its MFMAs.
+template <int MT, int NT, int KS, int R, int kBW>
+__device__ __forceinline__ void drive_scan8_sb(int w, const uint4* bpack, const bf16x8 (&bwin)[kBW][2],
+                                               const lds_byte* ub, const ModeTable& mtab, const Lane& ln,
+                                               cf (&st)[MT][4], lds_byte* xb) {
+  constexpr int T = MT * KS;   // (tile, K-step) steps
+  bf16x8 bq[T][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pm = 16 * j + 4 * ln.g + r;
-      cf x = st[m][r];
-      if constexpr (TV) {
-        const StepMode sm = mtab.step_mode(pm);
+  for (int t = 0; t < kBW && t < T; ++t) {
+    bq[t][0] = bwin[t][0];
+    bq[t][1] = bwin[t][1];
+  }
+  const float4 dl[1][1] = {};
 #pragma unroll
-        for (int n = 0; n < R; ++n) {
-          x = step_am1(disc_am1(bil, sm, f4_at(dl[m][n], r)), x, {acc[0][n][r], acc[1][n][r]});
-          acc[0][n][r] = x.re;
-          acc[1][n][r] = x.im;
-        }
-      } else {
-        const cf ab = ld_pf2(mtab.ab + pm);
+  for (int m = 0; m < MT; ++m) {
+    const int j = w + kW8 * m;
+    if ((NT % kW8) != 0 && j >= NT) continue;   // wave-uniform
+    f32x4 acc[2][R];
 #pragma unroll
-        for (int n = 0; n < R; ++n) {
-          x = cfma(ab, x, {acc[0][n][r], acc[1][n][r]});
-          acc[0][n][r] = x.re;
-          acc[1][n][r] = x.im;
-        }
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int n = 0; n < R; ++n) acc[cc][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 uq[2][1][R];
+    get_u8<R, true>(ub, 0, ln.l, uq[0]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int t = m * KS + s;
+      const int tn = t + kBW;   // the step loaded now
+      if (tn < T) {
+        const int jn = w + kW8 * (tn / KS);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          bq[tn][cc] = jn < NT ? as_bf16x8(ldg16(bpack + ((jn * 2 + cc) * KS + tn % KS) * 64 + ln.l))
+                               : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
       }
-      st[m][r] = x;
-    }
+      if (s + 1 < KS) get_u8<R, true>(ub, s + 1, ln.l, uq[(s + 1) & 1]);
 #pragma unroll
-    for (int n = 0; n < R; ++n) {
-      float v[8];
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[2 * r] = acc[0][n][r];
-        v[2 * r + 1] = acc[1][n][r];
-      }
-      const int blk = j * R + n;
-      uint4 hi, lo;
-      put_frag(v, &hi, BF16 ? nullptr : &lo);
-      lds_st<uint4>(xb + blk * kBlock + ln.l * 16, hi);
-      if constexpr (!BF16) lds_st<uint4>(xb + (K2 * R + blk) * kBlock + ln.l * 16, lo);
+        for (int n = 0; n < R; ++n) acc[cc][n] = mfma(bq[t][cc], uq[s & 1][0][n], acc[cc][n]);
+      // each step's loads beside its MFMAs (left alone, the scheduler issues
+      // every load of the chunk first and runs out of registers)
+      if (tn < T) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      if (s + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * R, 0);
     }
+    scan_tile8<MT, NT, R, false, true>(false, j, m, acc, mtab, ln, dl, st, xb);
+  }
+}
+
+// B_bar fragments of the streamed drive's first kBW (tile, K-step) steps
+template <int MT, int NT, int KS, int kBW>
+__device__ __forceinline__ void get_bwin8(const uint4* bpack, int w, int l, bf16x8 (&b)[kBW][2]) {
+#pragma unroll
+  for (int t = 0; t < kBW; ++t) {
+    const int j = w + kW8 * (t / KS);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      b[t][cc] = t < MT * KS && j < NT ? as_bf16x8(ldg16(bpack + ((j * 2 + cc) * KS + t % KS) * 64 + l))
+                                       : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
   }
 }
 
@@ -335,6 +410,13 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   constexpr int HT = 2 * KS;                    // h-tiles
   constexpr int ET = (HT + kW8 - 1) / kW8;      // h-tiles per wave, at most
   constexpr bool kAcc = XM == 3;                // backward scan: add to y
+  // More than four drive K-steps (H > 128, bf16): the weights of both
+  // products exceed the registers; C' stays, B_bar is streamed from L2 (see
+  // drive_scan8_sb), its first kBW K-steps loaded at the top of the iteration
+  // before the drive, so that they arrive during the readout.
+  constexpr bool SB = KS > 4;
+  constexpr int kBW = 2;
+  static_assert(!SB || (BF16 && !TV), "the streamed drive is built for time-invariant bf16 I/O");
   extern __shared__ __align__(16) unsigned char smem[];
   if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R) return;   // dispatch mismatch: do nothing
   Lane ln = lane_ids();
@@ -354,23 +436,25 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   if (threadIdx.x < static_cast<unsigned>(q.Ppad)) range_carry<EXT>(q, b, qq, threadIdx.x, s_c0);
 
   // weights: B_bar fragments of the wave's mode tiles, C' fragments of its h-tiles
-  bf16x8 bw[KS][MT][2][NP];
+  bf16x8 bw[SB ? 1 : KS][MT][2][NP];
   bf16x8 cw[ET][K2][NP];
   {
     const int nb = (q.Ppad / 16) * 2 * KS * 64;
     const int nc = (q.Hpad / 16) * K2 * 64;
+    if constexpr (!SB) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+          for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int pl = 0; pl < NP; ++pl) {
-            const int j = w + kW8 * m;
-            bw[s][m][cc][pl] = j < NT ? as_bf16x8(ldg16(q.bpack + pl * nb + ((j * 2 + cc) * KS + s) * 64 + ln.l))
-                                      : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-          }
+            for (int pl = 0; pl < NP; ++pl) {
+              const int j = w + kW8 * m;
+              bw[s][m][cc][pl] = j < NT ? as_bf16x8(ldg16(q.bpack + pl * nb + ((j * 2 + cc) * KS + s) * 64 + ln.l))
+                                        : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+            }
+    }
 #pragma unroll
     for (int e = 0; e < ET; ++e)
 #pragma unroll
@@ -414,7 +498,13 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
     }
     float4 dl[TV ? MT : 1][TV ? R : 1];
     if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, 0, w, ln, dl);
-    drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
+    bf16x8 bwin[SB ? kBW : 1][2];   // streamed drive: its first steps of B_bar
+    if constexpr (SB) {
+      get_bwin8<MT, NT, KS, kBW>(q.bpack, w, ln.l, bwin);
+      drive_scan8_sb<MT, NT, KS, R, kBW>(w, q.bpack, bwin, lds, mtab, ln, st, xlds);
+    } else {
+      drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
+    }
     // Delta of chunk i+1 is loaded an iteration ahead (before that
     // iteration's u loads), so that waiting for it never waits for them
     if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, 1, w, ln, dl);
@@ -453,6 +543,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       UStage<NB> ust;
       fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, i + 2, ust);
       if constexpr (kAcc) load_y_old8<R, BF16, VEC, ET>(q, yrsrc, rmap, i, w, ln, yold_cur);
+      if constexpr (SB) {
+        if (i + 1 < q.nck) get_bwin8<MT, NT, KS, kBW>(q.bpack, w, ln.l, bwin);
+      }
       // readout of chunk i
       f32x4 yacc[ET][R];
 #pragma unroll
@@ -463,7 +556,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       if (w < HT) {   // wave-uniform: waves past the h-tiles read nothing out
         // x fragments read kAhead K-steps ahead of their MFMAs (left alone,
         // the scheduler puts each read next to its use and waits there)
-        constexpr int kAhead = NP == 2 ? 1 : 3;
+        constexpr int kAhead = NP == 2 || SB ? 1 : 3;
         bf16x8 xf[K2][NP][R];
 #pragma unroll
         for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
@@ -477,20 +570,30 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
           __builtin_amdgcn_sched_group_barrier(0x008, ET * R * (NP == 2 ? 3 : 1), 0);
         }
       }
-      // y of chunk i-1 beside those MFMAs
-      if (i > 0) epilogue_of(i - 1, yprev, yold_prev);
+      if constexpr (SB) {
+        epilogue_of(i, yacc, yold_cur);   // (no registers to keep the sums for the next iteration)
+      } else if (i > 0) {
+        epilogue_of(i - 1, yprev, yold_prev);   // y of chunk i-1 beside those MFMAs
+      }
       // drive and scan of chunk i+1 (none after the last chunk)
       if (i + 1 < q.nck) {
-        drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
+        if constexpr (SB) {
+          drive_scan8_sb<MT, NT, KS, R, kBW>(w, q.bpack, bwin, lds + ((i + 1) & 3) * ut, mtab, ln, st,
                                              xlds + ((i + 1) & 1) * xt);
+        } else {
+          drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
+                                               xlds + ((i + 1) & 1) * xt);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the chunk's work
       stash8<R, BF16, NB>(q, ust, lds + ((i + 2) & 3) * ut, w, ln.l);
+      if constexpr (!SB) {
 #pragma unroll
-      for (int e = 0; e < ET; ++e)
+        for (int e = 0; e < ET; ++e)
 #pragma unroll
-        for (int n = 0; n < R; ++n) yprev[e][n] = yacc[e][n];
-      if constexpr (kAcc) yold_prev = yold_cur;
+          for (int n = 0; n < R; ++n) yprev[e][n] = yacc[e][n];
+        if constexpr (kAcc) yold_prev = yold_cur;
+      }
       if constexpr (TV) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -499,7 +602,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       }
       lds_barrier();   // x tile i+1, u tile i+2 complete; x tile i, u tile i-2 free
     }
-    epilogue_of(q.nck - 1, yprev, yold_prev);
+    if constexpr (!SB) epilogue_of(q.nck - 1, yprev, yold_prev);
   };
   if (u_rows_vectorized(q.H, BF16)) {
     chunks(std::true_type{});
