@@ -337,8 +337,19 @@ __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[
 // K-steps), tile by tile: the fragments of (tile, K-step) step t + kBW are
 // loaded at step t, the first kBW steps' come in bwin (loaded by the caller
 // ahead of the chunk); each tile's scan follows its MFMAs.
+// B_bar fragment (tile j, component cc, K-step s) of the lane from the packed
+// operand's buffer descriptor: the lane's 16 bytes at a wave-uniform offset
+// (one scalar offset per load, where 64-bit addresses would take two vector
+// registers each)
+template <int KS>
+__device__ __forceinline__ bf16x8 ld_bfrag8(__amdgpu_buffer_rsrc_t br, int j, int cc, int s, int l) {
+  const int soff = __builtin_amdgcn_readfirstlane(((j * 2 + cc) * KS + s) * kBlock);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(br, l * 16, soff, 0);
+  return as_bf16x8(make_uint4(v[0], v[1], v[2], v[3]));
+}
+
 template <int MT, int NT, int KS, int R, int kBW>
-__device__ __forceinline__ void drive_scan8_sb(int w, const uint4* bpack, const bf16x8 (&bwin)[kBW][2],
+__device__ __forceinline__ void drive_scan8_sb(int w, __amdgpu_buffer_rsrc_t br, const bf16x8 (&bwin)[kBW][2],
                                                const lds_byte* ub, const ModeTable& mtab, const Lane& ln,
                                                cf (&st)[MT][4], lds_byte* xb) {
   constexpr int T = MT * KS;   // (tile, K-step) steps
@@ -368,8 +379,7 @@ __device__ __forceinline__ void drive_scan8_sb(int w, const uint4* bpack, const 
         const int jn = w + kW8 * (tn / KS);
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          bq[tn][cc] = jn < NT ? as_bf16x8(ldg16(bpack + ((jn * 2 + cc) * KS + tn % KS) * 64 + ln.l))
-                               : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+          bq[tn][cc] = jn < NT ? ld_bfrag8<KS>(br, jn, cc, tn % KS, ln.l) : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
       }
       if (s + 1 < KS) get_u8<R, true>(ub, s + 1, ln.l, uq[(s + 1) & 1]);
 #pragma unroll
@@ -388,14 +398,13 @@ __device__ __forceinline__ void drive_scan8_sb(int w, const uint4* bpack, const 
 
 // B_bar fragments of the streamed drive's first kBW (tile, K-step) steps
 template <int MT, int NT, int KS, int kBW>
-__device__ __forceinline__ void get_bwin8(const uint4* bpack, int w, int l, bf16x8 (&b)[kBW][2]) {
+__device__ __forceinline__ void get_bwin8(__amdgpu_buffer_rsrc_t br, int w, int l, bf16x8 (&b)[kBW][2]) {
 #pragma unroll
   for (int t = 0; t < kBW; ++t) {
     const int j = w + kW8 * (t / KS);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
-      b[t][cc] = t < MT * KS && j < NT ? as_bf16x8(ldg16(bpack + ((j * 2 + cc) * KS + t % KS) * 64 + l))
-                                       : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+      b[t][cc] = t < MT * KS && j < NT ? ld_bfrag8<KS>(br, j, cc, t % KS, l) : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
   }
 }
 
@@ -415,7 +424,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   // drive_scan8_sb), its first kBW K-steps loaded at the top of the iteration
   // before the drive, so that they arrive during the readout.
   constexpr bool SB = KS > 4;
-  constexpr int kBW = 2;
+  constexpr int kBW = MPW >= 4 ? 2 : MPW == 3 ? 3 : 4;   // (what the registers allow)
   static_assert(!SB || (BF16 && !TV), "the streamed drive is built for time-invariant bf16 I/O");
   extern __shared__ __align__(16) unsigned char smem[];
   if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R) return;   // dispatch mismatch: do nothing
@@ -470,6 +479,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   constexpr int NB = (KS * R * (BF16 ? 1 : 2) + kW8 - 1) / kW8;
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
   const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
+  // the packed B_bar (bf16: one plane of 2 Ppad/16 KS fragments) for the streamed drive
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(q.bpack), 0, (q.Ppad / 16) * 2 * KS * kBlock, kBufferWord3);
   const int HTv = (q.H + 15) >> 4;   // h-tiles holding a feature < H
   const Epi ep = epilogue<XM>(q);
 
@@ -483,9 +495,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       stash8<R, BF16, NB>(q, ust, lds + ut, w, ln.l);
     }
     lds_barrier();   // carry, mode table, u tiles 0 and 1
-    float4 dk[ET];   // D of the wave's h-tiles: features 16 ht + 4 g + 0..3
+    float4 dk[SB ? 1 : ET];   // D of the wave's h-tiles: features 16 ht + 4 g + 0..3 (streamed form: read at use)
 #pragma unroll
-    for (int e = 0; e < ET; ++e) {
+    for (int e = 0; e < (SB ? 0 : ET); ++e) {
       const int h0 = 16 * (w + kW8 * e) + 4 * ln.g;
       dk[e] = h0 < q.Hpad ? lds_ld<float4>(reinterpret_cast<const lds_byte*>(mtab.d + h0))
                           : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -500,8 +512,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
     if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, 0, w, ln, dl);
     bf16x8 bwin[SB ? kBW : 1][2];   // streamed drive: its first steps of B_bar
     if constexpr (SB) {
-      get_bwin8<MT, NT, KS, kBW>(q.bpack, w, ln.l, bwin);
-      drive_scan8_sb<MT, NT, KS, R, kBW>(w, q.bpack, bwin, lds, mtab, ln, st, xlds);
+      get_bwin8<MT, NT, KS, kBW>(brsrc, w, ln.l, bwin);
+      drive_scan8_sb<MT, NT, KS, R, kBW>(w, brsrc, bwin, lds, mtab, ln, st, xlds);
     } else {
       drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
     }
@@ -532,7 +544,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
           u_for_y8<R, BF16>(ub, ht, n, ln.t, ln.g, uv);
           f32x4 a = ya[e][n];
           if constexpr (kAcc) a += y_old_f32<BF16>(yo.v[e][n]);
-          store_y<BF16, VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, a, dk[e], uv,
+          const float4 d = SB ? lds_ld<float4>(reinterpret_cast<const lds_byte*>(mtab.d + h0)) : dk[SB ? 0 : e];
+          store_y<BF16, VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, a, d, uv,
                              Epi{false, ep.gelu, ep.tanh_form});
         }
       }
@@ -544,7 +557,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, i + 2, ust);
       if constexpr (kAcc) load_y_old8<R, BF16, VEC, ET>(q, yrsrc, rmap, i, w, ln, yold_cur);
       if constexpr (SB) {
-        if (i + 1 < q.nck) get_bwin8<MT, NT, KS, kBW>(q.bpack, w, ln.l, bwin);
+        if (i + 1 < q.nck) get_bwin8<MT, NT, KS, kBW>(brsrc, w, ln.l, bwin);
       }
       // readout of chunk i
       f32x4 yacc[ET][R];
@@ -578,7 +591,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       // drive and scan of chunk i+1 (none after the last chunk)
       if (i + 1 < q.nck) {
         if constexpr (SB) {
-          drive_scan8_sb<MT, NT, KS, R, kBW>(w, q.bpack, bwin, lds + ((i + 1) & 3) * ut, mtab, ln, st,
+          drive_scan8_sb<MT, NT, KS, R, kBW>(w, brsrc, bwin, lds + ((i + 1) & 3) * ut, mtab, ln, st,
                                              xlds + ((i + 1) & 1) * xt);
         } else {
           drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
