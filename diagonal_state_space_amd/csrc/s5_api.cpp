@@ -44,18 +44,19 @@ bool alloc_fail_hook() {
 // Scratch memory: a cache of device buffers owned by the library, reused
 // across calls. (Stream-ordered hipMallocAsync/hipFreeAsync per call would do,
 // but hipFreeAsync blocks the host until the stream has caught up, which
-// serialises the host's launches with the GPU's work.) A buffer is reused by a
-// later call on the stream that used it last (stream order makes that safe),
-// or by any call once the event recorded after its last use has completed;
-// otherwise a new buffer is allocated. Buffers are kept until the process
-// ends: at most the calls in flight on distinct streams at once, each no
-// larger than the largest scratch asked for so far.
+// serialises the host's launches with the GPU's work.) A buffer belongs to the
+// stream of its last use and is reused only by later calls on that stream,
+// where stream order makes it safe; a call on another stream takes a new
+// buffer. No event marks a buffer's last use: a marker between two calls on
+// one stream cost ~5 us of GPU time between their kernels. When all 64 slots
+// hold buffers of other streams, the call waits for the device once (after
+// which none of them is in use) and takes one over. Buffers are kept until
+// the process ends.
 struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;
   int dev = -1;
   hipStream_t last = nullptr;   // stream of the last use
-  hipEvent_t done = nullptr;    // recorded on `last` after the last use
   bool busy = false;            // taken by a call that has not enqueued its release yet
 };
 std::mutex g_scratch_mu;
@@ -71,31 +72,35 @@ hipError_t scratch_acquire(size_t bytes, hipStream_t stream, Scratch** out) {
   Scratch* pick = nullptr;
   for (int i = 0; i < g_nscratch && pick == nullptr; ++i) {
     Scratch* s = g_scratch[i];
-    if (s->busy || s->dev != dev || s->bytes < bytes) continue;
-    if (s->last == stream || hipEventQuery(s->done) == hipSuccess) pick = s;
+    if (!s->busy && s->dev == dev && s->bytes >= bytes && s->last == stream) pick = s;
   }
-  if (pick == nullptr) {
-    if (g_nscratch == 64) {
-      // full: drop an idle buffer (its last use has finished) to make room
-      int victim = -1;
-      for (int i = 0; i < g_nscratch && victim < 0; ++i)
-        if (!g_scratch[i]->busy && hipEventQuery(g_scratch[i]->done) == hipSuccess) victim = i;
+  if (pick == nullptr && g_nscratch == 64) {
+    // full: once the device is idle, no buffer that is not taken is in use
+    // (a buffer released before this point had its work enqueued before it)
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    int victim = -1;
+    for (int i = 0; i < g_nscratch && pick == nullptr; ++i) {
+      Scratch* s = g_scratch[i];
+      if (s->busy || s->dev != dev) continue;
+      if (s->bytes >= bytes) {
+        pick = s;
+      } else if (victim < 0) {
+        victim = i;
+      }
+    }
+    if (pick == nullptr) {
       if (victim < 0) return hipErrorOutOfMemory;
       Scratch* v = g_scratch[victim];
       (void)hipFree(v->ptr);
-      (void)hipEventDestroy(v->done);
       delete v;
       g_scratch[victim] = g_scratch[--g_nscratch];
     }
+  }
+  if (pick == nullptr) {
     Scratch* s = new Scratch();
     e = hipMalloc(&s->ptr, bytes);
     if (e != hipSuccess) {
-      delete s;
-      return e;
-    }
-    e = hipEventCreateWithFlags(&s->done, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      (void)hipFree(s->ptr);
       delete s;
       return e;
     }
@@ -109,13 +114,12 @@ hipError_t scratch_acquire(size_t bytes, hipStream_t stream, Scratch** out) {
   return hipSuccess;
 }
 
-// The call's work on `stream` is enqueued: the buffer is free once it is done.
+// The call's work on `stream` is enqueued: the buffer belongs to `stream` now.
 hipError_t scratch_release(Scratch* s, hipStream_t stream) {
-  const hipError_t e = hipEventRecord(s->done, stream);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   s->last = stream;
   s->busy = false;
-  return e;
+  return hipSuccess;
 }
 
 constexpr int kMaxDevices = 64;

@@ -30,11 +30,14 @@
  * - Every call is asynchronous on `stream` (NULL = the null stream) and does
  *   not synchronise the host (except when it allocates scratch, below).
  *   Internal scratch memory comes from buffers the library keeps for reuse:
- *   a later call on the same stream, or any call once the earlier call's
- *   work has finished, reuses a buffer; otherwise hipMalloc adds one (which
+ *   a buffer belongs to the stream of its last use and later calls on that
+ *   stream reuse it; a call on another stream has hipMalloc add one (which
  *   may synchronise). Buffers live until the process ends: one per stream
- *   with calls in flight, each as large as the largest scratch asked for so
- *   far (a few MB at the benchmark sizes).
+ *   the library was called on, at most 64, each as large as the largest
+ *   scratch asked for on it so far (a few MB at the benchmark sizes); past
+ *   64, a call waits for the device once and takes over another stream's
+ *   buffer. A stream must not be destroyed while work the library enqueued
+ *   on it is still executing (synchronise it first).
  * - Arguments are validated on the host before anything is enqueued; a call
  *   that returns an error has enqueued nothing. Errors of kernels that run
  *   later surface at the caller's next synchronisation with the stream.

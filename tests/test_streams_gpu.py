@@ -1,7 +1,8 @@
 """Forward calls from several host threads on several streams at once give
 the bits of the same calls run one after another: the library's reusable
-scratch buffers (each taken by one call at a time, reused in stream order or
-after the last user's work has finished) keep concurrent calls apart."""
+scratch buffers (each taken by one call at a time and reused only by later
+calls on the stream of its last use) keep concurrent calls apart; past 64
+streams a call waits for the device and takes over another stream's buffer."""
 
 import threading
 
@@ -81,3 +82,32 @@ def test_concurrent_streams_match_serial():
         for r in range(reps):
             assert torch.equal(outs[k][r], refs[k]), f"workload {k}, repetition {r}"
     print(f"[streams] {len(ws)} threads x {reps} calls on separate streams: bitwise equal", flush=True)
+
+
+def test_more_streams_than_scratch_slots():
+    """70 streams, two rounds of calls with growing and shrinking sizes: the
+    65th stream onwards takes over buffers of earlier streams after waiting
+    for the device, and every output still matches its serial reference."""
+    import diagonal_state_space_amd as s5
+    cuda = torch.device("cuda:0")
+    ws = [wl.make_random(2, 200 + 37 * (k % 5), 64, 64, io="bf16", seed=40 + k % 5) for k in range(5)]
+    ts = [_inputs(w, cuda) for w in ws]
+    refs = []
+    for w, t in zip(ws, ts):
+        y = torch.empty_like(t["u"])
+        _call(s5, w, t, y)
+        refs.append(y)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(70)]
+    outs = []
+    for rnd in range(2):
+        for k, st in enumerate(streams):
+            j = (k + rnd) % len(ws)
+            with torch.cuda.stream(st):   # the poison fill and the call in one stream's order
+                y = torch.full_like(ts[j]["u"], float("nan"))
+                _call(s5, ws[j], ts[j], y)
+            outs.append((j, y))
+    torch.cuda.synchronize()
+    for n, (j, y) in enumerate(outs):
+        assert torch.equal(y, refs[j]), f"call {n} (workload {j})"
+    print(f"[streams] {len(outs)} calls over {len(streams)} streams: bitwise equal", flush=True)
