@@ -239,7 +239,8 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.xlast = reinterpret_cast<float2*>(x_last);
   a.c_scale = opt.c_scale;
   a.bilinear = opt.bilinear;
-  a.gelu = opt.bidir ? 0 : opt.gelu;
+  a.gelu = opt.gelu;
+  a.bidir = opt.bidir;
   a.c_ld = static_cast<int>(c_cols);
 
   s5::ForwardLayout lay;
@@ -257,19 +258,6 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
   e = s5::launch_forward(a, lay, ws->ptr, stream, tl_events, tl_nevents);
-  if (e == hipSuccess && opt.bidir) {
-    // backward scan: reverse time, second half of C~, no feedthrough (the
-    // forward pass added it), added to the forward pass's y; then GELU
-    s5::ForwardArgs r = a;
-    r.c_off = static_cast<int>(P);
-    r.d = nullptr;
-    r.rev = true;
-    r.accum = true;
-    r.gelu = opt.gelu;
-    const int skip = 6;   // events of the forward pass's three launches
-    e = s5::launch_forward(r, lay, ws->ptr, stream, tl_nevents > skip ? tl_events + skip : nullptr,
-                           tl_nevents > skip ? tl_nevents - skip : 0);
-  }
   const hipError_t ef = scratch_release(ws, stream);
   if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
   return S5_OK;

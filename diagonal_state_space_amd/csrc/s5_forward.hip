@@ -68,6 +68,9 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
       if (p.scan8) ls = l8;
     }
     p.group = k ? fused::reduce_group(bf16_io, time_varying, KS) : 1;
+    // (above four K-steps with two mode tiles per wave, the second sum's
+    // registers do not fit beside the weights)
+    p.both = k && !time_varying && (KS <= 4 || M8 == 1);
     p.lds_reduce_ws = lrw;
     p.lds_reduce = lr;
     p.lds_scan = ls;
@@ -129,6 +132,12 @@ bool forward_layout(const ForwardArgs& a, ForwardLayout& l) {
   l.tot = off;    off += align_up(nranges * l.Ppad * sizeof(float2));
   l.tot_a = off;  off += align_up(nranges * l.Ppad * sizeof(float2));
   l.cap = off;    off += align_up(static_cast<size_t>(a.B) * 2 * l.Ppad * sizeof(float2));
+  if (a.bidir) {
+    l.sagg_b = off;  off += align_up(nranges * kStreams * l.Ppad * sizeof(float2));
+    l.tot_b = off;   off += align_up(nranges * l.Ppad * sizeof(float2));
+    l.tot_a_b = off; off += align_up(nranges * l.Ppad * sizeof(float2));
+    l.yp = off;      off += a.bf16_io ? align_up(static_cast<size_t>(a.B) * a.L * a.H * sizeof(float)) : 0;
+  }
   l.total = off;
   return true;
 }
@@ -204,11 +213,55 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   q.tot = reinterpret_cast<float2*>(base + l.tot);
   q.tot_a = reinterpret_cast<float2*>(base + l.tot_a);
   q.cap = reinterpret_cast<float2*>(base + l.cap);
+  if (!a.bidir) {
+    hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
+    if (e != hipSuccess) return e;
+    e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);
+    if (e != hipSuccess) return e;
+    return timed(2, ev, nev, stream, launch_scan, q, l.plan);
+  }
+  // Bidirectional form (time-invariant, stateless): the backward scan runs in
+  // reverse time over the mirrored ranges (backward range qq = forward range
+  // Q-1-qq), so the eight-wave pass 1 sums both scans' aggregates from one
+  // drive. The forward pass 2 stores y (D u included) as float32 (into the
+  // workspace for bf16 I/O, into y itself for float32 I/O); the backward
+  // pass 2 adds its readout (second half of C~) and stores y once, then GELU.
+  q.yp = a.bf16_io ? reinterpret_cast<float*>(base + l.yp) : static_cast<float*>(a.y);
+  q.sagg_b = reinterpret_cast<float2*>(base + l.sagg_b);
+  q.tot_b = reinterpret_cast<float2*>(base + l.tot_b);
+  q.tot_a_b = reinterpret_cast<float2*>(base + l.tot_a_b);
+  q.rev = 0;
+  q.accum = 0;
+  q.gelu = 0;
+  q.both = l.plan.both ? 1 : 0;
+  q.ypart = a.bf16_io ? 1 : 0;
   hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
   if (e != hipSuccess) return e;
   e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);
   if (e != hipSuccess) return e;
-  return timed(2, ev, nev, stream, launch_scan, q, l.plan);
+  e = timed(2, ev, nev, stream, launch_scan, q, l.plan);
+  if (e != hipSuccess) return e;
+  FusedParams r = q;
+  r.c_off = a.c_off + a.P;
+  r.d = nullptr;
+  r.rev = 1;
+  r.accum = 1;
+  r.gelu = a.gelu;
+  r.both = 0;
+  r.ypart = 0;
+  r.sagg = q.sagg_b;
+  r.tot = q.tot_b;
+  r.tot_a = q.tot_a_b;
+  e = timed(3, ev, nev, stream, pack_launcher, r, l.plan);   // C' of the second half (B_bar and modes as before)
+  if (e != hipSuccess) return e;
+  if (!q.both) {
+    e = timed(4, ev, nev, stream, launch_reduce, r, l.plan);
+  } else if (ev != nullptr && 9 < nev) {
+    (void)hipEventRecord(ev[8], stream);
+    (void)hipEventRecord(ev[9], stream);
+  }
+  if (e != hipSuccess) return e;
+  return timed(5, ev, nev, stream, launch_scan, r, l.plan);
 }
 
 }  // namespace s5

@@ -84,6 +84,13 @@ struct FusedParams {
   float2* tot_a;      // [B*Q][Ppad] workgroup range transition product
   float2* cap;        // [B][2][Ppad] state (from zero) and transition product of the
                       // stream holding token L-1, from its first token through L-1
+  // bidirectional form (time-invariant)
+  int both;           // pass 1 also writes the backward scan's aggregates (sagg_b, tot_b, tot_a_b)
+  int ypart;          // pass 2 writes y (D u included) as float32 into yp (the forward half)
+  float* yp;          // [B, L, H] float32 forward half of y; the backward pass adds it
+  float2* sagg_b;     // backward scan's stream and range aggregates, indexed as the
+  float2* tot_b;      // backward pass sees its ranges (range qq mirrors forward range
+  float2* tot_a_b;    // Q-1-qq, stream t mirrors stream 15-t)
 };
 
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.
@@ -94,6 +101,7 @@ struct FusedPlan {
   bool scan8 = false;       // pass 2 on the symmetric eight-wave kernel (with keep_scan)
   int ks = 0;               // its drive K-steps (Hpad / 32)
   int group = 1;            // nck is a multiple of this (reduce_group with `keep`)
+  bool both = false;        // the eight-wave pass 1 can sum the backward scan's aggregates too
   size_t lds_reduce = 0, lds_scan = 0, lds_reduce_ws = 0;
 };
 
@@ -103,6 +111,7 @@ struct ForwardLayout {
   FusedPlan plan;
   int Ppad = 0, Hpad = 0;
   size_t bpack = 0, cpack = 0, modes = 0, sagg = 0, sagg_a = 0, tot = 0, tot_a = 0, cap = 0, total = 0;
+  size_t sagg_b = 0, tot_b = 0, tot_a_b = 0, yp = 0;   // bidirectional form (yp: bf16 I/O)
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).

@@ -114,6 +114,11 @@ __device__ __forceinline__ void row_scan(cf& A, cf& X) {
   row_scan_step<8>(A, X);
 }
 
+// the value of lane 15 - t of the lane's 16-lane row (DPP row_mirror)
+__device__ __forceinline__ float row_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
 // ---- geometry ---------------------------------------------------------------------
 
 struct Lane {
@@ -248,15 +253,17 @@ constexpr int kBufferWord3 = 0x00020000;                     // raw buffer, 32-b
 
 // descriptor over the rows (of H elements) of workgroup range (b, qq) of u or
 // y: rows past the sequence end are outside it (below 1 GiB, host-checked).
-// In reverse time the range's tokens are the rows just before the first
-// tokens of the earlier ranges, counted from the end of the sequence.
+// In reverse time (the backward scan) range qq is the mirror of forward range
+// Q-1-qq: the same rows, run from the last of the padded range to the first
+// (see RowMap), so that both scans cut the sequence at the same tokens.
 template <bool BF16>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, const FusedParams& q, int b, int qq,
                                                              bool rev) {
   constexpr int esz = BF16 ? 2 : 4;
-  const int tok0 = qq * kStreams * q.Lseg;
+  const int qf = rev ? q.Q - 1 - qq : qq;
+  const int tok0 = qf * kStreams * q.Lseg;
   const int rows = min(q.L - tok0, kStreams * q.Lseg);
-  const size_t row0 = rev ? static_cast<size_t>(b) * q.L + (q.L - tok0 - rows) : range_row0(q, b, qq);
+  const size_t row0 = range_row0(q, b, qf);
   // The fields are workgroup-uniform; reading them from the first lane tells
   // the compiler so (where it cannot prove it, every buffer access would be
   // wrapped in a loop over the distinct descriptors of the wave's lanes).
@@ -269,22 +276,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* t, cons
 }
 
 // Memory row, relative to the range descriptor's base, of relative token row
-// r: r in forward time. In reverse time (the backward scan) the range's tokens
-// run backward from its last row, so row last - r; token rows past the
-// sequence end (r > last) go to last + 1, outside the descriptor.
+// r: r in forward time. In reverse time (the backward scan) the range's token
+// rows run backward from the last row of the padded range, so row
+// 16 Lseg - 1 - r; rows past the sequence end (the padding of the last
+// forward range, which the backward scan meets first, from a zero state that
+// zero inputs leave zero) go to last + 1, outside the descriptor.
 struct RowMap {
   bool rev;
   int last;   // rows of the range - 1
+  int full;   // 16 Lseg - 1
   __device__ __forceinline__ int operator()(uint32_t r) const {
     const int ri = static_cast<int>(r);
-    return !rev ? ri : (ri <= last ? last - ri : last + 1);
+    const int m = full - ri;
+    return !rev ? ri : (m <= last ? m : last + 1);
   }
 };
 
 template <bool REV>
 __device__ __forceinline__ RowMap row_map(const FusedParams& q, int qq) {
-  if (REV && q.rev) return {true, min(q.L - qq * kStreams * q.Lseg, kStreams * q.Lseg) - 1};
-  return {false, 0};
+  if (REV && q.rev) {
+    const int qf = q.Q - 1 - qq;
+    return {true, min(q.L - qf * kStreams * q.Lseg, kStreams * q.Lseg) - 1, kStreams * q.Lseg - 1};
+  }
+  return {false, 0, 0};
 }
 
 // Output epilogue by instance: XM = 2 always GELU (the form from q.gelu:
@@ -306,6 +320,18 @@ __device__ __forceinline__ Epi epilogue(const FusedParams& q) {
   return {XM == 3, XM == 2 || (XM == 3 && q.gelu != 0), (XM == 2 || XM == 3) && q.gelu == 2};
 }
 
+// Instances of the bidirectional form's two passes 2: XM = 4 (forward half)
+// stores y, D u included, as float32 into q.yp; XM = 3 (backward, reverse
+// time) adds those float32 values to its readout and stores y in the I/O type
+// once (for float32 I/O q.yp is y itself).
+template <int XM, bool BF16>
+constexpr bool y_bf16() { return BF16 && XM != 4; }
+
+template <int XM, bool BF16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedParams& q, int b, int qq, bool rev) {
+  return range_rsrc<y_bf16<XM, BF16>()>(XM == 4 ? static_cast<void*>(q.yp) : q.y, q, b, qq, rev);
+}
+
 template <int R, bool BF16, int NB, int NWV, bool VEC>
 __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rsrc_t rsrc, const RowMap& rm, int qq,
                                         int i, UStage<NB>& st) {
@@ -324,7 +350,8 @@ __device__ __forceinline__ void fetch_u(const FusedParams& q, __amdgpu_buffer_rs
     const int s = f / R;
     const int tok = tok_of<R>(q, qq, ln.t, i, n);
     const int h0 = 32 * s + 8 * ln.g + 4 * half;
-    const bool row_ok = live && blk < nblk && tok < q.L;
+    // (in reverse time the row map sends the padding outside the descriptor)
+    const bool row_ok = live && blk < nblk && (rm.rev || tok < q.L);
     const int roff = rm(rel_row<R>(q, ln.t, i, n)) * q.H;
     if constexpr (VEC) {
       const int off = row_ok && h0 < q.H ? (roff + h0) * esz : kBufferOOB;
@@ -714,9 +741,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_reduce(FusedParams q) {
 // and states of a four-wave split, so two waves fit on each SIMD and one
 // wave's scan overlaps the other's MFMAs. All waves share each u tile.
 // KS: the drive's K-steps (Hpad = 32 KS, at most 4), so that no MFMA multiplies padding.
+// XM = 2 (time-invariant, forward time): the bidirectional form's pass 1,
+// which also sums each stream's backward-scan aggregate from the same drive:
+// the backward scan enters a stream at its last token, so its state at the
+// stream's first token, from a zero start, is sum_k abar^k b_k over the
+// stream's tokens k = 0, 1, ... (with transition abar^Lseg, as forward).
 template <int MPW, int KS, int R, bool TV, bool BF16, int XM>
 __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
   constexpr bool EXT = XM != 0;   // options of the extended entry point
+  constexpr bool BOTH = XM == 2;
+  static_assert(!BOTH || !TV, "the backward scan is time-invariant");
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int NW8 = 2 * kWaves;
   constexpr int NT = 4 * MPW;                 // mode tiles
@@ -763,6 +797,17 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       z[m][r] = {0.0f, 0.0f};
       if constexpr (TV) A[m][r] = {1.0f, 0.0f};
     }
+  // backward aggregates (BOTH): sum of abar^k b_k and the running power abar^k
+  cf zb[BOTH ? M8 : 1][4], pw[BOTH ? M8 : 1][4];
+  if constexpr (BOTH) {
+#pragma unroll
+    for (int m = 0; m < M8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        zb[m][r] = {0.0f, 0.0f};
+        pw[m][r] = {1.0f, 0.0f};
+      }
+  }
 
   constexpr int NB = (KS * R * (BF16 ? 1 : 2) + NW8 - 1) / NW8;   // u staging blocks per wave
   constexpr int G = reduce_group(BF16, TV, KS);   // chunks per barrier (nck is a multiple of G)
@@ -850,7 +895,12 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
           const cf ab = ld_pf2(mt.ab + pm);
 #pragma unroll
           for (int n = 0; n < R; ++n) {
-            x = cfma(ab, x, {acc[m][0][n][r], acc[m][1][n][r]});
+            const cf bu = {acc[m][0][n][r], acc[m][1][n][r]};
+            x = cfma(ab, x, bu);
+            if constexpr (BOTH) {
+              zb[m][r] = cfma(pw[m][r], bu, zb[m][r]);
+              pw[m][r] = cmul(pw[m][r], ab);
+            }
             if (rec && n == lt.n && ln.t == lt.t) record_partial(q, b, pm, x, cf{1.0f, 0.0f});
           }
         }
@@ -953,11 +1003,25 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
         At = {aseg[m][r].x, aseg[m][r].y};
       }
       cf Xt = z[m][r];
+      cf Ab = At;
       row_scan(At, Xt);
       if (ln.t == kStreams - 1) {
         const size_t ti = static_cast<size_t>(bq) * q.Ppad + pm;
         q.tot[ti] = make_float2(Xt.re, Xt.im);
         q.tot_a[ti] = make_float2(At.re, At.im);
+      }
+      if constexpr (BOTH) {
+        // the backward pass's range Q-1-qq, stream 15-t; its range total
+        // combines the streams in its own order: lanes mirrored, then the scan
+        const size_t bqm = static_cast<size_t>(b) * q.Q + (q.Q - 1 - qq);
+        const size_t sib = (bqm * kStreams + (kStreams - 1 - ln.t)) * q.Ppad + pm;
+        q.sagg_b[sib] = make_float2(zb[m][r].re, zb[m][r].im);
+        cf Xb = {row_mirror(zb[m][r].re), row_mirror(zb[m][r].im)};
+        row_scan(Ab, Xb);
+        if (ln.t == kStreams - 1) {
+          q.tot_b[bqm * q.Ppad + pm] = make_float2(Xb.re, Xb.im);
+          q.tot_a_b[bqm * q.Ppad + pm] = make_float2(Ab.re, Ab.im);
+        }
       }
     }
   }
@@ -990,27 +1054,24 @@ __device__ __forceinline__ void u_for_y(const lds_byte* ub, int ht, int n, const
 }
 
 // y = acc + D u for 4 consecutive features h0..h0+3 of one row (row offset
-// roff, in elements, inside the range descriptor yr), then the GELU form the
-// epilogue asks for; bf16 rounding by the hardware conversion (round to
-// nearest even). Rows past the sequence end fall outside the descriptor and
-// features >= H get an offset beyond it, so the hardware drops those writes.
-// VEC: H % 4 == 0, one vector store.
+// roff, in elements, inside the range descriptor yr; y stored as bf16 when
+// BF16, else float32), plus (ep.accum) the float32 values at the same place
+// of descriptor yo, then the GELU form the epilogue asks for; bf16 rounding by
+// the hardware conversion (round to nearest even). Rows past the sequence end
+// fall outside the descriptor and features >= H get an offset beyond it, so
+// the hardware drops those writes. VEC: H % 4 == 0, one vector store.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int h0, int H, const f32x4& acc,
-                                        const float4& d4, const float (&uv)[4], const Epi& ep) {
+                                        const float4& d4, const float (&uv)[4], const Epi& ep,
+                                        __amdgpu_buffer_rsrc_t yo) {
   constexpr int esz = BF16 ? 2 : 4;
   f32x4 yv = {fmaf(d4.x, uv[0], acc[0]), fmaf(d4.y, uv[1], acc[1]), fmaf(d4.z, uv[2], acc[2]),
               fmaf(d4.w, uv[3], acc[3])};
   if constexpr (VEC) {
     const int off = h0 < H ? (roff + h0) * esz : kBufferOOB;
     if (ep.accum) {
-      if constexpr (BF16) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const auto o = __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0);
-        yv += __builtin_convertvector(__builtin_bit_cast(bf16x4, o), f32x4);
-      } else {
-        yv += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
-      }
+      const int offo = h0 < H ? (roff + h0) * 4 : kBufferOOB;
+      yv += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yo, offo, 0, 0));
     }
     if (ep.gelu) {
       if (ep.tanh_form) {
@@ -1035,11 +1096,8 @@ __device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t yr, int roff, int
     for (int m = 0; m < 4; ++m) {
       const int off = h0 + m < H ? (roff + h0 + m) * esz : kBufferOOB;
       if (ep.accum) {
-        if constexpr (BF16) {
-          yv[m] += __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(yr, off, 0, 0)) << 16);
-        } else {
-          yv[m] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(yr, off, 0, 0));
-        }
+        const int offo = h0 + m < H ? (roff + h0 + m) * 4 : kBufferOOB;
+        yv[m] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(yo, offo, 0, 0));
       }
       if (ep.gelu) yv[m] = ep.tanh_form ? gelu_tanh(yv[m]) : gelu_erf(yv[m]);
       if constexpr (BF16) {
@@ -1088,11 +1146,14 @@ __device__ __forceinline__ void load_c_step(const FusedParams& q, int ht, int s,
 }
 
 // y for chunk i of the workgroup's streams from the x tile and u tile in LDS
-template <int MPW, int R, bool BF16, bool KEEP, bool VEC>
+// (y stored as bf16 when YB, else float32; yo: the float32 values added when
+// ep.accum)
+template <int MPW, int R, bool BF16, bool KEEP, bool VEC, bool YB>
 __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm,
                                         const Epi& ep,
                                         const CKeep<MPW, BF16 ? 1 : 2>& ck, const S5_LDS float* s_d,
-                                        const lds_byte* xb, const lds_byte* ub, int i, const Lane& ln) {
+                                        const lds_byte* xb, const lds_byte* ub, int i, const Lane& ln,
+                                        __amdgpu_buffer_rsrc_t yo) {
   constexpr int NP = BF16 ? 1 : 2;
   constexpr int K2 = 4 * MPW;
   const int HT = q.Hpad >> 4;
@@ -1121,7 +1182,7 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
       for (int n = 0; n < R; ++n) {
         float uv[4];
         u_for_y<R, BF16>(ub, ht, n, ln, uv);
-        store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], d4, uv, ep);
+        store_y<YB, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n], d4, uv, ep, yo);
       }
     }
   } else {
@@ -1178,8 +1239,8 @@ __device__ __forceinline__ void readout(const FusedParams& q, __amdgpu_buffer_rs
         for (int n = 0; n < R; ++n) {
           float uv[4];
           u_for_y<R, BF16>(ub, ht, n, ln, uv);
-          store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n],
-                             make_float4(dv[0], dv[1], dv[2], dv[3]), uv, ep);
+          store_y<YB, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, yacc[e][n],
+                           make_float4(dv[0], dv[1], dv[2], dv[3]), uv, ep, yo);
         }
       }
     }
@@ -1245,13 +1306,14 @@ __device__ __forceinline__ f32x4 y_old_f32(const std::conditional_t<BF16, uint2,
   }
 }
 
-// ACC: add `old` (the y already in memory, loaded a chunk ahead) to the sums
-template <int R, bool BF16, bool VEC, bool ACC = false>
+// ACC: add `old` (float32 values already in memory, loaded a chunk ahead) to
+// the sums; y stored as bf16 when YB, else float32
+template <int R, bool BF16, bool VEC, bool ACC, bool YB>
 __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buffer_rsrc_t yr, const RowMap& rm,
                                               const Epi& ep,
                                               const float4 (&dk)[kKeepHT], const f32x4 (&yacc)[kKeepHT][R],
                                               const lds_byte* ub, int i, const Lane& ln,
-                                              const YOld<BF16>* old = nullptr) {
+                                              const YOld<false>* old) {
   float uv[kKeepHT][R][4];
 #pragma unroll
   for (int e = 0; e < kKeepHT; ++e)
@@ -1263,9 +1325,9 @@ __device__ __forceinline__ void readout_store(const FusedParams& q, __amdgpu_buf
 #pragma unroll
     for (int n = 0; n < R; ++n) {
       f32x4 a = yacc[e][n];
-      if constexpr (ACC) a += y_old_f32<BF16>(old->v[e][n]);
-      store_y<BF16, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, a, dk[e], uv[e][n],
-                         Epi{ACC ? false : ep.accum, ep.gelu, ep.tanh_form});
+      if constexpr (ACC) a += y_old_f32<false>(old->v[e][n]);
+      store_y<YB, VEC>(yr, rm(rel_row<R>(q, ln.t, i, n)) * q.H, h0, q.H, a, dk[e], uv[e][n],
+                       Epi{false, ep.gelu, ep.tanh_form}, yr);
     }
   }
 }
@@ -1379,7 +1441,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
   // ---- chunk pipeline ----
   constexpr int NB = u_stage_blocks<R, BF16, KEEP>();
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
-  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = y_rsrc<XM, BF16>(q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yorsrc = XM == 3 ? range_rsrc<false>(q.yp, q, b, qq, rmap.rev) : yrsrc;
   auto chunks = [&](auto vec_c) {
   constexpr bool VEC = decltype(vec_c)::value;
   {
@@ -1475,7 +1538,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       const int ui2 = ui1 == 2 ? 0 : ui1 + 1;
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the drive
       stash_u<R, BF16, NB, kWaves>(q, ust, lds + ui2 * ut);
-      readout<MPW, R, BF16, KEEP, VEC>(q, yrsrc, rmap, epilogue<XM>(q), ck, mt.d, xb, lds + ui * ut, i, ln);
+      readout<MPW, R, BF16, KEEP, VEC, y_bf16<XM, BF16>()>(q, yrsrc, rmap, epilogue<XM>(q), ck, mt.d, xb,
+                                                         lds + ui * ut, i, ln, yorsrc);
       ui = ui1;
     }
   }
@@ -1697,7 +1761,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
-  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = y_rsrc<XM, BF16>(q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yorsrc = XM == 3 ? range_rsrc<false>(q.yp, q, b, qq, rmap.rev) : yrsrc;
   // one register array holds the role's weights: B_bar fragments [s][jj][cc][pl]
   // in drive waves, C' fragments [e][s][pl] in readout waves (16 MPW NP each)
   static_assert(sizeof(BKeep<MPW, NP>) == sizeof(CKeep<MPW, NP>), "both roles hold 16 MPW NP fragments");
@@ -1770,8 +1835,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   } else {
     // backward scan (XM = 3): the y being added to, a chunk ahead in registers
     constexpr bool kAcc = XM == 3;
-    YOld<BF16> yold;
-    if constexpr (kAcc) load_y_old<R, BF16, VEC>(q, yrsrc, rmap, 0, ln, yold);
+    YOld<false> yold;
+    if constexpr (kAcc) load_y_old<R, false, VEC>(q, yorsrc, rmap, 0, ln, yold);
     int ui = 0;   // i % 3
     for (int i = 0; i < q.nck; ++i) {
       const int ui1 = ui == 2 ? 0 : ui + 1;
@@ -1780,8 +1845,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // (not carried across iterations: no register shuffles, no early wait)
       UStage<NB> ust2;
       fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 2, ust2);
-      YOld<BF16> ynext;
-      if constexpr (kAcc) load_y_old<R, BF16, VEC>(q, yrsrc, rmap, i + 1, ln, ynext);
+      YOld<false> ynext;
+      if constexpr (kAcc) load_y_old<R, false, VEC>(q, yorsrc, rmap, i + 1, ln, ynext);
       const lds_byte* xr = xlds + (i & 1) * xt;
       f32x4 yacc[kKeepHT][R];
 #pragma unroll
@@ -1811,7 +1876,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // y stores, so that waiting for the loads does not wait for them
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the MFMAs
       stash_u<R, BF16, NB, kWaves>(q, ust2, lds + ui2 * ut);
-      readout_store<R, BF16, VEC, kAcc>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc, lds + ui * ut, i, ln, &yold);
+      readout_store<R, BF16, VEC, kAcc, y_bf16<XM, BF16>()>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc,
+                                                             lds + ui * ut, i, ln, &yold);
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
       if constexpr (kAcc) yold = ynext;
       ui = ui1;
@@ -1854,14 +1920,18 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
   const int blocks = q.B * q.Q;
   const bool xm = q.x0 != nullptr || q.xlast != nullptr || q.rev || (q.bilinear && TV);
   if constexpr (KEEP) {
+    constexpr int M8 = (4 * MPW + 2 * kWaves - 1) / (2 * kWaves);   // mode tiles per wave
     auto go = [&](auto ks_c) {
       constexpr int KS = decltype(ks_c)::value;
+      if constexpr (!TV && (KS <= 4 || M8 == 1)) {
+        if (q.both) return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
+      }
+      if (q.both) return hipErrorInvalidValue;   // not planned
       if (xm) return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
       return launch_one<k_reduce_ws<MPW, KS, R, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_reduce_ws, s, q);
     };
     // the drive's K-steps: H <= 128, and time-invariant H <= 256 where the
     // weights fit 128 registers (M8 KS NP <= 16)
-    constexpr int M8 = (4 * MPW + 2 * kWaves - 1) / (2 * kWaves);
     constexpr int kMaxKS = TV ? 4 : 16 / (M8 * (BF16 ? 1 : 2));
     auto big = [&](auto ks_c) {
       if constexpr (decltype(ks_c)::value <= kMaxKS) {
@@ -1882,6 +1952,7 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
       default: return hipErrorInvalidValue;
     }
   } else {
+    if (q.both) return hipErrorInvalidValue;   // the host runs the backward pass 1 separately here
     if (xm) return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_reduce, s, q);
     return launch_one<k_reduce<MPW, R, TV, BF16, KEEP, 0>>(blocks, kThreads, p.lds_reduce, s, q);
   }
@@ -1892,11 +1963,15 @@ template <int MPW, int KS, bool TV, bool BF16>
 hipError_t launch_scan8_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
   if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
-  const int xm = q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
+  const int xm = q.ypart ? 4 : q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
   if constexpr (TV) {
-    if (xm == 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
+    if (xm >= 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
   } else {
     if (xm == 3) return launch_one<k_scan8<MPW, KS, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    if constexpr (BF16) {
+      if (xm == 4) return launch_one<k_scan8<MPW, KS, TV, BF16, 4>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    }
+    if (xm == 4) return hipErrorInvalidValue;   // float32 I/O: the forward half is y itself
   }
   if (xm == 2) return launch_one<k_scan8<MPW, KS, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
   if (xm == 1) return launch_one<k_scan8<MPW, KS, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
@@ -1907,15 +1982,19 @@ template <int MPW, int R, bool TV, bool BF16, bool KEEP>
 hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
   if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
-  const int xm = q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
+  const int xm = q.ypart ? 4 : q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
   if constexpr (TV) {
-    if (xm == 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
+    if (xm >= 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
   }
+  if (xm == 4 && !BF16) return hipErrorInvalidValue;   // float32 I/O: the forward half is y itself
   if constexpr (KEEP && TV && MPW > 2) {
     return hipErrorInvalidValue;   // not planned: the time-varying step keeps at most two tiles per wave
   } else if constexpr (KEEP) {
     if constexpr (!TV) {
       if (xm == 3) return launch_one<k_scan_ws<MPW, R, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+      if constexpr (BF16) {
+        if (xm == 4) return launch_one<k_scan_ws<MPW, R, TV, BF16, 4>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+      }
     }
     if (xm == 2) return launch_one<k_scan_ws<MPW, R, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
     if (xm == 1) return launch_one<k_scan_ws<MPW, R, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
@@ -1923,6 +2002,9 @@ hipError_t launch_scan_t(const FusedParams& q, const FusedPlan& p, hipStream_t s
   } else {
     if constexpr (!TV) {
       if (xm == 3) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 3>>(blocks, kThreads, p.lds_scan, s, q);
+      if constexpr (BF16) {
+        if (xm == 4) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 4>>(blocks, kThreads, p.lds_scan, s, q);
+      }
     }
     if (xm == 2) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 2>>(blocks, kThreads, p.lds_scan, s, q);
     if (xm == 1) return launch_one<k_scan<MPW, R, TV, BF16, KEEP, 1>>(blocks, kThreads, p.lds_scan, s, q);

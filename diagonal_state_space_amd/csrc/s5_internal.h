@@ -34,6 +34,7 @@ struct ForwardArgs {
   bool rev = false;             // reverse time (the backward scan)
   bool accum = false;           // add the result to y
   int gelu = 0;                 // GELU of the final y: 0 no, 1 exact form, 2 tanh form
+  bool bidir = false;           // bidirectional form: forward and backward scans, c_tilde [H, 2P]
 };
 
 // One recurrent step for B sequences (validated on the host): x [B, P] in
@@ -81,7 +82,10 @@ hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, 
 
 // Enqueue the whole forward path on `stream` using `ws` (l.total bytes,
 // 256-byte aligned), with the layout forward_layout gave for `a`. ev[2k] /
-// ev[2k+1] are recorded around the k-th kernel launch for k < nev/2.
+// ev[2k+1] are recorded around the k-th kernel launch for k < nev/2: packing,
+// pass 1, pass 2; for the bidirectional form then the backward scan's
+// packing, its own pass 1 (an empty pair where the forward pass 1 computed
+// its aggregates) and its pass 2.
 hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws, hipStream_t stream,
                           const hipEvent_t* ev, int nev);
 

@@ -478,7 +478,8 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
 
   constexpr int NB = (KS * R * (BF16 ? 1 : 2) + kW8 - 1) / kW8;
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
-  const __amdgpu_buffer_rsrc_t yrsrc = range_rsrc<BF16>(q.y, q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yrsrc = y_rsrc<XM, BF16>(q, b, qq, rmap.rev);
+  const __amdgpu_buffer_rsrc_t yorsrc = XM == 3 ? range_rsrc<false>(q.yp, q, b, qq, rmap.rev) : yrsrc;
   // the packed B_bar (bf16: one plane of 2 Ppad/16 KS fragments) for the streamed drive
   const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint4*>(q.bpack), 0, (q.Ppad / 16) * 2 * KS * kBlock, kBufferWord3);
@@ -526,12 +527,12 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
     // sums from the previous iteration, u tile i-1), drive and scan of chunk
     // i+1 (u tile i+1 -> x tile (i+1) & 1), u tile i+2 staged.
     f32x4 yprev[ET][R];
-    YOld<BF16> yold_prev, yold_cur;
+    YOld<false> yold_prev, yold_cur;
 #pragma unroll
     for (int e = 0; e < ET; ++e)
 #pragma unroll
       for (int n = 0; n < R; ++n) yprev[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto epilogue_of = [&](int c, const f32x4 (&ya)[ET][R], const YOld<BF16>& yo) __attribute__((always_inline)) {
+    auto epilogue_of = [&](int c, const f32x4 (&ya)[ET][R], const YOld<false>& yo) __attribute__((always_inline)) {
       const lds_byte* ub = lds + (c & 3) * ut;
 #pragma unroll
       for (int e = 0; e < ET; ++e) {
@@ -543,10 +544,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
           float uv[4];
           u_for_y8<R, BF16>(ub, ht, n, ln.t, ln.g, uv);
           f32x4 a = ya[e][n];
-          if constexpr (kAcc) a += y_old_f32<BF16>(yo.v[e][n]);
+          if constexpr (kAcc) a += y_old_f32<false>(yo.v[e][n]);
           const float4 d = SB ? lds_ld<float4>(reinterpret_cast<const lds_byte*>(mtab.d + h0)) : dk[SB ? 0 : e];
-          store_y<BF16, VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, a, d, uv,
-                             Epi{false, ep.gelu, ep.tanh_form});
+          store_y<y_bf16<XM, BF16>(), VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, a, d, uv,
+                                           Epi{false, ep.gelu, ep.tanh_form}, yrsrc);
         }
       }
     };
@@ -555,7 +556,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, i + 2, w, ln, dnext);
       UStage<NB> ust;
       fetch_u<R, BF16, NB, kW8, VEC>(q, ursrc, rmap, qq, i + 2, ust);
-      if constexpr (kAcc) load_y_old8<R, BF16, VEC, ET>(q, yrsrc, rmap, i, w, ln, yold_cur);
+      if constexpr (kAcc) load_y_old8<R, false, VEC, ET>(q, yorsrc, rmap, i, w, ln, yold_cur);
       if constexpr (SB) {
         if (i + 1 < q.nck) get_bwin8<MT, NT, KS, kBW>(brsrc, w, ln.l, bwin);
       }

@@ -205,8 +205,8 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *       read out by the second half of C~, which then has 2P columns:
  *       y_k = Re(C~[:, :P] x_k) + Re(C~[:, P:] x'_k) + D u_k (wikillm
  *       notes, "Paper vs code", bidirectional scans). Time-invariant only,
- *       without x0/x_last. For bf16 io the forward half of y is rounded to
- *       bf16 once before the backward half is added.
+ *       without x0/x_last. The forward half is kept in float32 (for bf16
+ *       io in library scratch of 4*B*L*H bytes), so y is rounded once.
  *
  * Fields of s5_forward_desc:
  *   size        sizeof(s5_forward_desc) (for later extension)
