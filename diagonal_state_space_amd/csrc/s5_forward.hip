@@ -137,6 +137,7 @@ bool forward_layout(const ForwardArgs& a, ForwardLayout& l) {
     l.tot_b = off;   off += align_up(nranges * l.Ppad * sizeof(float2));
     l.tot_a_b = off; off += align_up(nranges * l.Ppad * sizeof(float2));
     l.yp = off;      off += a.bf16_io ? align_up(static_cast<size_t>(a.B) * a.L * a.H * sizeof(float)) : 0;
+    l.cpack_b = off; off += align_up(planes * nc * 16);
   }
   l.total = off;
   return true;
@@ -235,6 +236,7 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   q.gelu = 0;
   q.both = l.plan.both ? 1 : 0;
   q.ypart = a.bf16_io ? 1 : 0;
+  q.cpack_b = reinterpret_cast<uint4*>(base + l.cpack_b);   // both halves' C' in one packing launch
   hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
   if (e != hipSuccess) return e;
   e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);
@@ -252,8 +254,12 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   r.sagg = q.sagg_b;
   r.tot = q.tot_b;
   r.tot_a = q.tot_a_b;
-  e = timed(3, ev, nev, stream, pack_launcher, r, l.plan);   // C' of the second half (B_bar and modes as before)
-  if (e != hipSuccess) return e;
+  r.cpack = q.cpack_b;
+  r.cpack_b = nullptr;
+  if (ev != nullptr && 7 < nev) {   // (no second packing launch: an empty pair)
+    (void)hipEventRecord(ev[6], stream);
+    (void)hipEventRecord(ev[7], stream);
+  }
   if (!q.both) {
     e = timed(4, ev, nev, stream, launch_reduce, r, l.plan);
   } else if (ev != nullptr && 9 < nev) {

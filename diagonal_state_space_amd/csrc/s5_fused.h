@@ -77,6 +77,7 @@ struct FusedParams {
   uint4* bpack;       // drive operand fragments (hi plane, then lo plane for float32 I/O):
                       // B_bar, or B~/lambda for the time-varying path
   uint4* cpack;       // readout operand fragments (hi, then lo)
+  uint4* cpack_b;     // the backward scan's (bidirectional form; null otherwise)
   ModeParams* modes;  // [Ppad]
   float2* sagg;       // [B*Q][16][Ppad] stream state from a zero start
   float2* sagg_a;     // [B*Q][16][Ppad] stream transition product (time-varying)
@@ -111,7 +112,7 @@ struct ForwardLayout {
   FusedPlan plan;
   int Ppad = 0, Hpad = 0;
   size_t bpack = 0, cpack = 0, modes = 0, sagg = 0, sagg_a = 0, tot = 0, tot_a = 0, cap = 0, total = 0;
-  size_t sagg_b = 0, tot_b = 0, tot_a_b = 0, yp = 0;   // bidirectional form (yp: bf16 I/O)
+  size_t sagg_b = 0, tot_b = 0, tot_a_b = 0, yp = 0, cpack_b = 0;   // bidirectional form (yp: bf16 I/O)
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).

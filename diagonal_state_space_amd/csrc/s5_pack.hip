@@ -28,7 +28,9 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int nb = (q.Ppad / 16) * 2 * KS * 64;  // B_bar fragment lanes
   const int nc = (q.Hpad / 16) * K2 * 64;      // C' fragment lanes
   const int nm = q.Ppad;                        // per-mode values
-  const int total = nb + nc + nm;
+  // (bidirectional form: the backward scan's C' too, from the columns P
+  // further on, into cpack_b)
+  const int total = nb + nc + nm + (q.cpack_b != nullptr ? nc : 0);
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
     if (idx < nb) {
       // fragment ((j*2 + c)*KS + s), lane l: row m = l%16 (mode 16j+m), k = 8(l/16)+i
@@ -61,10 +63,13 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         v[i] = static_cast<float>(val);
       }
       put_frag(v, q.bpack + idx, split ? q.bpack + nb + idx : nullptr);
-    } else if (idx < nb + nc) {
+    } else if (idx < nb + nc || idx >= nb + nc + nm) {
       // fragment (ht*K2 + s), lane l: row h = 16 ht + l%16, k = 32 s + 8(l/16) + i,
       // k = 2p + comp with comp 0 -> Re C~, comp 1 -> -Im C~
-      const int e = idx - nb;
+      const bool second = idx >= nb + nc + nm;
+      const int e = second ? idx - nb - nc - nm : idx - nb;
+      const int c_off = second ? q.c_off + q.P : q.c_off;
+      uint4* cp = second ? q.cpack_b : q.cpack;
       const int l = e & 63;
       const int f = e >> 6;
       const int s = f % K2;
@@ -77,12 +82,12 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
         const int p = k >> 1;
         float val = 0.0f;
         if (h < q.H && p < q.P) {
-          const float2 ct = q.c_tilde[static_cast<size_t>(h) * q.c_ld + q.c_off + p];
+          const float2 ct = q.c_tilde[static_cast<size_t>(h) * q.c_ld + c_off + p];
           val = q.c_scale * ((k & 1) ? -ct.y : ct.x);
         }
         v[i] = val;
       }
-      put_frag(v, q.cpack + e, split ? q.cpack + nc + e : nullptr);
+      put_frag(v, cp + e, split ? cp + nc + e : nullptr);
     } else if (idx < nb + nc + nm) {
       const int p = idx - nb - nc;
       ModeParams mp{};
@@ -121,7 +126,8 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
 
 hipError_t launch_pack(const FusedParams& q, hipStream_t stream) {
   const int KS = q.Hpad / 32, K2 = 2 * q.Ppad / 32;
-  const int total = (q.Ppad / 16) * 2 * KS * 64 + (q.Hpad / 16) * K2 * 64 + q.Ppad;
+  const int nc = (q.Hpad / 16) * K2 * 64;
+  const int total = (q.Ppad / 16) * 2 * KS * 64 + nc + q.Ppad + (q.cpack_b != nullptr ? nc : 0);
   const int blocks = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
   hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, stream, q, q.bf16_io ? 0 : 1);
   return hipGetLastError();
