@@ -1836,7 +1836,6 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
     // backward scan (XM = 3): the y being added to, a chunk ahead in registers
     constexpr bool kAcc = XM == 3;
     YOld<false> yold;
-    if constexpr (kAcc) load_y_old<R, false, VEC>(q, yorsrc, rmap, 0, ln, yold);
     int ui = 0;   // i % 3
     for (int i = 0; i < q.nck; ++i) {
       const int ui1 = ui == 2 ? 0 : ui + 1;
@@ -1845,8 +1844,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       // (not carried across iterations: no register shuffles, no early wait)
       UStage<NB> ust2;
       fetch_u<R, BF16, NB, kWaves, VEC>(q, ursrc, rmap, qq, i + 2, ust2);
-      YOld<false> ynext;
-      if constexpr (kAcc) load_y_old<R, false, VEC>(q, yorsrc, rmap, i + 1, ln, ynext);
+      // (the values this chunk's readout adds: issued with the u loads, ahead
+      // of the readout MFMAs that hide their latency)
+      if constexpr (kAcc) load_y_old<R, false, VEC>(q, yorsrc, rmap, i, ln, yold);
       const lds_byte* xr = xlds + (i & 1) * xt;
       f32x4 yacc[kKeepHT][R];
 #pragma unroll
@@ -1879,7 +1879,6 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
       readout_store<R, BF16, VEC, kAcc, y_bf16<XM, BF16>()>(q, yrsrc, rmap, epilogue<XM>(q), dk, yacc,
                                                              lds + ui * ut, i, ln, &yold);
       lds_barrier();   // x tile i+1 and u tile i+2 complete; x tile i and u tile i-1 free
-      if constexpr (kAcc) yold = ynext;
       ui = ui1;
     }
   }
