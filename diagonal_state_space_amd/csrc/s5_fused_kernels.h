@@ -852,7 +852,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
       bf16x8 uf[NP][R];
       get_u<R, BF16, !BF16>(ub, s, ln.l, uf);
 #pragma unroll
-      for (int m = 0; m < M8; ++m)
+      for (int m = 0; m < M8; ++m) {
+        // waves past the last tile (NT not a multiple of 8) issue no MFMAs
+        if ((NT % NW8) != 0 && ln.w + NW8 * m >= NT) continue;   // wave-uniform
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -863,6 +865,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_reduce_ws(FusedParams q) {
               acc[m][cc][n] = mfma(bw[s][m][cc][1], uf[0][n], acc[m][cc][n]);
             }
           }
+      }
     }
   };
   // the stream states through one chunk's drive; rec: the chunk holding token
