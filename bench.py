@@ -502,6 +502,11 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
         ct_run = ct
     opts = {"stateful": {}, "half": {"half_spectrum": True}, "bilinear": {"bilinear": True},
             "gelu": {"gelu": True}, "bidir": {"bidirectional": True}}
+    if v == "gated":
+        # the gated activation (variant 1, with bias) in the same call
+        gw, gb = gate_params(w.H)
+        opts["gated"] = {"glu_w": torch.from_numpy(gw).to(lam.device),
+                         "glu_bias": torch.from_numpy(gb).to(lam.device), "glu_variant": 1}
     chunk = int(v.split(":")[1]) if v.startswith("chunked:") else 0
     if v == "step":
         return bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas)
@@ -585,6 +590,13 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
     return 0
 
 
+def gate_params(H: int):
+    """Seeded W [H, H] ~ N(0, 1/H) and bias ~ N(0, 1/4) of the gated activation, float32."""
+    rng = np.random.default_rng(7)
+    return ((rng.normal(size=(H, H)) / math.sqrt(H)).astype(np.float32),
+            (0.5 * rng.normal(size=H)).astype(np.float32))
+
+
 def cpu_baseline_variant(w, v, ct_run, budget_s: float):
     """The oracle's forward_ex with the variant's options on the whole
     workload (chunked: one call over the whole sequence, as the chunks carry
@@ -596,10 +608,13 @@ def cpu_baseline_variant(w, v, ct_run, budget_s: float):
             "bidir": {"bidirectional": True}}.get(v, {})
     if v == "stateful" or v.startswith("chunked:"):
         kw["x0"] = np.zeros((w.B, w.P), np.complex128)
+    gate = gate_params(w.H) if v == "gated" else None
     times = []
     while not times or (sum(times) < budget_s and len(times) < 25):
         t0 = time.perf_counter()
-        orc.forward_ex(w.u, w.lam, w.b_tilde, c, w.d, **kw, **opts)
+        y, _ = orc.forward_ex(w.u, w.lam, w.b_tilde, c, w.d, **kw, **opts)
+        if gate is not None:
+            orc.glu(y, gate[0], gate[1], 1)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": w.B * w.L / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
@@ -626,7 +641,7 @@ def main() -> int:
     ap.add_argument("--cpu-repeats", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--variant", default="plain",
-                    help="plain | stateful | half | bilinear | gelu | bidir | chunked:C | step | glu | glu2")
+                    help="plain | stateful | half | bilinear | gelu | bidir | gated | chunked:C | step | glu | glu2")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     ap.add_argument("--other-configs", default="0,1,2,4",

@@ -51,6 +51,7 @@ FLAG_BILINEAR = 1 << 1
 FLAG_GELU = 1 << 2
 FLAG_BIDIRECTIONAL = 1 << 3
 FLAG_GELU_TANH = 1 << 4
+FLAG_GLU = 1 << 5
 
 
 class ForwardDesc(ctypes.Structure):
@@ -60,7 +61,8 @@ class ForwardDesc(ctypes.Structure):
                 ("u", ctypes.c_void_p), ("lam", ctypes.c_void_p), ("b_tilde", ctypes.c_void_p),
                 ("c_tilde", ctypes.c_void_p), ("d", ctypes.c_void_p), ("log_delta", ctypes.c_void_p),
                 ("delta", ctypes.c_void_p), ("x0", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("x_last", ctypes.c_void_p)]
+                ("x_last", ctypes.c_void_p),
+                ("glu_w", ctypes.c_void_p), ("glu_bias", ctypes.c_void_p), ("glu_variant", ctypes.c_int32)]
 
 
 class S5Error(RuntimeError):
@@ -260,11 +262,14 @@ def forward_timevarying_stateful(u, lam, b_tilde, c_tilde, d, delta, x0=None, y=
 
 def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None, *,
                half_spectrum=False, bilinear=False, gelu=False, bidirectional=False,
-               final_state=False, gelu_tanh=False, y=None, x_last=None, stream=None):
+               final_state=False, gelu_tanh=False, glu_w=None, glu_bias=None, glu_variant=1,
+               y=None, x_last=None, stream=None):
     """The forward pass with its options (s5_forward_ex): exactly one of
     log_delta [P] (time-invariant) and delta [B, L, P] (time-varying);
-    c_tilde [H, 2P] when bidirectional. Returns (y, x_last), x_last None
-    unless final_state is set or an x_last buffer is given."""
+    c_tilde [H, 2P] when bidirectional; glu_w [H, H] float32 (with glu_bias
+    [H] or None, glu_variant 1 or 2) applies the gated activation to y.
+    Returns (y, x_last), x_last None unless final_state is set or an x_last
+    buffer is given."""
     import torch
     if u.dim() != 3:
         raise ValueError("u must be [B, L, H]")
@@ -292,14 +297,21 @@ def forward_ex(u, lam, b_tilde, c_tilde, d, log_delta=None, delta=None, x0=None,
         x_last = torch.empty(B, P, dtype=torch.complex64, device=u.device)
     if x_last is not None:
         _dev_tensor(x_last, "x_last", torch.complex64, (B, P))
+    if glu_w is not None:
+        _dev_tensor(glu_w, "glu_w", torch.float32, (H, H))
+        if glu_bias is not None:
+            _dev_tensor(glu_bias, "glu_bias", torch.float32, (H,))
     flags = ((FLAG_HALF_SPECTRUM if half_spectrum else 0) | (FLAG_BILINEAR if bilinear else 0) |
              (FLAG_GELU if gelu else 0) | (FLAG_BIDIRECTIONAL if bidirectional else 0) |
-             (FLAG_GELU_TANH if gelu_tanh else 0))
+             (FLAG_GELU_TANH if gelu_tanh else 0) | (FLAG_GLU if glu_w is not None else 0))
     desc = ForwardDesc(ctypes.sizeof(ForwardDesc), flags, io, B, L, H, P, u.data_ptr(), lam.data_ptr(),
                        b_tilde.data_ptr(), c_tilde.data_ptr(), d.data_ptr(),
                        log_delta.data_ptr() if log_delta is not None else None,
                        delta.data_ptr() if delta is not None else None, x0p, y.data_ptr(),
-                       x_last.data_ptr() if x_last is not None else None)
+                       x_last.data_ptr() if x_last is not None else None,
+                       glu_w.data_ptr() if glu_w is not None else None,
+                       glu_bias.data_ptr() if glu_bias is not None and glu_w is not None else None,
+                       glu_variant if glu_w is not None else 0)
     _check(lib().s5_forward_ex(ctypes.byref(desc), _stream_handle(stream)), "s5_forward_ex")
     return y, x_last
 

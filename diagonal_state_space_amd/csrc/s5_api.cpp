@@ -156,6 +156,9 @@ struct Options {
   bool bilinear = false;   // bilinear discretisation
   int gelu = 0;            // GELU epilogue: 0 no, 1 exact form, 2 tanh form
   bool bidir = false;      // forward and backward scans, C~ with 2P columns
+  const float* glu_w = nullptr;      // gated activation of the output (null: none)
+  const float* glu_bias = nullptr;
+  int glu_variant = 0;
 };
 
 s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io, const void* u,
@@ -174,8 +177,9 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (tokens > 0 && (!u || !y || (time_varying && !delta))) return S5_ERR_INVALID_ARGUMENT;
   // the backward scan is defined for the time-invariant, stateless form only
   if (opt.bidir && (time_varying || x0 || x_last)) return S5_ERR_INVALID_ARGUMENT;
+  if (opt.glu_w && H > S5_GLU_MAX_H) return S5_ERR_UNSUPPORTED;
   const int64_t c_cols = opt.bidir ? 2 * P : P;
-  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y, x0, x_last};
+  const void* ptrs[] = {u, lambda, b_tilde, c_tilde, d, log_delta, delta, y, x0, x_last, opt.glu_w, opt.glu_bias};
   for (const void* p : ptrs) {
     if (p && !aligned16(p)) return S5_ERR_UNSUPPORTED;
   }
@@ -189,7 +193,9 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
                             range_of(d, H * 4),
                             log_delta ? range_of(log_delta, P * 4) : Range{0, 0},
                             delta ? range_of(delta, tokens * P * 4) : Range{0, 0},
-                            x0 ? range_of(x0, B * P * 8) : Range{0, 0}};
+                            x0 ? range_of(x0, B * P * 8) : Range{0, 0},
+                            opt.glu_w ? range_of(opt.glu_w, H * H * 4) : Range{0, 0},
+                            opt.glu_bias ? range_of(opt.glu_bias, H * 4) : Range{0, 0}};
     for (const Range& r : inputs) {
       if (overlaps(ry, r)) return S5_ERR_INVALID_ARGUMENT;
     }
@@ -242,9 +248,25 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.gelu = opt.gelu;
   a.bidir = opt.bidir;
   a.c_ld = static_cast<int>(c_cols);
+  // the gate inside the output pass where that pass's symmetric kernel
+  // takes it (bf16 io, H <= 128, no backward scan), else after the layer
+  bool glu_fused = opt.glu_w != nullptr && a.bf16_io && H <= 128 && !opt.bidir;
+  if (glu_fused) {
+    a.glu_w = opt.glu_w;
+    a.glu_bias = opt.glu_bias;
+    a.glu_variant = opt.glu_variant;
+  }
 
   s5::ForwardLayout lay;
   if (!s5::forward_layout(a, lay)) return S5_ERR_UNSUPPORTED;
+  if (glu_fused && !lay.plan.scan8) {
+    // no symmetric output pass for this shape: the plain plan, gate after it
+    glu_fused = false;
+    a.glu_w = nullptr;
+    a.glu_bias = nullptr;
+    a.glu_variant = 0;
+    if (!s5::forward_layout(a, lay)) return S5_ERR_UNSUPPORTED;
+  }
   if (noalloc) {
     // the fixed per-device array; the options path (backward scan) never comes here
     if (lay.total > S5_NOALLOC_SCRATCH_BYTES || opt.bidir) return S5_ERR_UNSUPPORTED;
@@ -258,6 +280,18 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
   e = s5::launch_forward(a, lay, ws->ptr, stream, tl_events, tl_nevents);
+  if (e == hipSuccess && opt.glu_w != nullptr && !glu_fused) {
+    s5::GluArgs g{};
+    g.T = static_cast<int>(tokens);
+    g.H = static_cast<int>(H);
+    g.bf16_io = a.bf16_io;
+    g.variant = opt.glu_variant;
+    g.y = y;
+    g.w = opt.glu_w;
+    g.bias = opt.glu_bias;
+    g.out = y;   // in place
+    e = s5::launch_glu(g, stream);
+  }
   const hipError_t ef = scratch_release(ws, stream);
   if (e != hipSuccess || ef != hipSuccess) return S5_ERR_HIP;
   return S5_OK;
@@ -332,9 +366,11 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
 }
 
 s5_status s5_forward_ex(const s5_forward_desc* x, hipStream_t stream) {
-  if (x == nullptr || x->size != sizeof(s5_forward_desc)) return S5_ERR_INVALID_ARGUMENT;
-  const uint32_t known =
-      S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_BIDIRECTIONAL | S5_FLAG_GELU_TANH;
+  if (x == nullptr) return S5_ERR_INVALID_ARGUMENT;
+  const bool v1 = x->size == S5_FORWARD_DESC_SIZE_V1;   // a caller built before the gate fields
+  if (!v1 && x->size != sizeof(s5_forward_desc)) return S5_ERR_INVALID_ARGUMENT;
+  const uint32_t known = S5_FLAG_HALF_SPECTRUM | S5_FLAG_BILINEAR | S5_FLAG_GELU | S5_FLAG_BIDIRECTIONAL |
+                         S5_FLAG_GELU_TANH | (v1 ? 0u : static_cast<uint32_t>(S5_FLAG_GLU));
   if ((x->flags & ~known) != 0) return S5_ERR_INVALID_ARGUMENT;
   if ((x->flags & S5_FLAG_GELU) && (x->flags & S5_FLAG_GELU_TANH)) return S5_ERR_INVALID_ARGUMENT;
   if ((x->log_delta == nullptr) == (x->delta == nullptr)) return S5_ERR_INVALID_ARGUMENT;
@@ -343,6 +379,14 @@ s5_status s5_forward_ex(const s5_forward_desc* x, hipStream_t stream) {
   o.bilinear = (x->flags & S5_FLAG_BILINEAR) != 0;
   o.gelu = (x->flags & S5_FLAG_GELU) ? 1 : (x->flags & S5_FLAG_GELU_TANH) ? 2 : 0;
   o.bidir = (x->flags & S5_FLAG_BIDIRECTIONAL) != 0;
+  if (x->flags & S5_FLAG_GLU) {
+    // the gate applies its own GELU: no GELU form beside it
+    if (o.gelu != 0 || x->glu_w == nullptr || (x->glu_variant != 1 && x->glu_variant != 2))
+      return S5_ERR_INVALID_ARGUMENT;
+    o.glu_w = x->glu_w;
+    o.glu_bias = x->glu_bias;
+    o.glu_variant = x->glu_variant;
+  }
   return forward_common(x->B, x->L, x->H, x->P, x->io, x->u, x->lambda, x->b_tilde, x->c_tilde, x->d,
                         x->log_delta, x->delta, x->y, x->delta != nullptr, x->x0, x->x_last, o, stream);
 }

@@ -10,7 +10,7 @@ namespace s5 {
 
 using fused::kStreams;
 
-void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p) {
+void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, bool gate, FusedPlan& p) {
   const int MPW = Ppad / 64, KS = Hpad / 32, K2 = Ppad / 16, NP = bf16_io ? 1 : 2;
   const size_t lds_max = 160 * 1024;
   // weights in registers: all drive K-steps (H <= 128) and readout h-tiles,
@@ -63,9 +63,13 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan&
       // time-invariant pass 2 with H <= 128 is matrix-core bound and runs
       // faster with its roles specialized
       const bool tv8 = ks && time_varying && KS <= 4 && MPW <= (bf16_io ? 4 : 2);
-      p.scan8 = (tv8 || sb) && R == 2 && wregs <= 128 && l8 <= lds_max;
+      // the gated activation inside this pass (bf16, H <= 128): a ring of two
+      // g tiles of two planes, the multipliers and the bias too
+      const bool gate8 = gate && bf16_io && KS <= 4 && (tv8 || (ks && !time_varying));
+      const size_t lg = l8 + (gate8 ? (4 * static_cast<size_t>(KS) + 8 * ET) * R * fused::kBlock + 4 * Hpad : 0);
+      p.scan8 = (tv8 || sb || gate8) && R == 2 && wregs <= 128 && lg <= lds_max;
       p.ks = KS;
-      if (p.scan8) ls = l8;
+      if (p.scan8) ls = lg;
     }
     p.group = k ? fused::reduce_group(bf16_io, time_varying, KS) : 1;
     // (above four K-steps with two mode tiles per wave, the second sum's
@@ -115,7 +119,7 @@ bool forward_layout(const ForwardArgs& a, ForwardLayout& l) {
   l = ForwardLayout{};
   l.Ppad = ((a.P + 63) / 64) * 64;
   l.Hpad = ((a.H + 31) / 32) * 32;
-  fused_shape(a.bf16_io, a.time_varying, l.Ppad, l.Hpad, l.plan);
+  fused_shape(a.bf16_io, a.time_varying, l.Ppad, l.Hpad, a.glu_w != nullptr, l.plan);
   if (l.plan.R == 0) return false;
   const int ncu = device_cus();
   fused_split(a.B, a.L, a.H, a.P, ncu > 0 ? ncu : 256, l.plan);
@@ -138,6 +142,9 @@ bool forward_layout(const ForwardArgs& a, ForwardLayout& l) {
     l.tot_a_b = off; off += align_up(nranges * l.Ppad * sizeof(float2));
     l.yp = off;      off += a.bf16_io ? align_up(static_cast<size_t>(a.B) * a.L * a.H * sizeof(float)) : 0;
     l.cpack_b = off; off += align_up(planes * nc * 16);
+  }
+  if (a.glu_w != nullptr) {
+    l.gpack = off;   off += align_up(2 * static_cast<size_t>(l.Hpad / 16) * (l.Hpad / 32) * 64 * 16);
   }
   l.total = off;
   return true;
@@ -199,6 +206,8 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   q.lam = a.lam; q.b_tilde = a.b_tilde; q.c_tilde = a.c_tilde;
   q.d = a.d; q.log_delta = a.log_delta; q.delta = a.delta;
   q.x0 = a.x0; q.xlast = a.xlast;
+  q.glu_w = a.glu_w; q.glu_bias = a.glu_bias; q.glu_variant = a.glu_variant;
+  q.gpack = a.glu_w != nullptr ? reinterpret_cast<uint4*>(base + l.gpack) : nullptr;
   q.c_ld = a.c_ld > 0 ? a.c_ld : a.P;
   q.c_off = a.c_off;
   q.c_scale = a.c_scale;

@@ -92,6 +92,12 @@ struct FusedParams {
   float2* sagg_b;     // backward scan's stream and range aggregates, indexed as the
   float2* tot_b;      // backward pass sees its ranges (range qq mirrors forward range
   float2* tot_a_b;    // Q-1-qq, stream t mirrors stream 15-t)
+  // gated activation in the output pass (symmetric kernel, bf16 I/O)
+  const float* glu_w;     // [H, H] float32, output j reads row j; null: no gate
+  const float* glu_bias;  // [H] or null
+  int glu_variant;        // 1: GELU(y) * gate, 2: y * gate
+  uint4* gpack;           // the gate's W as A-operand fragments, bf16 hi plane then lo plane
+                          // ([Hpad/16][Hpad/32][64 lanes] each); null: no gate
 };
 
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.
@@ -113,10 +119,11 @@ struct ForwardLayout {
   int Ppad = 0, Hpad = 0;
   size_t bpack = 0, cpack = 0, modes = 0, sagg = 0, sagg_a = 0, tot = 0, tot_a = 0, cap = 0, total = 0;
   size_t sagg_b = 0, tot_b = 0, tot_a_b = 0, yp = 0, cpack_b = 0;   // bidirectional form (yp: bf16 I/O)
+  size_t gpack = 0;   // the gate's packed W (gated activation in the output pass)
 };
 
 // R and `keep` for these sizes (R = 0: no compiled instance fits).
-void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, FusedPlan& p);
+void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, bool gate, FusedPlan& p);
 // Fill in nck, Lseg and Q for B sequences of length L (features H, modes P)
 // on `ncu` compute units.
 void fused_split(int B, int L, int H, int P, int ncu, FusedPlan& p);

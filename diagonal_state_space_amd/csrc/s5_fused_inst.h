@@ -24,9 +24,12 @@ constexpr int kKeepMaxMPW = kBF16 ? 4 : 2;
 // and the time-varying step
 template <int MPW, int KS>
 hipError_t scan8_ks(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
-  // instances whose LDS (four u tiles, two x tiles, the mode table) fits
+  // instances whose LDS (four u tiles, two x tiles, the mode table, and for
+  // the gate (bf16 I/O, at most four K-steps) its ring of two-plane g tiles,
+  // multipliers and bias) fits
   constexpr size_t lds = 4 * fused::u8_tile_bytes(KS, 2, kBF16) + 2 * fused::x_tile_bytes(4 * MPW, 2, kBF16) +
-                         fused::mode_table_bytes(64 * MPW, 32 * KS, kTV, true);
+                         fused::mode_table_bytes(64 * MPW, 32 * KS, kTV, true) +
+                         (kBF16 && KS <= 4 ? (4 * KS + 8 * ((2 * KS + 7) / 8)) * 2 * fused::kBlock + 128 * KS : 0);
   if constexpr (lds > 160 * 1024) {
     return hipErrorInvalidValue;
   } else {
@@ -53,7 +56,11 @@ hipError_t scan8(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
       }
     }
   } else if constexpr (kBF16) {
-    switch (p.ks) {
+    switch (p.ks) {   // (1..4: the gate only)
+      case 1: return scan8_ks<MPW, 1>(q, p, s);
+      case 2: return scan8_ks<MPW, 2>(q, p, s);
+      case 3: return scan8_ks<MPW, 3>(q, p, s);
+      case 4: return scan8_ks<MPW, 4>(q, p, s);
       case 5: return scan8_ks<MPW, 5>(q, p, s);
       case 6: return scan8_ks<MPW, 6>(q, p, s);
       case 7: return scan8_ks<MPW, 7>(q, p, s);

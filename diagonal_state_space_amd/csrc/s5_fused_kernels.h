@@ -1960,24 +1960,52 @@ hipError_t launch_reduce_t(const FusedParams& q, const FusedPlan& p, hipStream_t
   }
 }
 
-// pass 2 on the symmetric eight-wave kernel (KS drive K-steps)
+// pass 2 on the symmetric eight-wave kernel (KS drive K-steps). Instances:
+// the time-varying step (plain, state, GELU; the gate with bf16 I/O), the
+// streamed drive above four K-steps (time-invariant bf16: plain, state, GELU,
+// both bidirectional halves) and, at most four K-steps time-invariant, the
+// gate only (the plain call takes the wave-specialized kernel there).
 template <int MPW, int KS, bool TV, bool BF16>
 hipError_t launch_scan8_t(const FusedParams& q, const FusedPlan& p, hipStream_t s) {
   const int blocks = q.B * q.Q;
   if (q.rev != q.accum) return hipErrorInvalidValue;   // reverse time only for the backward scan
-  const int xm = q.ypart ? 4 : q.accum ? 3 : q.gelu ? 2 : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
+  const int xm = q.glu_w != nullptr ? 5
+               : q.ypart ? 4
+               : q.accum ? 3
+               : q.gelu ? 2
+               : (q.x0 != nullptr || q.xlast != nullptr || (q.bilinear && TV)) ? 1 : 0;
+  auto go = [&](auto xm_c) {
+    return launch_one<k_scan8<MPW, KS, TV, BF16, decltype(xm_c)::value>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+  };
+  using X0 = std::integral_constant<int, 0>;
+  using X1 = std::integral_constant<int, 1>;
+  using X2 = std::integral_constant<int, 2>;
+  using X3 = std::integral_constant<int, 3>;
+  using X4 = std::integral_constant<int, 4>;
+  using X5 = std::integral_constant<int, 5>;
   if constexpr (TV) {
-    if (xm >= 3) return hipErrorInvalidValue;   // the backward scan is time-invariant only
-  } else {
-    if (xm == 3) return launch_one<k_scan8<MPW, KS, TV, BF16, 3>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+    if (xm == 0) return go(X0{});
+    if (xm == 1) return go(X1{});
+    if (xm == 2) return go(X2{});
     if constexpr (BF16) {
-      if (xm == 4) return launch_one<k_scan8<MPW, KS, TV, BF16, 4>>(blocks, 2 * kThreads, p.lds_scan, s, q);
+      if (xm == 5) return go(X5{});
     }
-    if (xm == 4) return hipErrorInvalidValue;   // float32 I/O: the forward half is y itself
+    return hipErrorInvalidValue;   // the backward scan is time-invariant only
+  } else if constexpr (KS > 4) {
+    if constexpr (BF16) {
+      if (xm == 0) return go(X0{});
+      if (xm == 1) return go(X1{});
+      if (xm == 2) return go(X2{});
+      if (xm == 3) return go(X3{});
+      if (xm == 4) return go(X4{});
+    }
+    return hipErrorInvalidValue;
+  } else {
+    if constexpr (BF16) {
+      if (xm == 5) return go(X5{});
+    }
+    return hipErrorInvalidValue;
   }
-  if (xm == 2) return launch_one<k_scan8<MPW, KS, TV, BF16, 2>>(blocks, 2 * kThreads, p.lds_scan, s, q);
-  if (xm == 1) return launch_one<k_scan8<MPW, KS, TV, BF16, 1>>(blocks, 2 * kThreads, p.lds_scan, s, q);
-  return launch_one<k_scan8<MPW, KS, TV, BF16, 0>>(blocks, 2 * kThreads, p.lds_scan, s, q);
 }
 
 template <int MPW, int R, bool TV, bool BF16, bool KEEP>

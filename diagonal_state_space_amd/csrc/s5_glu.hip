@@ -6,9 +6,11 @@
 // per workgroup eight waves, wave w holding the operand fragments of output
 // tiles w, w + 8, ... of W for all K-steps in registers (loaded once), and a
 // persistent loop over tiles of 64 tokens whose GELU(y) is staged in LDS as
-// B operands (bf16; float32 I/O splits every operand into hi and lo and sums
-// three products), with the epilogue's multiplier (GELU(y) or y, float32)
-// beside them. The epilogue adds the bias, applies the logistic gate and the
+// B operands, with the epilogue's multiplier (GELU(y) or y, float32) beside
+// them. Both operands are split into bf16 hi and lo parts and three products
+// summed (W_hi g_hi + W_hi g_lo + W_lo g_hi), for either I/O type: the gate's
+// slope times |g| amplifies the rounding of W g, so single bf16 products
+// lose accuracy once |y| grows past a few units. The epilogue adds the bias, applies the logistic gate and the
 // multiplier and stores the result, all in the same pass.
 #include <algorithm>
 
@@ -63,7 +65,7 @@ __device__ __forceinline__ void load8(const GluArgs& q, size_t idx, int count, b
 
 template <bool BF16, bool SMALL>
 __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
-  constexpr int NP = BF16 ? 1 : 2;
+  constexpr int NP = 2;   // hi and lo planes of both operands
   constexpr int kGluMaxKS = glu_ks<SMALL>();
   constexpr int kGluMaxMT = glu_mt<SMALL>();
   extern __shared__ __align__(16) unsigned char smem[];
@@ -102,7 +104,7 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
       }
       const bf16x8 hi = __builtin_convertvector(f, bf16x8);
       wf[mt][s][0] = hi;
-      if constexpr (NP == 2) wf[mt][s][1] = __builtin_convertvector(f - __builtin_convertvector(hi, f32x8), bf16x8);
+      wf[mt][s][1] = __builtin_convertvector(f - __builtin_convertvector(hi, f32x8), bf16x8);
     }
   }
 
@@ -145,9 +147,8 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
       for (int i = 0; i < 8; ++i) f[i] = gelu_erf(yv[i]);
       const bf16x8 hi = __builtin_convertvector(f, bf16x8);
       *reinterpret_cast<uint4*>(gblk(s, nt, 0) + l * 16) = as_u4(hi);
-      if constexpr (NP == 2)
-        *reinterpret_cast<uint4*>(gblk(s, nt, 1) + l * 16) =
-            as_u4(__builtin_convertvector(f - __builtin_convertvector(hi, f32x8), bf16x8));
+      *reinterpret_cast<uint4*>(gblk(s, nt, 1) + l * 16) =
+          as_u4(__builtin_convertvector(f - __builtin_convertvector(hi, f32x8), bf16x8));
       float4* dst = reinterpret_cast<float4*>(s_mul + tl * mstride + k0);
       if (q.variant == 1) {
         dst[0] = make_float4(f[0], f[1], f[2], f[3]);
@@ -172,12 +173,10 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
 #pragma unroll
         for (int nt = 0; nt < kGluNT; ++nt) {
           const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4*>(gblk(s, nt, 0) + l * 16));
+          const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4*>(gblk(s, nt, 1) + l * 16));
+          acc[nt] = mfma(wf[mt][s][0], b1, acc[nt]);
+          acc[nt] = mfma(wf[mt][s][1], b0, acc[nt]);
           acc[nt] = mfma(wf[mt][s][0], b0, acc[nt]);
-          if constexpr (NP == 2) {
-            const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4*>(gblk(s, nt, 1) + l * 16));
-            acc[nt] = mfma(wf[mt][s][0], b1, acc[nt]);
-            acc[nt] = mfma(wf[mt][s][1], b0, acc[nt]);
-          }
         }
       }
       // lane (t, g): token 16 nt + t, outputs j0 = 16 m + 4 g .. j0 + 3
@@ -229,7 +228,8 @@ __global__ void __launch_bounds__(kGluThreads) k_glu(GluArgs q) {
 
 size_t glu_lds_bytes(int H, bool bf16_io) {
   const size_t ks = (H + 31) / 32;
-  return ks * kGluNT * (bf16_io ? 1 : 2) * 1024 + static_cast<size_t>(kGluTokens) * (32 * ks + 4) * sizeof(float);
+  (void)bf16_io;   // (two operand planes for either I/O type)
+  return ks * kGluNT * 2 * 1024 + static_cast<size_t>(kGluTokens) * (32 * ks + 4) * sizeof(float);
 }
 
 // one launch of instance Kern; its first launch lifts the dynamic LDS limit

@@ -35,6 +35,9 @@ struct ForwardArgs {
   bool accum = false;           // add the result to y
   int gelu = 0;                 // GELU of the final y: 0 no, 1 exact form, 2 tanh form
   bool bidir = false;           // bidirectional form: forward and backward scans, c_tilde [H, 2P]
+  const float* glu_w = nullptr;     // gated activation in the output pass (bf16, H <= 128), or null
+  const float* glu_bias = nullptr;  // [H] or null
+  int glu_variant = 0;              // 1: GELU(y) * gate, 2: y * gate
 };
 
 // One recurrent step for B sequences (validated on the host): x [B, P] in

@@ -29,9 +29,30 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
   const int nc = (q.Hpad / 16) * K2 * 64;      // C' fragment lanes
   const int nm = q.Ppad;                        // per-mode values
   // (bidirectional form: the backward scan's C' too, from the columns P
-  // further on, into cpack_b)
-  const int total = nb + nc + nm + (q.cpack_b != nullptr ? nc : 0);
+  // further on, into cpack_b; gated activation: the gate's W, split into bf16
+  // hi and lo planes, into gpack)
+  const int nc2 = q.cpack_b != nullptr ? nc : 0;
+  const int ng = q.gpack != nullptr ? (q.Hpad / 16) * KS * 64 : 0;
+  const int g0 = nb + nc + nm + nc2;
+  const int total = g0 + ng;
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+    if (idx >= g0) {
+      // fragment (ht*KS + s), lane l: row j = 16 ht + l%16 (gate output j),
+      // k = 32 s + 8(l/16) + i (input feature k); zero past H
+      const int e = idx - g0;
+      const int l = e & 63;
+      const int f = e >> 6;
+      const int s = f % KS;
+      const int j = 16 * (f / KS) + (l & 15);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 32 * s + 8 * (l >> 4) + i;
+        v[i] = j < q.H && k < q.H ? q.glu_w[static_cast<size_t>(j) * q.H + k] : 0.0f;
+      }
+      put_frag(v, q.gpack + e, q.gpack + ng + e);
+      continue;
+    }
     if (idx < nb) {
       // fragment ((j*2 + c)*KS + s), lane l: row m = l%16 (mode 16j+m), k = 8(l/16)+i
       const int l = idx & 63;
@@ -127,7 +148,8 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
 hipError_t launch_pack(const FusedParams& q, hipStream_t stream) {
   const int KS = q.Hpad / 32, K2 = 2 * q.Ppad / 32;
   const int nc = (q.Hpad / 16) * K2 * 64;
-  const int total = (q.Ppad / 16) * 2 * KS * 64 + nc + q.Ppad + (q.cpack_b != nullptr ? nc : 0);
+  const int total = (q.Ppad / 16) * 2 * KS * 64 + nc + q.Ppad + (q.cpack_b != nullptr ? nc : 0) +
+                    (q.gpack != nullptr ? (q.Hpad / 16) * KS * 64 : 0);
   const int blocks = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
   hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, stream, q, q.bf16_io ? 0 : 1);
   return hipGetLastError();

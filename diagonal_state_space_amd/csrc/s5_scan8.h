@@ -279,13 +279,13 @@ __device__ __forceinline__ void scan_tile8(bool bil, int j, int m, f32x4 (&acc)[
 // Drive, scan and x tile of the wave's mode tiles for one chunk (u tile ub,
 // x tile xb). Tile by tile, so that one tile's scan runs beside the next
 // tile's MFMAs. bf16: the chunk's u fragments are read once for all tiles.
-template <int MT, int NT, int KS, int R, bool TV, bool BF16>
+template <int MT, int NT, int KS, int R, bool TV, bool BF16, bool ONCE = true>
 __device__ __forceinline__ void drive_scan8(bool bil, int w, const bf16x8 (&bw)[KS][MT][2][BF16 ? 1 : 2],
                                             const lds_byte* ub, const ModeTable& mtab, const Lane& ln,
                                             const float4 (&dl)[TV ? MT : 1][TV ? R : 1], cf (&st)[MT][4],
                                             lds_byte* xb) {
   constexpr int NP = BF16 ? 1 : 2;
-  constexpr bool kOnce = BF16 && MT > 1;
+  constexpr bool kOnce = ONCE && BF16 && MT > 1;
   bf16x8 ua[kOnce ? KS : 1][NP][R];
   if constexpr (kOnce) {
 #pragma unroll
@@ -426,6 +426,20 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   constexpr bool SB = KS > 4;
   constexpr int kBW = MPW >= 4 ? 2 : MPW == 3 ? 3 : 4;   // (what the registers allow)
   static_assert(!SB || (BF16 && !TV), "the streamed drive is built for time-invariant bf16 I/O");
+  // XM = 5: the gated activation in this pass (bf16 I/O, H <= 128). Chunk c's
+  // y (D u included), rounded to bf16 as the layer would store it (so that
+  // the gate sees the same input as after a separate layer call), gives
+  // g = GELU(y), written as B-operand fragments (the
+  // layout of a bf16 u tile, inputs = features) split into a bf16 hi and lo
+  // plane, into a ring of two g tiles, and the multiplier (g or y, float32)
+  // into LDS; after the next barrier every wave forms W g for its h-tiles on
+  // the matrix cores from three products (W_hi g_hi + W_hi g_lo + W_lo g_hi:
+  // float32-level accuracy, since the gate's slope times |g| amplifies any
+  // rounding of W or g) and stores y = multiplier * sigma(W g + bias): one
+  // store of y, after the gate. W_hi stays in registers; W_lo is read from L2
+  // once per chunk (at the end of the previous iteration).
+  constexpr bool GATE = XM == 5;
+  static_assert(!GATE || (BF16 && !SB), "the fused gate is built for bf16 I/O with H <= 128");
   extern __shared__ __align__(16) unsigned char smem[];
   if (q.Ppad != 64 * MPW || q.Hpad != 32 * KS || q.R != R) return;   // dispatch mismatch: do nothing
   Lane ln = lane_ids();
@@ -441,6 +455,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   lds_byte* lds = (lds_byte*)smem;
   lds_byte* xlds = lds + 4 * ut;
   const ModeTable mtab = fill_mode_table<TV>(q, xlds + 2 * xt, true);
+  // the gate's ring of two g tiles (hi and lo planes), after the mode table,
+  // then its multipliers and the bias
+  constexpr int gt = static_cast<int>(KS * R * kBlock);   // one plane of one g tile
+  lds_byte* glds = xlds + 2 * xt + mode_table_bytes(64 * MPW, 32 * KS, TV, true);
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
   if (threadIdx.x < static_cast<unsigned>(q.Ppad)) range_carry<EXT>(q, b, qq, threadIdx.x, s_c0);
 
@@ -475,6 +493,42 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
                                  : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
         }
   }
+
+  // the gate's W fragments of the wave's h-tiles, hi plane (rows 16 ht +
+  // l%16, inputs 32 s + 8 (l/16) + 0..7, zero past H), and the descriptor of
+  // the lo plane
+  bf16x8 wg[GATE ? ET : 1][GATE ? KS : 1];
+  const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
+      GATE ? q.gpack + HT * KS * 64 : q.bpack, 0, GATE ? HT * KS * kBlock : 0, kBufferWord3);
+  if constexpr (GATE) {
+#pragma unroll
+    for (int e = 0; e < ET; ++e)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int ht = w + kW8 * e;
+        wg[e][s] = ht < HT ? as_bf16x8(ldg16(q.gpack + (ht * KS + s) * 64 + ln.l))
+                           : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+      }
+    lds_byte* gbias = glds + 4 * gt + 8 * ET * R * kBlock;
+    for (int h = threadIdx.x; h < q.Hpad; h += 2 * kThreads)
+      reinterpret_cast<S5_LDS float*>(gbias)[h] = q.glu_bias != nullptr && h < q.H ? q.glu_bias[h] : 0.0f;
+  }
+  bf16x8 wlo[GATE ? ET : 1][GATE ? KS : 1];
+  auto load_wlo = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < ET; ++e)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int ht = w + kW8 * e;
+        if (ht < HT) {
+          const int soff = __builtin_amdgcn_readfirstlane((ht * KS + s) * kBlock);
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(grsrc, ln.l * 16, soff, 0);
+          wlo[e][s] = as_bf16x8(make_uint4(v[0], v[1], v[2], v[3]));
+        } else {
+          wlo[e][s] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+        }
+      }
+  };
 
   constexpr int NB = (KS * R * (BF16 ? 1 : 2) + kW8 - 1) / kW8;
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);
@@ -516,7 +570,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       get_bwin8<MT, NT, KS, kBW>(brsrc, w, ln.l, bwin);
       drive_scan8_sb<MT, NT, KS, R, kBW>(w, brsrc, bwin, lds, mtab, ln, st, xlds);
     } else {
-      drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
+      drive_scan8<MT, NT, KS, R, TV, BF16, !GATE>(bil, w, bw, lds, mtab, ln, dl, st, xlds);
     }
     // Delta of chunk i+1 is loaded an iteration ahead (before that
     // iteration's u loads), so that waiting for it never waits for them
@@ -551,6 +605,86 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
         }
       }
     };
+    // the gate: chunk c's y -> g tile (c & 1) and the multiplier (first
+    // half), then, a barrier later, W g, the logistic gate and the store
+    // (each lane's multipliers wait in LDS for its own gate_out, one block
+    // per wave, h-tile and step)
+    lds_byte* gml = glds + 4 * gt + (w * ET * R) * kBlock + ln.l * 16;
+    const lds_byte* gbias = glds + 4 * gt + 8 * ET * R * kBlock;
+    auto gate_in = [&](int c, const f32x4 (&ya)[ET][R]) __attribute__((always_inline)) {
+      const lds_byte* ub = lds + (c & 3) * ut;
+      lds_byte* gb = glds + (c & 1) * 2 * gt;
+#pragma unroll
+      for (int e = 0; e < ET; ++e) {
+        const int ht = w + kW8 * e;
+        if (ht >= HT) continue;   // wave-uniform
+        // g fragment position of the lane's 4 features (as u_for_y8 reads a u tile)
+        const int sk = ht >> 1;
+        const int off = (ln.t + 16 * (2 * (ht & 1) + (ln.g >> 1))) * 16 + 8 * (ln.g & 1);
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          f32x4 yv = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (ht < HTv) {   // (features past H: g = 0, and W is zero there)
+            float uv[4];
+            u_for_y8<R, BF16>(ub, ht, n, ln.t, ln.g, uv);
+            const float4 d = dk[e];
+            yv = f32x4{fmaf(d.x, uv[0], ya[e][n][0]), fmaf(d.y, uv[1], ya[e][n][1]),
+                       fmaf(d.z, uv[2], ya[e][n][2]), fmaf(d.w, uv[3], ya[e][n][3])};
+            yv = __builtin_convertvector(__builtin_convertvector(yv, bf16x4), f32x4);   // the stored y
+          }
+          f32x4 g;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) g[r] = gelu_erf(yv[r]);
+          const bf16x4 ghi = __builtin_convertvector(g, bf16x4);
+          const bf16x4 glo = __builtin_convertvector(g - __builtin_convertvector(ghi, f32x4), bf16x4);
+          lds_st<uint2>(gb + (sk * R + n) * kBlock + off, __builtin_bit_cast(uint2, ghi));
+          lds_st<uint2>(gb + gt + (sk * R + n) * kBlock + off, __builtin_bit_cast(uint2, glo));
+          const f32x4 mv = q.glu_variant == 1 ? g : yv;
+          lds_st<float4>(gml + (e * R + n) * kBlock, make_float4(mv[0], mv[1], mv[2], mv[3]));
+        }
+      }
+    };
+    auto gate_out = [&](int c) __attribute__((always_inline)) {
+      const lds_byte* gb = glds + (c & 1) * 2 * gt;
+      f32x4 z[ET][R];
+#pragma unroll
+      for (int e = 0; e < ET; ++e)
+#pragma unroll
+        for (int n = 0; n < R; ++n) z[e][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int sk = 0; sk < KS; ++sk) {
+        bf16x8 gh[1][R], gl[1][R];
+        get_u8<R, true>(gb, sk, ln.l, gh);
+        get_u8<R, true>(gb + gt, sk, ln.l, gl);
+#pragma unroll
+        for (int e = 0; e < ET; ++e)
+#pragma unroll
+          for (int n = 0; n < R; ++n) {
+            z[e][n] = mfma(wg[e][sk], gl[0][n], z[e][n]);
+            z[e][n] = mfma(wlo[e][sk], gh[0][n], z[e][n]);
+            z[e][n] = mfma(wg[e][sk], gh[0][n], z[e][n]);
+          }
+      }
+#pragma unroll
+      for (int e = 0; e < ET; ++e) {
+        const int ht = w + kW8 * e;
+        if (ht >= HTv) continue;   // wave-uniform
+        const int h0 = 16 * ht + 4 * ln.g;
+        const float4 b4 = lds_ld<float4>(gbias + 4 * h0);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int n = 0; n < R; ++n) {
+          const float4 m4 = lds_ld<float4>(gml + (e * R + n) * kBlock);
+          const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+          f32x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = mv[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-(z[e][n][r] + bv[r])));
+          const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          store_y<BF16, VEC>(yrsrc, rmap(rel_row<R>(q, ln.t, c, n)) * q.H, h0, q.H, o,
+                             make_float4(0.0f, 0.0f, 0.0f, 0.0f), zero4, Epi{false, false, false}, yrsrc);
+        }
+      }
+    };
     for (int i = 0; i < q.nck; ++i) {
       float4 dnext[TV ? MT : 1][TV ? R : 1];
       if constexpr (TV) load_delta8<MT, NT, R>(q, b, qq, i + 2, w, ln, dnext);
@@ -559,6 +693,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       if constexpr (kAcc) load_y_old8<R, false, VEC, ET>(q, yorsrc, rmap, i, w, ln, yold_cur);
       if constexpr (SB) {
         if (i + 1 < q.nck) get_bwin8<MT, NT, KS, kBW>(brsrc, w, ln.l, bwin);
+      }
+      if constexpr (GATE) {
+        if (i > 0) gate_out(i - 1);   // g tile (i-1) & 1 is complete (the last barrier)
       }
       // readout of chunk i
       f32x4 yacc[ET][R];
@@ -570,7 +707,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       if (w < HT) {   // wave-uniform: waves past the h-tiles read nothing out
         // x fragments read kAhead K-steps ahead of their MFMAs (left alone,
         // the scheduler puts each read next to its use and waits there)
-        constexpr int kAhead = NP == 2 || SB ? 1 : 3;
+        constexpr int kAhead = NP == 2 || SB || GATE ? 1 : 3;
         bf16x8 xf[K2][NP][R];
 #pragma unroll
         for (int s = 0; s < kAhead && s < K2; ++s) get_x<R, NP>(xr, K2, s, ln.l, xf[s]);
@@ -584,7 +721,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
           __builtin_amdgcn_sched_group_barrier(0x008, ET * R * (NP == 2 ? 3 : 1), 0);
         }
       }
-      if constexpr (SB) {
+      if constexpr (GATE) {
+        gate_in(i, yacc);
+      } else if constexpr (SB) {
         epilogue_of(i, yacc, yold_cur);   // (no registers to keep the sums for the next iteration)
       } else if (i > 0) {
         epilogue_of(i - 1, yprev, yold_prev);   // y of chunk i-1 beside those MFMAs
@@ -595,13 +734,14 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
           drive_scan8_sb<MT, NT, KS, R, kBW>(w, brsrc, bwin, lds + ((i + 1) & 3) * ut, mtab, ln, st,
                                              xlds + ((i + 1) & 1) * xt);
         } else {
-          drive_scan8<MT, NT, KS, R, TV, BF16>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
-                                               xlds + ((i + 1) & 1) * xt);
+          drive_scan8<MT, NT, KS, R, TV, BF16, !GATE>(bil, w, bw, lds + ((i + 1) & 3) * ut, mtab, ln, dl, st,
+                                                      xlds + ((i + 1) & 1) * xt);
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the stash (and its wait) after the chunk's work
       stash8<R, BF16, NB>(q, ust, lds + ((i + 2) & 3) * ut, w, ln.l);
-      if constexpr (!SB) {
+      if constexpr (GATE) load_wlo();   // for gate_out of chunk i (next iteration, or after the loop)
+      if constexpr (!SB && !GATE) {
 #pragma unroll
         for (int e = 0; e < ET; ++e)
 #pragma unroll
@@ -616,7 +756,11 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
       }
       lds_barrier();   // x tile i+1, u tile i+2 complete; x tile i, u tile i-2 free
     }
-    if constexpr (!SB) epilogue_of(q.nck - 1, yprev, yold_prev);
+    if constexpr (GATE) {
+      gate_out(q.nck - 1);   // (after the loop's last barrier)
+    } else if constexpr (!SB) {
+      epilogue_of(q.nck - 1, yprev, yold_prev);
+    }
   };
   if (u_rows_vectorized(q.H, BF16)) {
     chunks(std::true_type{});

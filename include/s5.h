@@ -50,6 +50,7 @@
 #ifndef S5_H
 #define S5_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -207,6 +208,17 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *       notes, "Paper vs code", bidirectional scans). Time-invariant only,
  *       without x0/x_last. The forward half is kept in float32 (for bf16
  *       io in library scratch of 4*B*L*H bytes), so y is rounded once.
+ *   S5_FLAG_GLU  the gated activation of s5_glu applied to the layer's
+ *       output, out = (GELU(y) or y) * sigma(W GELU(y) + bias) with W =
+ *       glu_w, bias = glu_bias (NULL: none), variant glu_variant (1 or 2),
+ *       written to y. For bf16 io with H <= 128 and without the backward
+ *       scan it runs inside the output pass (y is stored once, gated);
+ *       otherwise as s5_glu on y in place after the layer. Either way the
+ *       gate reads y as the layer stores it (rounded to bf16 for bf16 io)
+ *       and gives the bits of s5_glu on that y. H <= S5_GLU_MAX_H.
+ *       Scratch: 4*H*H bytes more (W's packed operand planes) when fused.
+ *       Exclusive with S5_FLAG_GELU and S5_FLAG_GELU_TANH (the gate applies
+ *       its own GELU, the exact form).
  *
  * Fields of s5_forward_desc:
  *   size        sizeof(s5_forward_desc) (for later extension)
@@ -217,16 +229,24 @@ s5_status s5_forward_timevarying_stateful(int64_t B, int64_t L, int64_t H, int64
  *   delta       [B,L,P] per-step interval (time-varying), or NULL;
  *               exactly one of log_delta and delta is given
  *   x0, x_last  as s5_forward_stateful (NULL: zero / not written)
+ *   glu_w, glu_bias, glu_variant   with S5_FLAG_GLU: W [H,H] float32
+ *               (output j reads row j), bias [H] float32 or NULL, 1 or 2;
+ *               ignored without it. A caller built before these fields may
+ *               pass size = S5_FORWARD_DESC_SIZE_V1 (then no S5_FLAG_GLU).
  * Errors: as s5_forward_stateful; S5_ERR_INVALID_ARGUMENT for a wrong size
- * field, unknown flags, both GELU forms, both or neither interval arrays, or
- * S5_FLAG_BIDIRECTIONAL with delta, x0 or x_last.
+ * field, unknown flags, both GELU forms or a GELU form with the gate, both or
+ * neither interval arrays, S5_FLAG_BIDIRECTIONAL with delta, x0 or x_last,
+ * or S5_FLAG_GLU without glu_w, with another variant or with glu_w or
+ * glu_bias overlapping y; S5_ERR_UNSUPPORTED for S5_FLAG_GLU with
+ * H > S5_GLU_MAX_H.
  */
 enum {
   S5_FLAG_HALF_SPECTRUM = 1u << 0,
   S5_FLAG_BILINEAR = 1u << 1,
   S5_FLAG_GELU = 1u << 2,
   S5_FLAG_BIDIRECTIONAL = 1u << 3,
-  S5_FLAG_GELU_TANH = 1u << 4
+  S5_FLAG_GELU_TANH = 1u << 4,
+  S5_FLAG_GLU = 1u << 5
 };
 
 typedef struct {
@@ -244,7 +264,14 @@ typedef struct {
   const s5_c64* x0;
   void* y;
   s5_c64* x_last;
+  /* fields added after the first version (see S5_FORWARD_DESC_SIZE_V1) */
+  const float* glu_w;
+  const float* glu_bias;
+  int32_t glu_variant;
 } s5_forward_desc;
+
+/* size of s5_forward_desc up to x_last, the first version of the struct */
+#define S5_FORWARD_DESC_SIZE_V1 ((uint32_t)offsetof(s5_forward_desc, glu_w))
 
 s5_status s5_forward_ex(const s5_forward_desc* desc, hipStream_t stream);
 
@@ -296,9 +323,9 @@ s5_status s5_step(int64_t B, int64_t H, int64_t P, s5_dtype io, uint32_t flags, 
  *   w           [H,H]  float32, row-major: output j reads w[j, :]
  *   bias        [H]    float32, or NULL for none
  *   out         [T,H]  out; may be y itself (in place), else overlaps no input
- * Precision: W g on the matrix cores with bf16 operands (bf16 io) or the
- * bf16 hi/lo split of each float32 operand with three products (float32
- * io); float32 sums, GELU and gate.
+ * Precision: W g on the matrix cores from the bf16 hi/lo split of both
+ * float32 operands with three products (relative error below 2^-15 of
+ * sum |W||g|, for either io); float32 sums, GELU and gate.
  * Errors: S5_ERR_INVALID_ARGUMENT (null pointer, T < 0, H < 1, variant not
  * 1 or 2, overlaps), S5_ERR_UNSUPPORTED (io, H > S5_GLU_MAX_H,
  * misalignment), S5_ERR_HIP.

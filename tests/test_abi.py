@@ -187,9 +187,10 @@ def test_stateful_validation(tv):
 
 
 def _fwd_ex(flags=0, B=2, L=8, H=4, P=3, io=0, ct=FAKE + 0x3000, logd=FAKE + 0x5000, delta=None,
-            x0=None, x_last=None, y=FAKE + 0x100000, size=None):
+            x0=None, x_last=None, y=FAKE + 0x100000, size=None, glu_w=None, glu_bias=None, glu_variant=0):
     desc = s5.ForwardDesc(ctypes.sizeof(s5.ForwardDesc) if size is None else size, flags, io, B, L, H, P,
-                          FAKE, FAKE + 0x1000, FAKE + 0x2000, ct, FAKE + 0x4000, logd, delta, x0, y, x_last)
+                          FAKE, FAKE + 0x1000, FAKE + 0x2000, ct, FAKE + 0x4000, logd, delta, x0, y, x_last,
+                          glu_w, glu_bias, glu_variant)
     return s5.lib().s5_forward_ex(ctypes.byref(desc), None)
 
 
@@ -212,6 +213,21 @@ def test_forward_ex_validation():
     assert _fwd_ex(flags=bidir | s5.FLAG_GELU | s5.FLAG_HALF_SPECTRUM, B=0) == OK   # empty: no-op
     assert _fwd_ex(flags=s5.FLAG_BILINEAR, L=0) == OK
     assert _fwd_ex(P=0) == INVALID and _fwd_ex(H=1000) == UNSUPPORTED
+    # the gated activation
+    glu = s5.FLAG_GLU
+    w = FAKE + 0x9000
+    assert _fwd_ex(flags=glu, glu_variant=1) == INVALID                      # no W
+    assert _fwd_ex(flags=glu, glu_w=w, glu_variant=3) == INVALID             # no such variant
+    assert _fwd_ex(flags=glu | s5.FLAG_GELU, glu_w=w, glu_variant=1) == INVALID   # a GELU beside the gate's
+    assert _fwd_ex(flags=glu, glu_w=FAKE + 0x100000 - 32, glu_variant=2) == INVALID   # W overlaps y
+    assert _fwd_ex(flags=glu, glu_w=w, glu_bias=FAKE + 0x100000, glu_variant=1) == INVALID   # bias in y
+    assert _fwd_ex(flags=glu, glu_w=w + 4, glu_variant=1) == UNSUPPORTED     # misaligned
+    assert _fwd_ex(flags=glu, H=300, glu_w=w, glu_variant=1) == UNSUPPORTED  # beyond the gate's H
+    assert _fwd_ex(flags=glu, B=0, glu_w=w, glu_variant=2) == OK             # empty: no-op
+    # a caller built before the gate fields: the first version's size, no gate
+    v1 = s5.ForwardDesc.glu_w.offset
+    assert _fwd_ex(size=v1, B=0) == OK
+    assert _fwd_ex(size=v1, flags=glu, B=0, glu_w=w, glu_variant=1) == INVALID
 
 
 def _step(B=2, H=4, P=3, io=0, flags=0, logd=FAKE + 0x5000, delta=None, x=FAKE + 0x8000, y=FAKE + 0x9000,
@@ -260,7 +276,7 @@ def test_header_compiles_standalone(tmp_path, lang, std):
         pytest.skip("no host compiler")
     src = tmp_path / "use.c"
     src.write_text('#include "s5.h"\nint s5_probe(void) { s5_forward_desc d; d.size = sizeof d; '
-                   'return (int)d.size + S5_FLAG_BIDIRECTIONAL + S5_GLU_MAX_H; }\n')
+                   'return (int)d.size + (int)S5_FORWARD_DESC_SIZE_V1 + S5_FLAG_GLU + S5_GLU_MAX_H; }\n')
     r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.dirname(HEADER)}",
                         "-c", str(src), "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr

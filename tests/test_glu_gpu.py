@@ -1,7 +1,10 @@
 """GPU parity of the gated activation (s5_glu) against the float64 oracle's
-glu, through the C ABI. Bounds: max |out - out_oracle| / rms(out_oracle)
-<= 2e-4 for float32 I/O (bf16 hi/lo products); for bf16 I/O the excess over
-the output's own bf16 rounding (2^-8 |out|) <= 2e-2 of rms (bf16 operands)."""
+glu, through the C ABI. The error beyond the product's own rounding bound
+(gate_bound.glu_allowance with an exact input: the gate's slope times |m|
+times 2^-15 sum |W||GELU(y)|), and for bf16 I/O beyond the output's bf16
+rounding (2^-8 |out|), is <= 2e-4 of rms(out_oracle) for float32 I/O and
+<= 2e-2 for bf16 I/O. Both I/O types use bf16 hi/lo products; the
+large-scale cases (y of rms 15) fail with a single bf16 product."""
 
 import math
 
@@ -9,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle.s5_oracle as orc
+from gate_bound import glu_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -30,25 +34,28 @@ def _bf16_round(a):
 
 
 CASES = [
-    # T, H, io, variant, bias, in place
-    (17, 1, "f32", 1, True, False),
-    (100, 5, "f32", 2, False, False),
-    (1000, 96, "f32", 1, True, False),
-    (3001, 128, "f32", 2, True, True),
-    (2048, 256, "f32", 1, True, False),
-    (4099, 128, "bf16", 1, True, False),
-    (999, 256, "bf16", 2, True, True),
-    (64, 16, "bf16", 1, False, False),
+    # T, H, io, variant, bias, in place, scale of y
+    (17, 1, "f32", 1, True, False, 1.5),
+    (100, 5, "f32", 2, False, False, 1.5),
+    (1000, 96, "f32", 1, True, False, 1.5),
+    (3001, 128, "f32", 2, True, True, 1.5),
+    (2048, 256, "f32", 1, True, False, 1.5),
+    (4099, 128, "bf16", 1, True, False, 1.5),
+    (999, 256, "bf16", 2, True, True, 1.5),
+    (64, 16, "bf16", 1, False, False, 1.5),
+    (4099, 128, "bf16", 1, True, False, 15.0),
+    (2000, 256, "bf16", 2, True, False, 15.0),
+    (1000, 96, "f32", 1, True, False, 15.0),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"T{c[0]}_H{c[1]}_{c[2]}_v{c[3]}{'_bias' if c[4] else ''}"
-                         f"{'_inplace' if c[5] else ''}")
+                         f"{'_inplace' if c[5] else ''}_s{c[6]:g}")
 def test_glu_parity(case):
     import diagonal_state_space_amd as s5
-    T, H, io, variant, with_bias, inplace = case
+    T, H, io, variant, with_bias, inplace, scale = case
     rng = np.random.default_rng(T + H)
-    y = (rng.normal(size=(T, H)) * 1.5).astype(np.float32)
+    y = (rng.normal(size=(T, H)) * scale).astype(np.float32)
     w = (rng.normal(size=(H, H)) / math.sqrt(H)).astype(np.float32)
     b = (rng.normal(size=H) * 0.5).astype(np.float32) if with_bias else None
     if io == "bf16":
@@ -63,7 +70,7 @@ def test_glu_parity(case):
     ref = orc.glu(y.astype(np.float64), w, b, variant)
     got = out.float().cpu().numpy().astype(np.float64)
     rms = math.sqrt(float(np.mean(ref ** 2)))
-    excess = np.abs(got - ref)
+    excess = np.abs(got - ref) - glu_allowance(y.astype(np.float64), w, b, variant, rho=0.0)
     tol = 2e-4
     if io == "bf16":
         excess = excess - 2.0 ** -8 * np.abs(ref)

@@ -7,7 +7,17 @@ Bounds as test_parity_gpu: max |y_gpu - y_oracle| / rms(y_oracle) <= 2e-4
 for float32 I/O; for bf16 I/O the excess over the bf16 output rounding
 (2^-8 |y|) <= 2e-2 of rms (the bidirectional form included: its forward half
 is kept in float32, so y is rounded once). Final states: <= the same
-fraction of rms(x)."""
+fraction of rms(x).
+
+The gated activation is checked in two parts: the layer's output y_hat (the
+same call without the gate) against the oracle's y as above, and the gated
+output against the oracle's gate of y_hat, beyond the gate's product
+rounding bound (gate_bound.glu_allowance, exact input). The gate applies to
+the layer's output as stored in the I/O type (inside the output pass too,
+where y is rounded to bf16 before the gate), and it amplifies perturbations
+of its input by its slope times |m| times |W| (a few percent of rms for bf16
+rounding at |y| ~ 15): comparing with the oracle's gate of the oracle's y
+would measure that conditioning, not the kernels."""
 
 import math
 
@@ -16,6 +26,7 @@ import pytest
 
 import oracle.s5_oracle as orc
 import workloads as wl
+from gate_bound import glu_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +82,11 @@ def _run(w, opts, c2=None, x0=None):
     else:
         kw["log_delta"] = dev["log_delta"]
     x0d = None if x0 is None else torch.from_numpy(x0.astype(np.complex64)).to(cuda)
+    if opts.get("glu"):
+        gw, gb = _glu_params(w.H, opts)
+        kw["glu_w"] = torch.from_numpy(gw).to(cuda)
+        kw["glu_bias"] = None if gb is None else torch.from_numpy(gb).to(cuda)
+        kw["glu_variant"] = opts["glu"]
     y, xl = s5.forward_ex(u, dev["lam"], dev["b_tilde"], ct, dev["d"], x0=x0d,
                           final_state=opts.get("state", False), half_spectrum=opts.get("half", False),
                           bilinear=opts.get("bilinear", False), gelu=opts.get("gelu", False),
@@ -79,12 +95,35 @@ def _run(w, opts, c2=None, x0=None):
     return y, xl
 
 
+def _glu_params(H, opts):
+    """The gate's W [H, H] (N(0, 1/H)) and bias (N(0, 1/4), or None), float32."""
+    rng = np.random.default_rng(1000 + H)
+    gw = (rng.normal(size=(H, H)) / math.sqrt(H)).astype(np.float32)
+    gb = (0.5 * rng.normal(size=H)).astype(np.float32) if opts.get("glu_bias") else None
+    return gw, gb
+
+
 def _oracle(w, opts, c2=None, x0=None):
+    """The oracle's layer output (without the gate) and final state."""
     kw = {"delta": w.delta} if w.time_varying else {"log_delta": w.log_delta}
     return orc.forward_ex(w.u, w.lam, w.b_tilde, c2 if c2 is not None else w.c_tilde, w.d, x0=x0,
                           conj_sym=opts.get("half", False), method="bilinear" if opts.get("bilinear") else "zoh",
                           activation="gelu" if opts.get("gelu") else "gelu_tanh" if opts.get("gelu_tanh") else None,
                           bidirectional=opts.get("bidir", False), **kw)
+
+
+def _gate_err(w, opts, y_gated, y_hat):
+    """Gated output against the oracle's gate of the layer's own output y_hat,
+    beyond the gate's amplification of its product's rounding (and, bf16, the
+    output's own rounding), / rms."""
+    gw, gb = _glu_params(w.H, opts)
+    yh = y_hat.float().cpu().numpy().astype(np.float64)
+    ref = orc.glu(yh, gw, gb, opts["glu"])
+    got = y_gated.float().cpu().numpy().astype(np.float64)
+    excess = np.abs(got - ref) - glu_allowance(yh, gw, gb, opts["glu"], rho=0.0)
+    if w.io == "bf16":
+        excess = excess - BF16_UNIT_ROUNDOFF * np.abs(ref)
+    return float(np.max(excess)) / math.sqrt(float(np.mean(ref ** 2)))
 
 
 CASES = [
@@ -120,13 +159,25 @@ CASES = [
     ((2, 1000, 256, 128, "bf16", False), {"bidir": True, "gelu": True}),
     ((2, 777, 250, 192, "bf16", False), {"bidir": True}),
     ((2, 600, 200, 256, "f32", False), {"bilinear": True, "state": True}),
+    # the gated activation: inside the output pass (bf16, H <= 128, no backward
+    # scan), else after the layer
+    ((2, 1000, 128, 256, "bf16", False), {"glu": 1, "glu_bias": True}),
+    ((2, 777, 96, 128, "bf16", False), {"glu": 2}),
+    ((2, 513, 96, 128, "bf16", True), {"glu": 1, "glu_bias": True}),
+    ((2, 600, 64, 64, "bf16", False), {"glu": 1, "state": True}),
+    ((2, 300, 24, 40, "bf16", False), {"glu": 2, "glu_bias": True, "half": True, "bilinear": True}),
+    ((2, 300, 24, 40, "f32", False), {"glu": 1, "glu_bias": True}),
+    ((2, 1000, 256, 192, "bf16", False), {"glu": 2}),
+    ((2, 97, 24, 40, "bf16", False), {"glu": 1, "bidir": True}),
+    ((1, 600, 128, 256, "bf16", True), {"glu": 1}),
     ((2, 513, 160, 96, "f32", True), {"bilinear": True, "gelu": True, "state": True}),
 ]
 
 
 def _name(case):
     (B, L, H, P, io, tv), o = case
-    return f"B{B}_L{L}_H{H}_P{P}_{io}{'_tv' if tv else ''}_" + "+".join(sorted(k for k, v in o.items() if v))
+    return f"B{B}_L{L}_H{H}_P{P}_{io}{'_tv' if tv else ''}_" + "+".join(
+        sorted(k if v is True else f"{k}{v}" for k, v in o.items() if v))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_name(c) for c in CASES])
@@ -141,14 +192,22 @@ def test_option_parity(case):
     print(f"[options] {_name(case)}", flush=True)
     y, xl = _run(w, opts, c2, x0)
     yo, xo = _oracle(w, opts, c2, x0)
+    eg = None
+    if opts.get("glu"):
+        y_gated = y
+        y, xl = _run(w, {k: v for k, v in opts.items() if k not in ("glu", "glu_bias")}, c2, x0)
+        eg = _gate_err(w, opts, y_gated, y)
     ey = _y_err(io, y, yo)
     msg = f"[options]   y {ey:.3e} (tol {w.tol:.0e})"
+    if eg is not None:
+        msg += f"  gated {eg:.3e}"
     if opts.get("state"):
         ex = _x_err(xl, xo)
         msg += f"  x_last {ex:.3e}"
         assert ex <= w.tol
     print(msg, flush=True)
     assert ey <= w.tol
+    assert eg is None or eg <= w.tol
 
 
 def test_plain_options_match_plain_entry_point():
