@@ -23,7 +23,8 @@ void fused_shape(bool bf16_io, bool time_varying, int Ppad, int Hpad, bool gate,
   // 128 registers of weights (M8 KS NP <= 16), so time-invariant shapes up to
   // H = 256 (KS = 8) keep them; the time-varying step up to H = 128
   const int M8 = (4 * MPW + 7) / 8;
-  const bool keep = MPW * NP <= 4 && M8 * KS * NP <= 16 && (KS <= 4 || !time_varying);
+  // (pass 1's register-weight instances are compiled for KS <= 8)
+  const bool keep = MPW * NP <= 4 && M8 * KS * NP <= 16 && KS <= 8 && (KS <= 4 || !time_varying);
   const bool keep_scan = KS <= 4 && MPW * NP <= 4 && !(time_varying && MPW > 2);
   p.R = 0;
   // bf16 instances are compiled for R = 2 (which always fits); float32 ones

@@ -112,6 +112,8 @@ def test_config_full_size(i):
     (1, 1, 1, 1), (1, 7, 5, 3), (2, 33, 20, 13), (3, 100, 64, 64), (1, 257, 16, 8),
     (2, 129, 96, 128), (1, 300, 130, 70), (2, 1000, 256, 192), (1, 77, 512, 256),
     (2, 600, 200, 256), (1, 333, 160, 100), (3, 250, 250, 40),
+    # H > 256 with P <= 128: pass 1 with more than eight drive K-steps
+    (2, 300, 443, 33), (1, 200, 512, 128), (2, 150, 300, 64),
 ])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_ragged_shapes(shape, io):

@@ -1,7 +1,11 @@
 """Seeded random sweep over shapes and option combinations of s5_forward_ex
 against the float64 oracle (bounds as test_options_gpu: 2e-4 of rms for
-float32 I/O; bf16: the excess over the output's rounding, and for the
-bidirectional form over the forward half's rounding, <= 2e-2 of rms)."""
+float32 I/O; bf16: the excess over the output's rounding <= 2e-2 of rms, the
+bidirectional form included, whose y is rounded once). About half of the
+cases with H <= 256 and no GELU also apply the gated activation, checked as in
+test_options_gpu: the layer's own output against the oracle, the gated
+output against the oracle's gate of that output beyond its product's
+rounding bound."""
 
 import math
 
@@ -10,6 +14,7 @@ import pytest
 
 import oracle.s5_oracle as orc
 import workloads as wl
+from gate_bound import glu_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +28,7 @@ def _need_gpu():
     import diagonal_state_space_amd  # noqa: F401  (fails loudly if libs5.so is missing)
 
 
-def _cases(n=24, seed=2024):
+def _cases(n=32, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for k in range(n):
@@ -58,10 +63,24 @@ def test_random_options(case):
     t = {n: torch.from_numpy(np.ascontiguousarray(getattr(w, n))).to(dev)
          for n in ("lam", "b_tilde", "c_tilde", "d", "log_delta")}
     kw = {"delta": torch.from_numpy(w.delta).to(dev)} if tv else {"log_delta": t["log_delta"]}
-    y, xl = s5.forward_ex(u, t["lam"], t["b_tilde"], torch.from_numpy(c2).to(dev) if bidir else t["c_tilde"],
-                          t["d"], x0=torch.from_numpy(x0).to(dev) if x0 is not None else None,
-                          final_state=opts["state"], half_spectrum=opts["half"], bilinear=opts["bilinear"],
-                          gelu=opts["gelu"], bidirectional=bidir, **kw)
+    # the gated activation (its own draws, so that the cases above stay as they were)
+    grng = np.random.default_rng(10000 + k)
+    glu = H <= 256 and not opts["gelu"] and bool(grng.random() < 0.6)
+    gvar = 1 + int(grng.random() < 0.5)
+    gw = (grng.normal(size=(H, H)) / math.sqrt(H)).astype(np.float32)
+    gb = (0.5 * grng.normal(size=H)).astype(np.float32) if grng.random() < 0.5 else None
+
+    def call(gate):
+        gkw = {}
+        if gate:
+            gkw = {"glu_w": torch.from_numpy(gw).to(dev), "glu_variant": gvar,
+                   "glu_bias": torch.from_numpy(gb).to(dev) if gb is not None else None}
+        return s5.forward_ex(u, t["lam"], t["b_tilde"], torch.from_numpy(c2).to(dev) if bidir else t["c_tilde"],
+                             t["d"], x0=torch.from_numpy(x0).to(dev) if x0 is not None else None,
+                             final_state=opts["state"], half_spectrum=opts["half"], bilinear=opts["bilinear"],
+                             gelu=opts["gelu"], bidirectional=bidir, **kw, **gkw)
+    y_gated = call(True)[0] if glu else None
+    y, xl = call(False)
     torch.cuda.synchronize()
     okw = {"delta": w.delta} if tv else {"log_delta": w.log_delta}
     method = "bilinear" if opts["bilinear"] else "zoh"
@@ -72,11 +91,16 @@ def test_random_options(case):
     excess = np.abs(yg - yo)
     if io == "bf16":
         excess = excess - 2.0 ** -8 * np.abs(yo)
-        if bidir:
-            yf, _ = orc.forward_ex(w.u, w.lam, w.b_tilde, c2[:, :P], w.d, conj_sym=opts["half"], method=method, **okw)
-            excess = excess - 2.0 ** -9 * np.abs(yf) * (1.13 if opts["gelu"] else 1.0)
     err = float(np.max(excess)) / rms
     msg = f"[random]   y {err:.3e} (tol {w.tol:.0e})"
+    if glu:
+        ref = orc.glu(yg, gw, gb, gvar)
+        gx = np.abs(y_gated.float().cpu().numpy().astype(np.float64) - ref) - glu_allowance(yg, gw, gb, gvar, rho=0.0)
+        if io == "bf16":
+            gx = gx - 2.0 ** -8 * np.abs(ref)
+        gerr = float(np.max(gx)) / (math.sqrt(float(np.mean(ref ** 2))) or 1.0)
+        msg += f"  gated (variant {gvar}) {gerr:.3e}"
+        assert gerr <= w.tol
     if opts["state"]:
         xerr = float(np.max(np.abs(xl.cpu().numpy() - xo))) / (math.sqrt(float(np.mean(np.abs(xo) ** 2))) or 1.0)
         msg += f"  x_last {xerr:.3e}"
