@@ -26,7 +26,9 @@ Prints one JSON line with the contract fields plus
                 below is also given against them (frac_measured)
   configs       the four other workloads (tiny, medium, long, irregular),
                 each measured in this run: wall time per call over rotating
-                buffer sets, tokens/s, per-launch kernel times, the dominant
+                buffer sets (20 warm-up calls, then max(--steps, 100) timed:
+                the first few hundred microseconds after a synchronisation
+                run slower), tokens/s, per-launch kernel times, the dominant
                 kernel's roofline fraction, the layer's HBM fraction and the
                 parity of its output against the oracle
 
@@ -780,7 +782,7 @@ def main() -> int:
             if c == args.config:
                 continue
             print(f"[bench] workload {c} (in-run measurement)", file=sys.stderr, flush=True)
-            out["configs"][str(c)] = measure_config(c, s5, torch, wl, peaks, 5, max(args.steps, 20))
+            out["configs"][str(c)] = measure_config(c, s5, torch, wl, peaks, 20, max(args.steps, 100))
 
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
