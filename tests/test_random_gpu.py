@@ -102,7 +102,10 @@ def test_random_options(case):
         msg += f"  gated (variant {gvar}) {gerr:.3e}"
         assert gerr <= w.tol
     if opts["state"]:
-        xerr = float(np.max(np.abs(xl.cpu().numpy() - xo))) / (math.sqrt(float(np.mean(np.abs(xo) ** 2))) or 1.0)
+        xex = np.abs(xl.cpu().numpy() - xo)
+        if io == "bf16":
+            xex = xex - 2.0 ** -8 * np.abs(xo)   # (each mode's state carries the bf16 operands' rounding)
+        xerr = float(np.max(xex)) / (math.sqrt(float(np.mean(np.abs(xo) ** 2))) or 1.0)
         msg += f"  x_last {xerr:.3e}"
         assert xerr <= w.tol
     print(msg, flush=True)

@@ -5,7 +5,11 @@ y uses the bounds of test_parity_gpu (2e-4 of rms for float32 I/O, 2e-2 of
 rms plus the bf16 output rounding for bf16 I/O). The final state is float32
 in both I/O types; its error comes from the bf16 matrix-core operands (bf16
 I/O) or the bf16x3 split (float32 I/O): max |x_gpu - x_oracle| / rms(x_oracle)
-<= 2e-2 (bf16) and 2e-4 (float32)."""
+<= 2e-4 (float32); for bf16 I/O each mode's state carries a relative error
+up to about 2^-8 (B_bar and the drive's u rounded to bf16), so, in the form of
+y's bound, the excess over 2^-8 |x_oracle| <= 2e-2 of rms(x_oracle) (the
+largest states reach ~10 rms under per-step intervals, where 2e-2 of rms
+alone is below their operand rounding)."""
 
 import math
 
@@ -73,10 +77,13 @@ def _y_ok(w, y, yo):
     return float(np.max(excess)) / rms
 
 
-def _x_err(xg, xo):
+def _x_err(xg, xo, io="f32"):
     xg = xg.cpu().numpy().astype(np.complex128)
     rms = math.sqrt(float(np.mean(np.abs(xo) ** 2)))
-    return float(np.max(np.abs(xg - xo))) / rms
+    excess = np.abs(xg - xo)
+    if io == "bf16":
+        excess = excess - BF16_UNIT_ROUNDOFF * np.abs(xo)
+    return float(np.max(excess)) / rms
 
 
 SHAPES = [
@@ -103,7 +110,7 @@ def test_stateful_parity(shape):
     t = _dev(w)
     y, xl = _run_gpu(w, t, x0=x0)
     yo, xo = _run_oracle(w, x0)
-    ey, ex = _y_ok(w, y, yo), _x_err(xl, xo)
+    ey, ex = _y_ok(w, y, yo), _x_err(xl, xo, w.io)
     print(f"[state]   y {ey:.3e}  x_last {ex:.3e}  (tol {w.tol:.0e})", flush=True)
     assert ey <= w.tol
     assert ex <= w.tol
@@ -111,7 +118,7 @@ def test_stateful_parity(shape):
     y0, xl0 = _run_gpu(w, t, x0=None)
     yo0, xo0 = _run_oracle(w, None)
     assert _y_ok(w, y0, yo0) <= w.tol
-    assert _x_err(xl0, xo0) <= w.tol
+    assert _x_err(xl0, xo0, w.io) <= w.tol
 
 
 @pytest.mark.parametrize("io,tv", [("bf16", False), ("f32", True)])
@@ -133,9 +140,9 @@ def test_split_run_equals_one_run(io, tv):
     yo, xo = _run_oracle(w, x0)
     ys = torch.cat([y1, y2], dim=1)
     print(f"[state]   one run {_y_ok(w, y, yo):.3e}, split {_y_ok(w, ys, yo):.3e}, "
-          f"x_last {_x_err(xl2, xo):.3e}", flush=True)
+          f"x_last {_x_err(xl2, xo, w.io):.3e}", flush=True)
     assert _y_ok(w, ys, yo) <= w.tol
-    assert _x_err(xl2, xo) <= w.tol
+    assert _x_err(xl2, xo, w.io) <= w.tol
     assert _x_err(xl2, xl.cpu().numpy().astype(np.complex128)) <= w.tol
 
 
