@@ -267,6 +267,9 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
     a.glu_variant = 0;
     if (!s5::forward_layout(a, lay)) return S5_ERR_UNSUPPORTED;
   }
+  // every launch of the plan has a compiled kernel instance (a host-side walk
+  // of the dispatch): otherwise refuse the call before anything is enqueued
+  if (s5::launch_forward(a, lay, nullptr, stream, nullptr, 0, true) != hipSuccess) return S5_ERR_UNSUPPORTED;
   if (noalloc) {
     // the fixed per-device array; the options path (backward scan) never comes here
     if (lay.total > S5_NOALLOC_SCRATCH_BYTES || opt.bidir) return S5_ERR_UNSUPPORTED;

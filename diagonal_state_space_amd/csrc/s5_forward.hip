@@ -194,10 +194,13 @@ hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, 
 }
 
 hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws, hipStream_t stream,
-                          const hipEvent_t* ev, int nev) {
+                          const hipEvent_t* ev, int nev, bool dry) {
   if (l.plan.R == 0) return hipErrorInvalidValue;
-  char* base = static_cast<char*>(ws);
+  if (dry) ev = nullptr;
+  // workspace addresses (integer arithmetic: ws is null on a dry walk)
+  auto at = [ws](size_t off) { return reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(ws) + off); };
   FusedParams q{};
+  q.dry = dry ? 1 : 0;
   q.B = a.B; q.L = a.L; q.H = a.H; q.P = a.P;
   q.Hpad = l.Hpad; q.Ppad = l.Ppad;
   q.R = l.plan.R; q.nck = l.plan.nck; q.Lseg = l.plan.Lseg; q.Q = l.plan.Q;
@@ -208,7 +211,7 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   q.d = a.d; q.log_delta = a.log_delta; q.delta = a.delta;
   q.x0 = a.x0; q.xlast = a.xlast;
   q.glu_w = a.glu_w; q.glu_bias = a.glu_bias; q.glu_variant = a.glu_variant;
-  q.gpack = a.glu_w != nullptr ? reinterpret_cast<uint4*>(base + l.gpack) : nullptr;
+  q.gpack = a.glu_w != nullptr ? static_cast<uint4*>(at(l.gpack)) : nullptr;
   q.c_ld = a.c_ld > 0 ? a.c_ld : a.P;
   q.c_off = a.c_off;
   q.c_scale = a.c_scale;
@@ -216,14 +219,14 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   q.rev = a.rev;
   q.accum = a.accum;
   q.gelu = a.gelu;
-  q.bpack = reinterpret_cast<uint4*>(base + l.bpack);
-  q.cpack = reinterpret_cast<uint4*>(base + l.cpack);
-  q.modes = reinterpret_cast<ModeParams*>(base + l.modes);
-  q.sagg = reinterpret_cast<float2*>(base + l.sagg);
-  q.sagg_a = a.time_varying ? reinterpret_cast<float2*>(base + l.sagg_a) : nullptr;
-  q.tot = reinterpret_cast<float2*>(base + l.tot);
-  q.tot_a = reinterpret_cast<float2*>(base + l.tot_a);
-  q.cap = reinterpret_cast<float2*>(base + l.cap);
+  q.bpack = static_cast<uint4*>(at(l.bpack));
+  q.cpack = static_cast<uint4*>(at(l.cpack));
+  q.modes = static_cast<ModeParams*>(at(l.modes));
+  q.sagg = static_cast<float2*>(at(l.sagg));
+  q.sagg_a = a.time_varying ? static_cast<float2*>(at(l.sagg_a)) : nullptr;
+  q.tot = static_cast<float2*>(at(l.tot));
+  q.tot_a = static_cast<float2*>(at(l.tot_a));
+  q.cap = static_cast<float2*>(at(l.cap));
   if (!a.bidir) {
     hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
     if (e != hipSuccess) return e;
@@ -237,16 +240,16 @@ hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws
   // drive. The forward pass 2 stores y (D u included) as float32 (into the
   // workspace for bf16 I/O, into y itself for float32 I/O); the backward
   // pass 2 adds its readout (second half of C~) and stores y once, then GELU.
-  q.yp = a.bf16_io ? reinterpret_cast<float*>(base + l.yp) : static_cast<float*>(a.y);
-  q.sagg_b = reinterpret_cast<float2*>(base + l.sagg_b);
-  q.tot_b = reinterpret_cast<float2*>(base + l.tot_b);
-  q.tot_a_b = reinterpret_cast<float2*>(base + l.tot_a_b);
+  q.yp = a.bf16_io ? static_cast<float*>(at(l.yp)) : static_cast<float*>(a.y);
+  q.sagg_b = static_cast<float2*>(at(l.sagg_b));
+  q.tot_b = static_cast<float2*>(at(l.tot_b));
+  q.tot_a_b = static_cast<float2*>(at(l.tot_a_b));
   q.rev = 0;
   q.accum = 0;
   q.gelu = 0;
   q.both = l.plan.both ? 1 : 0;
   q.ypart = a.bf16_io ? 1 : 0;
-  q.cpack_b = reinterpret_cast<uint4*>(base + l.cpack_b);   // both halves' C' in one packing launch
+  q.cpack_b = static_cast<uint4*>(at(l.cpack_b));   // both halves' C' in one packing launch
   hipError_t e = timed(0, ev, nev, stream, pack_launcher, q, l.plan);
   if (e != hipSuccess) return e;
   e = timed(1, ev, nev, stream, launch_reduce, q, l.plan);

@@ -98,6 +98,9 @@ struct FusedParams {
   int glu_variant;        // 1: GELU(y) * gate, 2: y * gate
   uint4* gpack;           // the gate's W as A-operand fragments, bf16 hi plane then lo plane
                           // ([Hpad/16][Hpad/32][64 lanes] each); null: no gate
+  // host only: walk the launch sequence and its instance dispatch without
+  // launching anything (whether every launch has a compiled kernel)
+  int dry;
 };
 
 // Launch plan of one call: chunk size, stream length, grid and LDS bytes.

@@ -1905,6 +1905,7 @@ namespace fused {
 
 template <auto Kern>
 hipError_t launch_one(int blocks, int threads, size_t lds, hipStream_t s, const FusedParams& q) {
+  if (q.dry) return hipSuccess;   // the instance exists; nothing is launched
   // the first launch of each instance lifts its dynamic LDS limit
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

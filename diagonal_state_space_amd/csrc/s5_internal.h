@@ -89,7 +89,11 @@ hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, 
 // pass 1, pass 2; for the bidirectional form then the backward scan's
 // packing, its own pass 1 (an empty pair where the forward pass 1 computed
 // its aggregates) and its pass 2.
+// With dry = true nothing is launched or recorded and ws may be null: the
+// result says whether every launch of the plan has a compiled kernel instance
+// (hipErrorInvalidValue where one is missing), so a caller can refuse the
+// call before it enqueues anything.
 hipError_t launch_forward(const ForwardArgs& a, const ForwardLayout& l, void* ws, hipStream_t stream,
-                          const hipEvent_t* ev, int nev);
+                          const hipEvent_t* ev, int nev, bool dry = false);
 
 }  // namespace s5

@@ -146,6 +146,7 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
 }  // namespace
 
 hipError_t launch_pack(const FusedParams& q, hipStream_t stream) {
+  if (q.dry) return hipSuccess;
   const int KS = q.Hpad / 32, K2 = 2 * q.Ppad / 32;
   const int nc = (q.Hpad / 16) * K2 * 64;
   const int total = (q.Ppad / 16) * 2 * KS * 64 + nc + q.Ppad + (q.cpack_b != nullptr ? nc : 0) +

@@ -72,7 +72,10 @@ typedef enum { S5_F32 = 0, S5_BF16 = 1 } s5_dtype;
 typedef enum {
   S5_OK = 0,
   S5_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, overlapping output */
-  S5_ERR_UNSUPPORTED = 2,      /* dtype, size limit or alignment not supported */
+  S5_ERR_UNSUPPORTED = 2,      /* dtype, size limit or alignment not supported, or
+                                  no compiled kernel for the call (checked on the
+                                  host before anything is enqueued; no call within
+                                  the size limits meets it) */
   S5_ERR_OUT_OF_MEMORY = 3,    /* scratch allocation failed */
   S5_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } s5_status;

@@ -298,3 +298,54 @@ def test_missing_library_fails_loudly(tmp_path):
                          env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=300)
     assert out.returncode == 0, out.stderr
     assert "raised" in out.stdout and "libs5.so not found" in out.stdout
+
+
+_SWEEP = r"""
+import ctypes, json, sys
+import diagonal_state_space_amd as s5
+base, gap = 1 << 36, 1 << 26          # fake, aligned, disjoint device ranges (never dereferenced)
+ptr = [base + i * gap for i in range(12)]
+opts = [(0, False), (s5.FLAG_HALF_SPECTRUM, False), (s5.FLAG_BILINEAR, False), (s5.FLAG_GELU, False),
+        (s5.FLAG_GELU_TANH, False), (0, True), (s5.FLAG_BILINEAR | s5.FLAG_GELU, True),
+        (s5.FLAG_BIDIRECTIONAL, False), (s5.FLAG_BIDIRECTIONAL | s5.FLAG_GELU, False),
+        (s5.FLAG_GLU, False), (s5.FLAG_GLU | s5.FLAG_BILINEAR, True)]
+Ps = [1, 63, 64, 65, 128, 129, 192, 193, 255, 256]
+Hs = sorted({1, 2, 31, 96, 257, 511} | {32 * k + e for k in range(1, 17) for e in (0, 1) if 32 * k + e <= 512})
+bad, n = [], 0
+for io in (0, 1):
+    for tv in (False, True):
+        for flags, state in opts:
+            if tv and flags & s5.FLAG_BIDIRECTIONAL:
+                continue
+            glu = bool(flags & s5.FLAG_GLU)
+            for P in Ps:
+                for H in Hs:
+                    if glu and H > 256:
+                        continue
+                    d = s5.ForwardDesc(ctypes.sizeof(s5.ForwardDesc), flags, io, 2, 64, H, P,
+                                       ptr[0], ptr[1], ptr[2], ptr[3], ptr[4],
+                                       None if tv else ptr[5], ptr[6] if tv else None,
+                                       ptr[7] if state else None, ptr[8], ptr[9] if state else None,
+                                       ptr[10] if glu else None, None, 1 if glu else 0)
+                    r = s5.lib().s5_forward_ex(ctypes.byref(d), None)
+                    n += 1
+                    if r != 3:
+                        bad.append((io, tv, flags, state, P, H, r))
+print(json.dumps({"n": n, "bad": bad[:20], "nbad": len(bad)}))
+"""
+
+
+def test_every_supported_call_has_kernels():
+    """Every size within the limits, with every option, I/O type and interval
+    kind, passes validation and finds a compiled kernel instance for each of
+    its launches: with allocation forced to fail from the host, each call
+    ends at the scratch allocation (S5_ERR_OUT_OF_MEMORY), which comes after
+    the dispatch walk, and never at S5_ERR_UNSUPPORTED or S5_ERR_HIP."""
+    import json
+    env = dict(os.environ, S5_TEST_FAIL_ALLOC="1")
+    out = subprocess.run([sys.executable, "-c", _SWEEP], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    assert res["n"] > 10000
+    assert res["nbad"] == 0, res["bad"]
