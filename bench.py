@@ -31,6 +31,13 @@ Prints one JSON line with the contract fields plus
                 run slower), tokens/s, per-launch kernel times, the dominant
                 kernel's roofline fraction, the layer's HBM fraction and the
                 parity of its output against the oracle
+  device_warmup before the warm-up steps, untimed calls keep the GPU busy for
+                --device-warmup seconds (default 0.5), since the chip raises
+                its clocks only under sustained load: a timed region of a few
+                milliseconds right after set-up measures that ramp (config 3,
+                20 calls: 127-137 us per call cold, 108-109 us once warm).
+                ms_per_step_without gives the same K steps timed right after
+                the --warmup calls alone, before that phase
 
 --variant times the same workload through s5_forward_ex with one option
 (initial/final state, half spectrum, bilinear, GELU, bidirectional) or as a
@@ -216,13 +223,32 @@ class PeakProbes:
                           f"(median of {reps})"}
 
 
-def forward_timed(w, s5, torch, warmup: int, steps: int, event_steps: int = 0):
+def keep_busy(call, torch, seconds: float, batch: int = 20) -> int:
+    """Untimed calls call(0), call(1), ... for `seconds` (a synchronisation
+    after every `batch`): the chip raises its clocks only under sustained
+    load. Returns the number of calls."""
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(batch):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def forward_timed(w, s5, torch, warmup: int, steps: int, event_steps: int = 0, device_warmup_s: float = 0.0):
     """Time s5_forward / s5_forward_timevarying on workload w: rotating input
     and output sets (> 512 MB in total, so that the 256 MB Infinity Cache
     cannot serve repeats), `warmup` untimed calls, `steps` calls between two
     synchronisations (wall clock), then per-launch HIP events on `steps` more
-    calls, and (event_steps > 0) event pairs around whole calls. Returns a
-    dict of timings and the output of the last call."""
+    calls, and (event_steps > 0) event pairs around whole calls. With
+    device_warmup_s > 0 the wall-clock timing is taken twice: once right after
+    the `warmup` calls (returned as cold_wall_ms), then again after calls
+    have kept the GPU busy for device_warmup_s seconds and `warmup` more
+    calls (wall_ms): the chip raises its clocks only under sustained load, and
+    a timed region of a few milliseconds otherwise measures the ramp.
+    Returns a dict of timings and the output of the last call."""
     dev = torch.device("cuda:0")
     lam = torch.from_numpy(w.lam).to(dev)
     bt = torch.from_numpy(w.b_tilde).to(dev)
@@ -249,16 +275,26 @@ def forward_timed(w, s5, torch, warmup: int, steps: int, event_steps: int = 0):
         return k
 
     i = 0
-    for _ in range(warmup):
-        step(i)
-        i += 1
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(i)
-        i += 1
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    def timed_steps():
+        nonlocal i
+        for _ in range(warmup):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    cold_wall_ms = None
+    warm_calls = 0
+    if device_warmup_s > 0:
+        cold_wall_ms = timed_steps()
+        warm_calls = keep_busy(step, torch, device_warmup_s)
+    wall_ms = timed_steps()
     ev = HipEvents()
     evs = [[ev.create() for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -272,7 +308,8 @@ def forward_timed(w, s5, torch, warmup: int, steps: int, event_steps: int = 0):
     for e in evs:
         for h in e:
             ev.destroy(h)
-    res = {"wall_ms": wall_ms, "launch_ms": launch_ms, "n_sets": n_sets,
+    res = {"wall_ms": wall_ms, "cold_wall_ms": cold_wall_ms, "device_warmup_calls": warm_calls,
+           "launch_ms": launch_ms, "n_sets": n_sets,
            "set_last": (i - 1) % n_sets, "ys": ys, "step": step, "next": i,
            "params": (lam, bt, ct, d, logd), "us": us, "deltas": deltas}
     if event_steps > 0:
@@ -317,12 +354,12 @@ def roofline_fracs(w, k_ms: float, layer_ms: float, peaks: dict):
     return out
 
 
-def measure_config(i: int, s5, torch, wl, peaks: dict, warmup: int, steps: int) -> dict:
+def measure_config(i: int, s5, torch, wl, peaks: dict, warmup: int, steps: int, device_warmup_s: float) -> dict:
     """One of the other workloads, measured in this run (see the module
     docstring, `configs`)."""
     import oracle.s5_oracle as orc
     w = wl.make_config(i)
-    r = forward_timed(w, s5, torch, warmup, steps)
+    r = forward_timed(w, s5, torch, warmup, steps, device_warmup_s=device_warmup_s)
     mean = r["launch_ms"].mean(axis=0)
     wall = r["wall_ms"]
     yg = r["ys"][r["set_last"]].float().cpu().numpy().astype(np.float64)
@@ -337,6 +374,8 @@ def measure_config(i: int, s5, torch, wl, peaks: dict, warmup: int, steps: int) 
                         f"{'_timevarying' if w.time_varying else ''}"),
            "ms_per_step": round(wall, 5), "tokens_per_s": round(w.B * w.L / (wall * 1e-3), 1),
            "steps": steps, "buffer_sets": r["n_sets"],
+           "ms_per_step_without_device_warmup": (round(r["cold_wall_ms"], 5)
+                                                 if r["cold_wall_ms"] is not None else None),
            "kernels": {"pack_us": round(float(mean[0]) * 1e3, 2), "reduce_us": round(float(mean[1]) * 1e3, 2),
                        "scan_us": round(float(mean[2]) * 1e3, 2)},
            "roofline": roofline_fracs(w, float(mean[2]), float(mean.sum()), peaks),
@@ -386,6 +425,7 @@ def bench_step(args, w, s5, torch, us, lam, bt, ct, d, logd, deltas) -> int:
         s5.step(u1[i % n], lam, bt, ct, d, x, y=y, **kw)
 
     steps = max(args.steps, 200)
+    keep_busy(one, torch, args.device_warmup)
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
@@ -449,6 +489,7 @@ def bench_glu(args, w, s5, torch, us, ys, n_sets) -> int:
         k = i % n_sets
         s5.glu(yin[k], wd, bd, variant, out=outs[k])
 
+    keep_busy(one, torch, args.device_warmup)
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
@@ -540,6 +581,7 @@ def bench_variant(args, w, s5, torch, us, ys, deltas, lam, bt, ct, d, logd, n_se
         extra = {"x0": x0, "x_last": xl} if v == "stateful" else {}
         s5.forward_ex(us[k], lam, bt, ct_run, d, y=ys[k], **kw, **extra, **opts[v])
 
+    keep_busy(step, torch, args.device_warmup)   # as for the default line
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -651,6 +693,9 @@ def main() -> int:
     ap.add_argument("--event-steps", type=int, default=100,
                     help="calls timed one by one with a HIP event pair (median reported)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the in-run peak-rate probes")
+    ap.add_argument("--device-warmup", type=float, default=0.5, metavar="SECONDS",
+                    help="keep the GPU busy with untimed calls this long before the warm-up and timed "
+                         "steps (0: none); the timing without it is reported beside")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, 5)
@@ -700,7 +745,7 @@ def main() -> int:
 
     # warm-up, K timed calls (wall clock), K calls with per-launch events,
     # then calls timed one by one with event pairs
-    r = forward_timed(w, s5, torch, args.warmup, args.steps, args.event_steps)
+    r = forward_timed(w, s5, torch, args.warmup, args.steps, args.event_steps, args.device_warmup)
     launch_ms = r["launch_ms"]
     kernel_ms = launch_ms[:, 2]
     ms_per_step = r["wall_ms"]
@@ -766,6 +811,9 @@ def main() -> int:
         "kernels": kernels,
         "hbm": hbm,
     }
+    if r["cold_wall_ms"] is not None:
+        out["device_warmup"] = {"s": args.device_warmup, "calls": r["device_warmup_calls"],
+                                "ms_per_step_without": round(r["cold_wall_ms"], 5)}
     if call_ms is not None:
         out["step_events"] = {"median_us": round(float(np.median(call_ms)) * 1e3, 2),
                               "mean_us": round(float(np.mean(call_ms)) * 1e3, 2),
@@ -782,7 +830,7 @@ def main() -> int:
             if c == args.config:
                 continue
             print(f"[bench] workload {c} (in-run measurement)", file=sys.stderr, flush=True)
-            out["configs"][str(c)] = measure_config(c, s5, torch, wl, peaks, 20, max(args.steps, 100))
+            out["configs"][str(c)] = measure_config(c, s5, torch, wl, peaks, 20, max(args.steps, 100), args.device_warmup)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
