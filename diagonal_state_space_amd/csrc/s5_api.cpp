@@ -144,6 +144,15 @@ hipError_t noalloc_scratch(void** out) {
   return hipSuccess;
 }
 
+// bf16 I/O with at most this many features runs the float32-operand
+// arithmetic (u widened into scratch, y rounded to bf16 once at the end): with
+// so few outputs a readout sum over hundreds of modes can cancel to far
+// below its terms, and the bf16 rounding of B_bar, C' and the states then
+// shows at the percent level of the output's RMS
+constexpr int64_t kWidenMaxH = 8;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 s5_status check_sizes(int64_t P, int64_t H) {
   if (P < 1 || H < 1) return S5_ERR_INVALID_ARGUMENT;
   if (P > S5_MAX_P || H > S5_MAX_H) return S5_ERR_UNSUPPORTED;
@@ -231,7 +240,9 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   a.L = static_cast<int>(L);
   a.H = static_cast<int>(H);
   a.P = static_cast<int>(P);
-  a.bf16_io = io == S5_BF16;
+  const bool io_bf16 = io == S5_BF16;
+  const bool widen = io_bf16 && H <= kWidenMaxH;
+  a.bf16_io = io_bf16 && !widen;
   a.time_varying = time_varying;
   a.u = u;
   a.lam = reinterpret_cast<const float2*>(lambda);
@@ -270,24 +281,40 @@ s5_status forward_common(int64_t B, int64_t L, int64_t H, int64_t P, s5_dtype io
   // every launch of the plan has a compiled kernel instance (a host-side walk
   // of the dispatch): otherwise refuse the call before anything is enqueued
   if (s5::launch_forward(a, lay, nullptr, stream, nullptr, 0, true) != hipSuccess) return S5_ERR_UNSUPPORTED;
+  // widened bf16 I/O: float32 copies of u and y after the plan's scratch
+  const size_t wide = widen ? align256(static_cast<size_t>(tokens) * H * sizeof(float)) : 0;
+  const size_t total = lay.total + 2 * wide;
+  // the float32 pass on the scratch copies, between the two conversions
+  auto run = [&](void* base) -> hipError_t {
+    if (!widen) return s5::launch_forward(a, lay, base, stream, tl_events, tl_nevents);
+    float* u32 = reinterpret_cast<float*>(static_cast<char*>(base) + lay.total);
+    float* y32 = reinterpret_cast<float*>(static_cast<char*>(base) + lay.total + wide);
+    s5::ForwardArgs w = a;
+    w.u = u32;
+    w.y = y32;
+    hipError_t e = s5::launch_widen_bf16(u, u32, tokens * H, stream);
+    if (e == hipSuccess) e = s5::launch_forward(w, lay, base, stream, tl_events, tl_nevents);
+    if (e == hipSuccess) e = s5::launch_narrow_bf16(y32, y, tokens * H, stream);
+    return e;
+  };
   if (noalloc) {
     // the fixed per-device array; the options path (backward scan) never comes here
-    if (lay.total > S5_NOALLOC_SCRATCH_BYTES || opt.bidir) return S5_ERR_UNSUPPORTED;
+    if (total > S5_NOALLOC_SCRATCH_BYTES || opt.bidir) return S5_ERR_UNSUPPORTED;
     void* fixed = nullptr;
     if (noalloc_scratch(&fixed) != hipSuccess) return S5_ERR_HIP;
-    return s5::launch_forward(a, lay, fixed, stream, tl_events, tl_nevents) == hipSuccess ? S5_OK : S5_ERR_HIP;
+    return run(fixed) == hipSuccess ? S5_OK : S5_ERR_HIP;
   }
   if (alloc_fail_hook()) return S5_ERR_OUT_OF_MEMORY;
   Scratch* ws = nullptr;
-  hipError_t e = scratch_acquire(lay.total, stream, &ws);
+  hipError_t e = scratch_acquire(total, stream, &ws);
   if (e == hipErrorOutOfMemory) return S5_ERR_OUT_OF_MEMORY;
   if (e != hipSuccess) return S5_ERR_HIP;
-  e = s5::launch_forward(a, lay, ws->ptr, stream, tl_events, tl_nevents);
+  e = run(ws->ptr);
   if (e == hipSuccess && opt.glu_w != nullptr && !glu_fused) {
     s5::GluArgs g{};
     g.T = static_cast<int>(tokens);
     g.H = static_cast<int>(H);
-    g.bf16_io = a.bf16_io;
+    g.bf16_io = io_bf16;
     g.variant = opt.glu_variant;
     g.y = y;
     g.w = opt.glu_w;

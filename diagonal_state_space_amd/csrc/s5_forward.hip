@@ -186,6 +186,35 @@ __global__ void __launch_bounds__(256) k_state_passthrough(const float2* x0, flo
 }
 }  // namespace
 
+namespace {
+__global__ void __launch_bounds__(256) k_widen_bf16(const unsigned short* in, float* out, int64_t n) {
+  for (int64_t k = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; k < n;
+       k += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    out[k] = __uint_as_float(static_cast<unsigned>(in[k]) << 16);
+}
+
+__global__ void __launch_bounds__(256) k_narrow_bf16(const float* in, __bf16* out, int64_t n) {
+  for (int64_t k = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; k < n;
+       k += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    out[k] = static_cast<__bf16>(in[k]);   // hardware conversion: round to nearest even
+}
+
+unsigned copy_blocks(int64_t n) { return static_cast<unsigned>((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024); }
+}  // namespace
+
+hipError_t launch_widen_bf16(const void* in, float* out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_widen_bf16, dim3(copy_blocks(n)), dim3(256), 0, stream, static_cast<const unsigned short*>(in),
+                     out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow_bf16(const float* in, void* out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_narrow_bf16, dim3(copy_blocks(n)), dim3(256), 0, stream, in, static_cast<__bf16*>(out), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;

@@ -83,6 +83,12 @@ bool forward_layout(const ForwardArgs& a, ForwardLayout& l);
 // x0 is null); n = B*P complex values.
 hipError_t launch_state_passthrough(const float2* x0, float2* xlast, int64_t n, hipStream_t stream);
 
+// bf16 <-> float32 copies of n elements (float32 -> bf16 rounds to nearest
+// even; NaN and infinities carry through), for bf16 I/O computed with the
+// float32-operand arithmetic
+hipError_t launch_widen_bf16(const void* in, float* out, int64_t n, hipStream_t stream);
+hipError_t launch_narrow_bf16(const float* in, void* out, int64_t n, hipStream_t stream);
+
 // Enqueue the whole forward path on `stream` using `ws` (l.total bytes,
 // 256-byte aligned), with the layout forward_layout gave for `a`. ev[2k] /
 // ev[2k+1] are recorded around the k-th kernel launch for k < nev/2: packing,

@@ -123,7 +123,10 @@ s5_status s5_discretize(int64_t P, int64_t H, const s5_c64* lambda, const s5_c64
  * Precision: the state and all accumulation are float32. Products with B_bar
  * and C~ run on the matrix cores: bf16 operands for bf16 io; for float32 io
  * each float32 operand is split into a high and a low bf16 part and three
- * products are summed (about 2^-16 relative per product).
+ * products are summed (about 2^-16 relative per product). bf16 io with
+ * H <= 8 is computed as float32 io (u widened, y rounded to bf16 once, with
+ * 8*B*L*H bytes more scratch): with so few outputs a readout over many modes
+ * can cancel far below its terms, where bf16 operands would show.
  * Errors: S5_ERR_INVALID_ARGUMENT (null pointer, negative B or L, P or H < 1,
  * y overlapping an input), S5_ERR_UNSUPPORTED (unknown io, size limits,
  * misalignment), S5_ERR_OUT_OF_MEMORY, S5_ERR_HIP.

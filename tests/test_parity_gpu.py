@@ -232,3 +232,26 @@ def test_zero_pole_discretize():
     lbo, bbo = orc.discretize(lam.cpu().numpy(), bt.cpu().numpy(), np.exp(logd.cpu().numpy().astype(np.float64)))
     assert np.allclose(bb.cpu().numpy(), bbo, rtol=1e-6, atol=0)
     assert abs(bb[0, 0].item() - 0.05) < 1e-8
+
+
+@pytest.mark.parametrize("H,P,tv", [(1, 256, True), (1, 191, False), (2, 64, False), (8, 256, True), (8, 128, False)])
+def test_bf16_few_features_use_float32_operands(H, P, tv):
+    """bf16 I/O with at most 8 features runs the float32-operand arithmetic:
+    its output is the float32 I/O path's output on the same (bf16-valued)
+    input rounded to bf16 (nearest even), bit for bit, and its error against
+    the oracle is that rounding plus the float32 path's own (2e-4 of RMS)."""
+    w = wl.make_random(3, 400, H, P, io="bf16", tv=tv, seed=900 + H + P, kind="random_walk" if tv else "normal")
+    print(f"[parity] few features B={w.B} L={w.L} H={H} P={P} tv={tv}", flush=True)
+    t = dev(w)
+    y16 = run_gpu(w, t)
+    t32 = dict(t)
+    t32["u"] = t["u"].float()
+    y32 = run_gpu(w, t32)
+    assert y16.dtype == torch.bfloat16 and y32.dtype == torch.float32
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    yo = run_oracle(w)
+    rms = math.sqrt(float(np.mean(yo ** 2)))
+    yg = y16.float().cpu().numpy().astype(np.float64)
+    excess = float(np.max(np.abs(yg - yo) - BF16_UNIT_ROUNDOFF * np.abs(yo))) / rms
+    print(f"[parity]   beyond bf16 storage rounding: {excess:.3e} of rms", flush=True)
+    assert excess <= 2e-4
