@@ -43,6 +43,9 @@ def _abi_call(fn, w, t, y):
 @pytest.mark.parametrize("first,second", [
     ((16, 16384, 128, 256, "bf16"), (2, 1000, 64, 64, "bf16")),   # the long workload, then a small one
     ((8, 4096, 96, 128, "f32"), (1, 300, 24, 40, "f32")),
+    # bf16 with at most 8 features: the float32-operand path, with the
+    # widened u and y in the array beside the aggregates
+    ((16, 4096, 4, 256, "bf16"), (3, 700, 1, 65, "bf16")),
 ])
 def test_noalloc_matches_allocating_entry_point(first, second):
     import diagonal_state_space_amd as s5
