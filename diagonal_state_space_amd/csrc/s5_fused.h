@@ -40,6 +40,7 @@ struct ModeParams {
   float hrev;      // Im(lambda) / (4 pi): half-angle turns per unit interval  (time-varying)
   float2 alast;    // abar^m, m = ((L-1) mod Lseg) + 1: the stream holding token
                    // L-1, from its first token through L-1  (time-invariant)
+  float2 arange;   // exp(16 Lseg lambda Delta): one whole workgroup range   (time-invariant)
 };
 
 // One forward call, as the kernels see it.

@@ -1390,6 +1390,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       c = {v.x, v.y};
     }
     const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + ln.tid;
+    // time-invariant: the range power from the float64 packing (as range_carry)
+    cf ar = {0.0f, 0.0f};
+    if constexpr (!TV) {
+      const float2 v = q.modes[ln.tid].arange;
+      ar = {v.x, v.y};
+    }
     constexpr int kBatch = 8;
     for (int q0 = 0; q0 < qq; q0 += kBatch) {
       cf xs[kBatch], as[kBatch];
@@ -1397,9 +1403,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
       for (int e = 0; e < kBatch; ++e) {
         if (q0 + e < qq) {
           const float2 xv = q.tot[base + static_cast<size_t>(q0 + e) * q.Ppad];
-          const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
           xs[e] = {xv.x, xv.y};
-          as[e] = {av.x, av.y};
+          if constexpr (TV) {
+            const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
+            as[e] = {av.x, av.y};
+          } else {
+            as[e] = ar;
+          }
         }
       }
 #pragma unroll
@@ -1564,7 +1574,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_scan(FusedParams q) {
 
 // carry into the workgroup's range: the totals of the sequence's earlier
 // ranges folded in order (one thread per mode)
-template <bool EXT>
+template <bool EXT, bool TV>
 __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq, int p, S5_LDS pf2* s_c0) {
   cf c = {0.0f, 0.0f};   // the state before step 0: zero, or the caller's
   if (EXT && q.x0 != nullptr && p < q.P) {
@@ -1573,15 +1583,28 @@ __device__ __forceinline__ void range_carry(const FusedParams& q, int b, int qq,
   }
   const size_t base = static_cast<size_t>(b) * q.Q * q.Ppad + p;
   constexpr int kBatch = 16;
+  // time-invariant: every range's transition is the same power of abar,
+  // taken from the float64 packing (rounded once) rather than the range's
+  // product of its 16 stream powers (each rounded), whose rounding a fold
+  // over many ranges would compound for modes with |abar| near 1
+  cf ar = {0.0f, 0.0f};
+  if constexpr (!TV) {
+    const float2 v = q.modes[p].arange;
+    ar = {v.x, v.y};
+  }
   for (int q0 = 0; q0 < qq; q0 += kBatch) {
     cf xs[kBatch], as[kBatch];
 #pragma unroll
     for (int e = 0; e < kBatch; ++e) {
       if (q0 + e < qq) {
         const float2 xv = q.tot[base + static_cast<size_t>(q0 + e) * q.Ppad];
-        const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
         xs[e] = {xv.x, xv.y};
-        as[e] = {av.x, av.y};
+        if constexpr (TV) {
+          const float2 av = q.tot_a[base + static_cast<size_t>(q0 + e) * q.Ppad];
+          as[e] = {av.x, av.y};
+        } else {
+          as[e] = ar;
+        }
       }
     }
 #pragma unroll
@@ -1760,7 +1783,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan_ws(FusedParams q) {
   lds_byte* xlds = lds + 3 * ut;
   const ModeTable mt = fill_mode_table<TV>(q, lds + 3 * ut + 2 * xt, true);
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
-  if (driver && ln.tid < q.Ppad) range_carry<EXT>(q, b, qq, ln.tid, s_c0);
+  if (driver && ln.tid < q.Ppad) range_carry<EXT, TV>(q, b, qq, ln.tid, s_c0);
 
   constexpr int NB = u_stage_blocks<R, BF16, true>();
   const __amdgpu_buffer_rsrc_t ursrc = range_rsrc<BF16>(q.u, q, b, qq, rmap.rev);

@@ -135,6 +135,9 @@ __global__ void __launch_bounds__(256) k_pack(FusedParams q, int split) {
           mp.alast = make_float2(static_cast<float>(al.re), static_cast<float>(al.im));
           mp.abar = make_float2(static_cast<float>(a.re), static_cast<float>(a.im));
           mp.aseg = make_float2(static_cast<float>(as.re), static_cast<float>(as.im));
+          const double nr = static_cast<double>(fused::kStreams) * q.Lseg;
+          const zd ar = f64::zexp({z.re * nr, z.im * nr});
+          mp.arange = make_float2(static_cast<float>(ar.re), static_cast<float>(ar.im));
         }
       }
       q.modes[p] = mp;

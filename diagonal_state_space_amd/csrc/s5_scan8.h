@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) k_scan8(FusedParams q) {
   constexpr int gt = static_cast<int>(KS * R * kBlock);   // one plane of one g tile
   lds_byte* glds = xlds + 2 * xt + mode_table_bytes(64 * MPW, 32 * KS, TV, true);
   S5_LDS pf2* s_c0 = reinterpret_cast<S5_LDS pf2*>(xlds + xt);   // free until x tile 1
-  if (threadIdx.x < static_cast<unsigned>(q.Ppad)) range_carry<EXT>(q, b, qq, threadIdx.x, s_c0);
+  if (threadIdx.x < static_cast<unsigned>(q.Ppad)) range_carry<EXT, TV>(q, b, qq, threadIdx.x, s_c0);
 
   // weights: B_bar fragments of the wave's mode tiles, C' fragments of its h-tiles
   bf16x8 bw[SB ? 1 : KS][MT][2][NP];
