@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(lib_path):
             raise ImportError(f"{lib_path} not found: build it with "
                               "`python -m diagonal_state_space_amd.build_lib`")
+        # torch first: it carries its own HIP runtime, and libs5.so must bind
+        # to that one (loaded before torch, it would bind to the system's, and
+        # torch's streams would be foreign to it: every call S5_ERR_HIP)
+        import torch  # noqa: F401
         L = ctypes.CDLL(lib_path)
         i64, vp, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.s5_discretize.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]

@@ -111,3 +111,31 @@ def test_more_streams_than_scratch_slots():
     for n, (j, y) in enumerate(outs):
         assert torch.equal(y, refs[j]), f"call {n} (workload {j})"
     print(f"[streams] {len(outs)} calls over {len(streams)} streams: bitwise equal", flush=True)
+
+
+def test_library_loaded_before_torch_initialises():
+    """A program that loads the library before it touches torch (s5.lib()
+    first) still gets working calls: the binding imports torch before it
+    loads libs5.so, so both use torch's HIP runtime. (Loaded the other way
+    round, the library bound to the system's runtime and every call on
+    torch's stream returned S5_ERR_HIP.) Run in a child process, which must
+    start with nothing imported."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import diagonal_state_space_amd as s5\n"
+        "s5.lib()\n"
+        "import numpy as np, torch, workloads as wl\n"
+        "w = wl.make_random(1, 64, 16, 8, seed=3)\n"
+        "c = torch.device('cuda:0')\n"
+        "t = [torch.from_numpy(np.ascontiguousarray(getattr(w, k))).to(c) for k in "
+        "('u', 'lam', 'b_tilde', 'c_tilde', 'd', 'log_delta')]\n"
+        "y = s5.forward(*t)\n"
+        "torch.cuda.synchronize()\n"
+        "print('ok', bool(torch.isfinite(y).all()))\n"
+    )
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().endswith("ok True")
